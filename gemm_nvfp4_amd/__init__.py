@@ -1,0 +1,21 @@
+"""gemm_nvfp4_amd: NVFP4 weight-only MoE and dense-projection kernels for MI355X (gfx950).
+
+The compute lives in libnvfp4moe.so (HIP, C ABI in include/nvfp4moe.h); this package is its thin
+Python binding. Entry points carry the C names.
+"""
+from ._lib import (  # noqa: F401
+    MoELayer,
+    NVFP4Error,
+    NVFP4Tensor,
+    header_functions,
+    lib,
+    nvfp4_abi_version,
+    nvfp4_linear,
+    nvfp4_moe_plan,
+    nvfp4_moe_plan_bytes,
+    nvfp4_moe_w13_swiglu,
+    nvfp4_moe_w2_reduce,
+    nvfp4_moe_w2_workspace_bytes,
+    nvfp4_status_str,
+    plan_fields,
+)

@@ -1,0 +1,227 @@
+"""ctypes binding of libnvfp4moe.so (include/nvfp4moe.h).
+
+Argument marshalling only: torch tensors supply device memory and the current HIP stream, and
+every step of the computation runs in the library's HIP kernels. There is no fallback. If the
+library is missing, or a tensor is not on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import torch  # loads torch's HIP runtime first; the library binds to that same runtime (same SONAME)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnvfp4moe.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "nvfp4moe.h")
+
+NVFP4_OK = 0
+STATUS_NAMES = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_ALIGN",
+                4: "NVFP4_ERR_WORKSPACE", 5: "NVFP4_ERR_UNSUPPORTED", 6: "NVFP4_ERR_LAUNCH"}
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} ({status})")
+        self.status = status
+
+
+class nvfp4_weights(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("global_scale", C.c_void_p),
+                ("groups", C.c_int32), ("rows", C.c_int32), ("k", C.c_int32)]
+
+
+_LIB = None
+_vp, _i32, _sz = C.c_void_p, C.c_int32, C.c_size_t
+_SIGS = {
+    "nvfp4_abi_version": (C.c_int, []),
+    "nvfp4_status_str": (C.c_char_p, [C.c_int]),
+    "nvfp4_moe_plan_bytes": (_sz, [_i32, _i32, _i32]),
+    "nvfp4_moe_plan": (C.c_int, [_vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "nvfp4_moe_w13_swiglu": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _i32, _vp, _vp]),
+    "nvfp4_moe_w2_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "nvfp4_moe_w2_reduce": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _vp, _vp, _vp, _sz, _vp]),
+    "nvfp4_linear": (C.c_int, [_vp, _i32, C.POINTER(nvfp4_weights), _vp, _vp]),
+}
+
+
+def lib() -> C.CDLL:
+    """The loaded library. Raises if it has not been built (python gemm_nvfp4_amd/build.py)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python gemm_nvfp4_amd/build.py` "
+                               "(or __graft_entry__.build()); there is no fallback path")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        if L.nvfp4_abi_version() != 1:
+            raise RuntimeError(f"libnvfp4moe ABI version {L.nvfp4_abi_version()} != 1")
+        _LIB = L
+    return _LIB
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/nvfp4moe.h."""
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(nvfp4_\w+)\s*\(", txt, flags=re.M)))
+
+
+def _check(fn: str, status: int):
+    if status != NVFP4_OK:
+        raise NVFP4Error(fn, status, lib().nvfp4_status_str(status).decode())
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+class NVFP4Tensor:
+    """Device storage of an NVFP4 weight: codes uint8 [G,N,K/2], scales uint8 [G,N,K/16], global
+    float32 [G]."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, global_scale: torch.Tensor):
+        if codes.dim() != 3 or scales.dim() != 3 or global_scale.dim() != 1:
+            raise ValueError("codes/scales must be [G,N,K/2]/[G,N,K/16], global_scale [G]")
+        self.codes, self.scales, self.global_scale = codes, scales, global_scale
+        self.groups, self.rows, self.k = codes.shape[0], codes.shape[1], codes.shape[2] * 2
+        if tuple(scales.shape) != (self.groups, self.rows, self.k // 16) or global_scale.shape[0] != self.groups:
+            raise ValueError("inconsistent NVFP4 tensor shapes")
+
+    @classmethod
+    def from_numpy(cls, w, device="cuda"):
+        codes, scales, gs = w
+        return cls(torch.from_numpy(codes).to(device), torch.from_numpy(scales).to(device),
+                   torch.from_numpy(gs).to(device))
+
+    def desc(self) -> nvfp4_weights:
+        return nvfp4_weights(_dev(self.codes, "codes", torch.uint8), _dev(self.scales, "scales", torch.uint8),
+                             _dev(self.global_scale, "global_scale", torch.float32),
+                             self.groups, self.rows, self.k)
+
+
+def nvfp4_abi_version() -> int:
+    return lib().nvfp4_abi_version()
+
+
+def nvfp4_status_str(status: int) -> str:
+    return lib().nvfp4_status_str(int(status)).decode()
+
+
+def nvfp4_moe_plan_bytes(M: int, topk: int, E: int) -> int:
+    return int(lib().nvfp4_moe_plan_bytes(M, topk, E))
+
+
+def nvfp4_moe_plan(topk_ids: torch.Tensor, E: int, plan: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Build the routing plan of int32 ids [M, topk]; returns the plan buffer (int32 device tensor)."""
+    M, topk = topk_ids.shape
+    nbytes = nvfp4_moe_plan_bytes(M, topk, E)
+    if plan is None:
+        plan = torch.empty(max(nbytes, 4) // 4, dtype=torch.int32, device=topk_ids.device)
+    _check("nvfp4_moe_plan", lib().nvfp4_moe_plan(_dev(topk_ids, "topk_ids", torch.int32), M, topk, E,
+                                                  _dev(plan, "plan", torch.int32), plan.numel() * 4, _stream(stream)))
+    return plan
+
+
+def nvfp4_moe_w13_swiglu(plan: torch.Tensor, M: int, topk: int, E: int, x: torch.Tensor, w13: NVFP4Tensor,
+                         layout: int = 0, h: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Grouped W13 + SwiGLU. Returns h fp16 [M*topk, I] in bucket order (rows >= n_valid untouched)."""
+    I = w13.rows // 2
+    if h is None:
+        h = torch.empty((M * topk, I), dtype=torch.float16, device=x.device)
+    d = w13.desc()
+    _check("nvfp4_moe_w13_swiglu", lib().nvfp4_moe_w13_swiglu(
+        _dev(plan, "plan", torch.int32), M, topk, E, _dev(x, "x", torch.float16), C.byref(d), layout,
+        _dev(h, "h", torch.float16), _stream(stream)))
+    return h
+
+
+def nvfp4_moe_w2_workspace_bytes(M: int, topk: int, K: int) -> int:
+    return int(lib().nvfp4_moe_w2_workspace_bytes(M, topk, K))
+
+
+def nvfp4_moe_w2_reduce(plan: torch.Tensor, M: int, topk: int, E: int, h: torch.Tensor, w2: NVFP4Tensor,
+                        topk_weights: torch.Tensor, out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """Grouped W2 + slot-ordered top-k weighted reduction. Returns out fp16 [M, K]."""
+    K = w2.rows
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float16, device=h.device)
+    if ws is None:
+        ws = torch.empty(max(nvfp4_moe_w2_workspace_bytes(M, topk, K), 4), dtype=torch.uint8, device=h.device)
+    d = w2.desc()
+    _check("nvfp4_moe_w2_reduce", lib().nvfp4_moe_w2_reduce(
+        _dev(plan, "plan", torch.int32), M, topk, E, _dev(h, "h", torch.float16), C.byref(d),
+        _dev(topk_weights, "topk_weights", torch.float32), _dev(out, "out", torch.float16),
+        _dev(ws, "ws", ws.dtype), ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def nvfp4_linear(x: torch.Tensor, w: NVFP4Tensor, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Dense NVFP4 projection y = x W^T. x fp16 [M, K]; returns fp16 [M, N]."""
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, w.rows), dtype=torch.float16, device=x.device)
+    d = w.desc()
+    _check("nvfp4_linear", lib().nvfp4_linear(_dev(x, "x", torch.float16), M, C.byref(d),
+                                              _dev(y, "y", torch.float16), _stream(stream)))
+    return y
+
+
+class MoELayer:
+    """One MoE layer call (plan, W13+SwiGLU, W2+reduce) with its buffers allocated once, so the
+    three launches can be replayed (or captured in a HIP graph) without allocation."""
+
+    def __init__(self, M: int, topk: int, w13: NVFP4Tensor, w2: NVFP4Tensor, layout: int = 0, device="cuda"):
+        self.M, self.topk, self.E = M, topk, w13.groups
+        self.K, self.I = w13.k, w13.rows // 2
+        self.w13, self.w2, self.layout = w13, w2, layout
+        self.plan = torch.empty(max(nvfp4_moe_plan_bytes(M, topk, self.E), 4) // 4, dtype=torch.int32, device=device)
+        self.h = torch.empty((M * topk, self.I), dtype=torch.float16, device=device)
+        self.ws = torch.empty(max(nvfp4_moe_w2_workspace_bytes(M, topk, self.K), 4), dtype=torch.uint8, device=device)
+        self.out = torch.empty((M, self.K), dtype=torch.float16, device=device)
+
+    def __call__(self, x, topk_ids, topk_weights, w13: NVFP4Tensor | None = None, w2: NVFP4Tensor | None = None,
+                 stream=None):
+        nvfp4_moe_plan(topk_ids, self.E, plan=self.plan, stream=stream)
+        nvfp4_moe_w13_swiglu(self.plan, self.M, self.topk, self.E, x, w13 or self.w13, self.layout, h=self.h,
+                             stream=stream)
+        nvfp4_moe_w2_reduce(self.plan, self.M, self.topk, self.E, self.h, w2 or self.w2, topk_weights,
+                            out=self.out, ws=self.ws, stream=stream)
+        return self.out
+
+
+def plan_fields(plan: torch.Tensor, M: int, topk: int, E: int) -> dict:
+    """Slice a plan buffer (copied to the host) into its documented arrays (layout of nvfp4moe.h)."""
+    p = plan.cpu().numpy()
+    P = M * topk
+    A = min(E, P)
+    T = A + (P + 15) // 16
+    o = 16
+    f = {}
+    for name, n in (("counts", E), ("offsets", E + 1), ("active", A), ("tile_expert", T), ("tile_row0", T),
+                    ("sorted_pair", P), ("pos_of_pair", P)):
+        f[name] = p[o:o + n]
+        o += n
+    nv, na, nb, nt = (int(v) for v in p[0:4])
+    f.update(n_valid=nv, n_active=na, n_bad=nb, n_tiles=nt, hdr=p[:16])
+    f["sorted_pair"] = f["sorted_pair"][:nv]
+    f["active"] = f["active"][:na]
+    f["tile_expert"] = f["tile_expert"][:nt]
+    f["tile_row0"] = f["tile_row0"][:nt]
+    return f

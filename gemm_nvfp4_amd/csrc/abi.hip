@@ -1,0 +1,124 @@
+// abi.hip -- the exported C ABI (include/nvfp4moe.h): argument checks that fail closed, then the
+// kernel launches. Checks run on the host before anything is enqueued. Metadata gates that "fail
+// closed" are the pages' admission rule ("[Kernel][SM70] Improve Qwen3.8 no-MTP concurrency",
+// "Guarded production engine result").
+#include <stdint.h>
+
+#include "internal.hpp"
+
+#define NVFP4_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using nvfp4::PlanLayout;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool plan_shape_ok(int32_t M, int32_t topk, int32_t E)
+{
+    return M >= 0 && topk >= 1 && topk <= nvfp4::MAX_TOPK && E >= 1 && (int64_t)M * topk <= (int64_t(1) << 26);
+}
+
+int check_weights(const nvfp4_weights *w)
+{
+    if (!w || !w->codes || !w->scales || !w->global_scale) return NVFP4_ERR_NULL;
+    if (w->groups < 1 || w->rows < 1 || w->k < 16 || w->k % 16 != 0) return NVFP4_ERR_SHAPE;
+    if (!aligned(w->codes, 16) || !aligned(w->scales, 2) || !aligned(w->global_scale, 4)) return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+}  // namespace
+
+NVFP4_API int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+NVFP4_API const char *nvfp4_status_str(int status)
+{
+    switch (status) {
+    case NVFP4_OK: return "NVFP4_OK";
+    case NVFP4_ERR_NULL: return "NVFP4_ERR_NULL";
+    case NVFP4_ERR_SHAPE: return "NVFP4_ERR_SHAPE";
+    case NVFP4_ERR_ALIGN: return "NVFP4_ERR_ALIGN";
+    case NVFP4_ERR_WORKSPACE: return "NVFP4_ERR_WORKSPACE";
+    case NVFP4_ERR_UNSUPPORTED: return "NVFP4_ERR_UNSUPPORTED";
+    case NVFP4_ERR_LAUNCH: return "NVFP4_ERR_LAUNCH";
+    default: return "NVFP4_ERR_UNKNOWN";
+    }
+}
+
+NVFP4_API size_t nvfp4_moe_plan_bytes(int32_t M, int32_t topk, int32_t E)
+{
+    if (!plan_shape_ok(M, topk, E)) return 0;
+    return (size_t)nvfp4::plan_layout(M, topk, E).words * sizeof(int32_t);
+}
+
+NVFP4_API int nvfp4_moe_plan(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E, void *plan,
+                             size_t plan_bytes, void *stream)
+{
+    if (!plan_shape_ok(M, topk, E)) return NVFP4_ERR_SHAPE;
+    if (E > nvfp4::MAX_EXPERTS) return NVFP4_ERR_UNSUPPORTED;
+    if (M == 0) return NVFP4_OK;
+    if (!topk_ids || !plan) return NVFP4_ERR_NULL;
+    if (!aligned(topk_ids, 4) || !aligned(plan, 16)) return NVFP4_ERR_ALIGN;
+    const PlanLayout L = nvfp4::plan_layout(M, topk, E);
+    if (plan_bytes < (size_t)L.words * sizeof(int32_t)) return NVFP4_ERR_WORKSPACE;
+    return nvfp4::run_plan(topk_ids, M, topk, E, static_cast<int32_t *>(plan), L, static_cast<hipStream_t>(stream));
+}
+
+NVFP4_API int nvfp4_moe_w13_swiglu(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16_t *x,
+                                   const nvfp4_weights *w13, int32_t layout, uint16_t *h, void *stream)
+{
+    if (!plan_shape_ok(M, topk, E)) return NVFP4_ERR_SHAPE;
+    if (layout != 0 && layout != 1) return NVFP4_ERR_SHAPE;
+    if (E > nvfp4::MAX_EXPERTS) return NVFP4_ERR_UNSUPPORTED;
+    int st = check_weights(w13);
+    if (st != NVFP4_OK) return st;
+    if (w13->groups != E || w13->rows % 2 != 0) return NVFP4_ERR_SHAPE;
+    const int K = w13->k, I = w13->rows / 2;
+    if (K % 128 != 0 || K > nvfp4::MAX_MOE_RED || I % 16 != 0) return NVFP4_ERR_UNSUPPORTED;
+    if (M == 0) return NVFP4_OK;
+    if (!plan || !x || !h) return NVFP4_ERR_NULL;
+    if (!aligned(plan, 16) || !aligned(x, 16) || !aligned(h, 16)) return NVFP4_ERR_ALIGN;
+    const PlanLayout L = nvfp4::plan_layout(M, topk, E);
+    return nvfp4::run_w13(nvfp4::plan_view(plan, L), L.A, topk, x, *w13, layout, h, static_cast<hipStream_t>(stream));
+}
+
+NVFP4_API size_t nvfp4_moe_w2_workspace_bytes(int32_t M, int32_t topk, int32_t K)
+{
+    if (M < 0 || topk < 1 || topk > nvfp4::MAX_TOPK || K < 1) return 0;
+    const size_t b = (size_t)M * topk * K * sizeof(float);
+    return (b + 255) & ~(size_t)255;
+}
+
+NVFP4_API int nvfp4_moe_w2_reduce(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16_t *h,
+                                  const nvfp4_weights *w2, const float *topk_weights, uint16_t *out, void *ws,
+                                  size_t ws_bytes, void *stream)
+{
+    if (!plan_shape_ok(M, topk, E)) return NVFP4_ERR_SHAPE;
+    if (E > nvfp4::MAX_EXPERTS) return NVFP4_ERR_UNSUPPORTED;
+    int st = check_weights(w2);
+    if (st != NVFP4_OK) return st;
+    if (w2->groups != E) return NVFP4_ERR_SHAPE;
+    const int K = w2->rows, I = w2->k;
+    if (I % 128 != 0 || I > nvfp4::MAX_MOE_RED || K % 64 != 0) return NVFP4_ERR_UNSUPPORTED;
+    if (M == 0) return NVFP4_OK;
+    if (!plan || !h || !topk_weights || !out || !ws) return NVFP4_ERR_NULL;
+    if (!aligned(plan, 16) || !aligned(h, 16) || !aligned(out, 16) || !aligned(ws, 16) || !aligned(topk_weights, 4))
+        return NVFP4_ERR_ALIGN;
+    if (ws_bytes < nvfp4_moe_w2_workspace_bytes(M, topk, K)) return NVFP4_ERR_WORKSPACE;
+    const PlanLayout L = nvfp4::plan_layout(M, topk, E);
+    return nvfp4::run_w2(nvfp4::plan_view(plan, L), L.A, M, topk, h, *w2, topk_weights, out,
+                         static_cast<float *>(ws), static_cast<hipStream_t>(stream));
+}
+
+NVFP4_API int nvfp4_linear(const uint16_t *x, int32_t M, const nvfp4_weights *w, uint16_t *y, void *stream)
+{
+    if (M < 0) return NVFP4_ERR_SHAPE;
+    int st = check_weights(w);
+    if (st != NVFP4_OK) return st;
+    if (w->groups != 1) return NVFP4_ERR_SHAPE;
+    if (w->k % 128 != 0 || w->k > nvfp4::MAX_LINEAR_K || w->rows % 16 != 0) return NVFP4_ERR_UNSUPPORTED;
+    if (M == 0) return NVFP4_OK;
+    if (!x || !y) return NVFP4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(y, 16)) return NVFP4_ERR_ALIGN;
+    return nvfp4::run_linear(x, M, *w, y, static_cast<hipStream_t>(stream));
+}

@@ -1,0 +1,92 @@
+// internal.hpp -- declarations shared by the host ABI (abi.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+#include "../../include/nvfp4moe.h"
+
+namespace nvfp4 {
+
+// Word offsets of the routing plan's arrays inside the caller's plan buffer; the layout is the one
+// documented with nvfp4_moe_plan in nvfp4moe.h. P = M*topk pairs, A = min(E, P) active-expert
+// bound, T = A + ceil(P/16) row-tile bound. Plans with P > SMALL_PLAN_PAIRS also carry scratch:
+// per-chunk expert histograms hist[E][G] (G = ceil(P/PLAN_CHUNK)) and per-chunk bad-id counts.
+constexpr int PLAN_HDR_WORDS = 16;
+constexpr int PLAN_TILE_ROWS = 16;
+constexpr int SMALL_PLAN_PAIRS = 1024;
+constexpr int PLAN_CHUNK = 256;
+constexpr int MAX_EXPERTS = 4096;
+constexpr int MAX_TOPK = 32;
+// Largest reduction lengths with a kernel: the MoE kernels split at most four 512-element chunks
+// over a block's waves; the dense kernel keeps one LDS partial tile per chunk.
+constexpr int MAX_MOE_RED = 2048;
+constexpr int MAX_LINEAR_K = 32768;
+
+struct PlanLayout {
+    int64_t P, A, T, G;
+    int64_t hdr, counts, offsets, active, tile_expert, tile_row0, sorted_pair, pos_of_pair, hist, badc, words;
+};
+
+inline PlanLayout plan_layout(int32_t M, int32_t topk, int32_t E)
+{
+    PlanLayout L{};
+    L.P = (int64_t)M * topk;
+    L.A = L.P < E ? L.P : E;
+    L.T = L.A + (L.P + PLAN_TILE_ROWS - 1) / PLAN_TILE_ROWS;
+    L.G = L.P > SMALL_PLAN_PAIRS ? (L.P + PLAN_CHUNK - 1) / PLAN_CHUNK : 0;
+    int64_t o = 0;
+    L.hdr = o;         o += PLAN_HDR_WORDS;
+    L.counts = o;      o += E;
+    L.offsets = o;     o += E + 1;
+    L.active = o;      o += L.A;
+    L.tile_expert = o; o += L.T;
+    L.tile_row0 = o;   o += L.T;
+    L.sorted_pair = o; o += L.P;
+    L.pos_of_pair = o; o += L.P;
+    L.hist = o;        o += (int64_t)E * L.G;
+    L.badc = o;        o += L.G;
+    L.words = (o + 63) & ~(int64_t)63;  // whole 256-byte lines
+    return L;
+}
+
+// Read-only device view of a built plan.
+struct PlanView {
+    const int32_t *hdr, *counts, *offsets, *active, *tile_expert, *tile_row0, *sorted_pair, *pos_of_pair;
+};
+
+inline PlanView plan_view(const void *plan, const PlanLayout &L)
+{
+    const int32_t *p = static_cast<const int32_t *>(plan);
+    return PlanView{p + L.hdr, p + L.counts, p + L.offsets, p + L.active, p + L.tile_expert,
+                    p + L.tile_row0, p + L.sorted_pair, p + L.pos_of_pair};
+}
+
+// Launch `kernel` through hipLaunchKernel, so a rejected launch is reported as a status instead
+// of being left in the runtime's sticky last-error slot.
+template <typename... KArgs, typename... Args>
+inline int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem, hipStream_t s, Args &&...args)
+{
+    std::tuple<KArgs...> held(std::forward<Args>(args)...);
+    void *argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+    std::apply([&](auto &...a) {
+        int i = 0;
+        ((argv[i++] = static_cast<void *>(&a)), ...);
+    }, held);
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, shmem, s);
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+// Kernel launchers, one per translation unit. Arguments are validated by the caller (abi.hip).
+int run_plan(const int32_t *ids, int32_t M, int32_t topk, int32_t E, int32_t *plan, const PlanLayout &L,
+             hipStream_t s);
+int run_w13(const PlanView &pv, int64_t a_max, int32_t topk, const uint16_t *x, const nvfp4_weights &w,
+            int32_t layout, uint16_t *h, hipStream_t s);
+int run_w2(const PlanView &pv, int64_t a_max, int32_t M, int32_t topk, const uint16_t *h, const nvfp4_weights &w,
+           const float *topk_weights, uint16_t *out, float *ws, hipStream_t s);
+int run_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, uint16_t *y, hipStream_t s);
+
+}  // namespace nvfp4

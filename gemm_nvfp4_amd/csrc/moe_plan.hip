@@ -1,0 +1,249 @@
+// moe_plan.hip -- routing plan: top-k id histogram, prefix-sum expert bucketing and a stable
+// scatter into bucket order. W13 and W2 both reuse this integer plan, so planning happens once
+// ("grouped W2 reusing the same integer plan ... avoids repeated planning", "[Kernel][SM70] Improve
+// Qwen3.8 no-MTP concurrency", "Scope and related PRs").
+//
+// The plan is a stable counting sort of the valid (token, slot) pairs by expert; ties keep
+// ascending pair index p = t*topk + k. That makes it unique, and every path below produces it
+// bit-exactly.
+//   - Small path, P <= 1024 pairs (the decode regime): one 1024-thread block builds everything
+//     in LDS in one launch. At M = 1 the number of launches dominates the cost.
+//   - Large path (prefill): pairs are cut into chunks of 256, each with its own expert histogram.
+//     A per-expert scan over chunks gives every (expert, chunk) its start. Within a chunk a
+//     pair's rank counts the earlier pairs of the same expert, so the scatter is stable with no
+//     atomics on positions. Four launches, none of which is serial over the pairs.
+#include "internal.hpp"
+
+namespace nvfp4 {
+namespace {
+
+// Inclusive scan of one int across a wave64.
+__device__ __forceinline__ int wave_incl_scan(int v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(v, o, 64);
+        if (lane >= o) v += y;
+    }
+    return v;
+}
+
+// Exclusive scan of one int per thread over a block of nwaves*64 threads. `wsum` is LDS scratch
+// of at least nwaves ints. Ends with a barrier, so `wsum` can be reused at once.
+__device__ __forceinline__ int block_excl_scan(int v, int *wsum, int nwaves, int *total)
+{
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int incl = wave_incl_scan(v);
+    if (lane == 63) wsum[wid] = incl;
+    __syncthreads();
+    int pre = 0, tot = 0;
+    for (int w = 0; w < nwaves; ++w) {
+        const int s = wsum[w];
+        pre += (w < wid) ? s : 0;
+        tot += s;
+    }
+    __syncthreads();
+    *total = tot;
+    return pre + incl - v;
+}
+
+// Writes counts, offsets, the active list, the row-tile list and header words 0,1,3 from per-expert
+// counts `cnt` (LDS or global). Also leaves offsets in `off_lds` (E+1 ints of LDS) for the
+// caller. Runs on a 1024-thread block; E <= 4096, so each thread owns up to 4 consecutive experts.
+__device__ void build_lists(const int *cnt, int E, int32_t *plan, const PlanLayout &L, int *off_lds, int *wsum)
+{
+    const int ept = (E + 1023) / 1024;
+    const int e0 = threadIdx.x * ept;
+    int c[4], csum = 0, asum = 0, tsum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = e0 + i;
+        c[i] = (i < ept && e < E) ? cnt[e] : 0;
+        csum += c[i];
+        asum += c[i] > 0;
+        tsum += (c[i] + PLAN_TILE_ROWS - 1) / PLAN_TILE_ROWS;
+    }
+    int ctot, atot, ttot;
+    int cpre = block_excl_scan(csum, wsum, 16, &ctot);
+    int apre = block_excl_scan(asum, wsum, 16, &atot);
+    int tpre = block_excl_scan(tsum, wsum, 16, &ttot);
+    int32_t *counts = plan + L.counts, *offsets = plan + L.offsets, *active = plan + L.active;
+    int32_t *tile_e = plan + L.tile_expert, *tile_r = plan + L.tile_row0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = e0 + i;
+        if (i >= ept || e >= E) continue;
+        counts[e] = c[i];
+        offsets[e] = cpre;
+        off_lds[e] = cpre;
+        if (c[i] > 0) {
+            active[apre++] = e;
+            for (int r = 0; r < c[i]; r += PLAN_TILE_ROWS) {
+                tile_e[tpre] = e;
+                tile_r[tpre] = r;
+                ++tpre;
+            }
+        }
+        cpre += c[i];
+    }
+    if (threadIdx.x == 0) {
+        offsets[E] = ctot;
+        off_lds[E] = ctot;
+        int32_t *hdr = plan + L.hdr;
+        hdr[0] = ctot;
+        hdr[1] = atot;
+        hdr[3] = ttot;
+    }
+}
+
+__device__ __forceinline__ void write_header_tail(int32_t *plan, const PlanLayout &L, int n_bad, int M, int topk, int E)
+{
+    int32_t *hdr = plan + L.hdr;
+    hdr[2] = n_bad;
+    hdr[4] = M;
+    hdr[5] = topk;
+    hdr[6] = E;
+    hdr[7] = PLAN_TILE_ROWS;
+}
+
+// ---- small path: P <= 1024, one block -----------------------------------------------------------
+__global__ __launch_bounds__(1024) void plan_small_kernel(const int32_t *__restrict__ ids, int M, int topk, int E,
+                                                          int32_t *__restrict__ plan, PlanLayout L)
+{
+    __shared__ int cnt[MAX_EXPERTS];
+    __shared__ int off[MAX_EXPERTS + 1];
+    __shared__ int id_s[SMALL_PLAN_PAIRS];
+    __shared__ int wsum[16];
+    __shared__ int bad;
+    const int tid = threadIdx.x;
+    const int P = (int)L.P;
+    for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+    if (tid == 0) bad = 0;
+    __syncthreads();
+    int id = -1;
+    if (tid < P) {
+        const int raw = ids[tid];
+        const bool valid = raw >= 0 && raw < E;
+        id = valid ? raw : -1;
+        id_s[tid] = id;
+        if (valid) atomicAdd(&cnt[raw], 1);
+        else if (raw != -1) atomicAdd(&bad, 1);
+    }
+    __syncthreads();
+    build_lists(cnt, E, plan, L, off, wsum);
+    __syncthreads();
+    if (tid < P) {
+        int32_t *sorted_pair = plan + L.sorted_pair, *pos_of_pair = plan + L.pos_of_pair;
+        if (id >= 0) {
+            int rank = 0;
+            for (int j = 0; j < tid; ++j) rank += (id_s[j] == id);
+            const int pos = off[id] + rank;
+            sorted_pair[pos] = tid;
+            pos_of_pair[tid] = pos;
+        } else {
+            pos_of_pair[tid] = -1;
+        }
+    }
+    if (tid == 0) write_header_tail(plan, L, bad, M, topk, E);
+}
+
+// ---- large path ---------------------------------------------------------------------------------
+// 1) per-chunk histograms hist[e][g] and bad-id counts badc[g].
+__global__ __launch_bounds__(PLAN_CHUNK) void plan_hist_kernel(const int32_t *__restrict__ ids, int E,
+                                                               int32_t *__restrict__ plan, PlanLayout L)
+{
+    __shared__ int cnt[MAX_EXPERTS];
+    __shared__ int bad;
+    const int g = blockIdx.x, tid = threadIdx.x;
+    for (int e = tid; e < E; e += PLAN_CHUNK) cnt[e] = 0;
+    if (tid == 0) bad = 0;
+    __syncthreads();
+    const int64_t p = (int64_t)g * PLAN_CHUNK + tid;
+    if (p < L.P) {
+        const int raw = ids[p];
+        if (raw >= 0 && raw < E) atomicAdd(&cnt[raw], 1);
+        else if (raw != -1) atomicAdd(&bad, 1);
+    }
+    __syncthreads();
+    int32_t *hist = plan + L.hist;
+    for (int e = tid; e < E; e += PLAN_CHUNK) hist[(int64_t)e * L.G + g] = cnt[e];
+    if (tid == 0) plan[L.badc + g] = bad;
+}
+
+// 2) one wave per expert: hist[e][g] becomes the exclusive prefix over chunks; counts[e] = total.
+__global__ __launch_bounds__(256) void plan_scan_chunks_kernel(int E, int32_t *__restrict__ plan, PlanLayout L)
+{
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (e >= E) return;
+    int32_t *row = plan + L.hist + (int64_t)e * L.G;
+    int running = 0;
+    for (int64_t g0 = 0; g0 < L.G; g0 += 64) {
+        const bool in = g0 + lane < L.G;
+        const int v = in ? row[g0 + lane] : 0;
+        const int incl = wave_incl_scan(v);
+        if (in) row[g0 + lane] = running + incl - v;
+        running += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) plan[L.counts + e] = running;
+}
+
+// 3) one block: offsets, active list, tiles and the header.
+__global__ __launch_bounds__(1024) void plan_lists_kernel(int M, int topk, int E, int32_t *__restrict__ plan, PlanLayout L)
+{
+    __shared__ int off[MAX_EXPERTS + 1];
+    __shared__ int wsum[16];
+    __shared__ int cnt[MAX_EXPERTS];
+    for (int e = threadIdx.x; e < E; e += 1024) cnt[e] = plan[L.counts + e];
+    int bad = 0;
+    for (int64_t g = threadIdx.x; g < L.G; g += 1024) bad += plan[L.badc + g];
+    __syncthreads();
+    build_lists(cnt, E, plan, L, off, wsum);
+    int total_bad;
+    block_excl_scan(bad, wsum, 16, &total_bad);
+    if (threadIdx.x == 0) write_header_tail(plan, L, total_bad, M, topk, E);
+}
+
+// 4) stable scatter: position = offsets[e] + chunk prefix[e][g] + rank among the chunk's earlier
+//    pairs of expert e.
+__global__ __launch_bounds__(PLAN_CHUNK) void plan_scatter_kernel(const int32_t *__restrict__ ids, int E,
+                                                                  int32_t *__restrict__ plan, PlanLayout L)
+{
+    __shared__ int id_s[PLAN_CHUNK];
+    const int g = blockIdx.x, tid = threadIdx.x;
+    const int64_t p = (int64_t)g * PLAN_CHUNK + tid;
+    int id = -1;
+    if (p < L.P) {
+        const int raw = ids[p];
+        id = (raw >= 0 && raw < E) ? raw : -1;
+    }
+    id_s[tid] = id;
+    __syncthreads();
+    if (p >= L.P) return;
+    if (id < 0) {
+        plan[L.pos_of_pair + p] = -1;
+        return;
+    }
+    int rank = 0;
+    for (int j = 0; j < tid; ++j) rank += (id_s[j] == id);
+    const int pos = plan[L.offsets + id] + plan[L.hist + (int64_t)id * L.G + g] + rank;
+    plan[L.sorted_pair + pos] = (int32_t)p;
+    plan[L.pos_of_pair + p] = pos;
+}
+
+}  // namespace
+
+int run_plan(const int32_t *ids, int32_t M, int32_t topk, int32_t E, int32_t *plan, const PlanLayout &L, hipStream_t s)
+{
+    if (L.P <= SMALL_PLAN_PAIRS)
+        return launch(plan_small_kernel, dim3(1), dim3(1024), 0, s, ids, M, topk, E, plan, L);
+    const unsigned G = (unsigned)L.G;
+    int st = launch(plan_hist_kernel, dim3(G), dim3(PLAN_CHUNK), 0, s, ids, E, plan, L);
+    if (st == NVFP4_OK) st = launch(plan_scan_chunks_kernel, dim3((E + 3) / 4), dim3(256), 0, s, E, plan, L);
+    if (st == NVFP4_OK) st = launch(plan_lists_kernel, dim3(1), dim3(1024), 0, s, M, topk, E, plan, L);
+    if (st == NVFP4_OK) st = launch(plan_scatter_kernel, dim3(G), dim3(PLAN_CHUNK), 0, s, ids, E, plan, L);
+    return st;
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,155 @@
+/*
+ * nvfp4moe.h -- C ABI of the MI355X (gfx950) NVFP4 weight-only MoE / projection library.
+ *
+ * The operations follow three public pull-request pages of the 1Cat-vLLM project.
+ *   "[Kernel][SM70] Improve Qwen3.8 no-MTP concurrency", sections "Scope and related PRs", "Test
+ *   Result" and "Latest grouped-MoE screen": native NVFP4 weights with FP16 activations. Expert
+ *   dispatch runs an expert-grouped W13 with fused SiLU(gate)*up, then a grouped W2 and its
+ *   reduction. Both reuse one integer routing plan, so planning is not repeated. W13 has two
+ *   physical layouts. Metadata checks fail closed.
+ *   "[SM70][Draft] Extend Qwen3.8 DFlash2 concurrency paths", sections "Purpose" and "TP4-only
+ *   NVFP4 verifier follow-up": the dense "QPN" NVFP4 projection for small M, and its batch
+ *   invariance (an M-row result equals the concatenated 8-row results, bitwise).
+ *
+ * Number format (NVFP4). The pages name NVFP4 but print no layout. This library uses the
+ * standard one, the plainest reading:
+ *   codes   uint8  [groups][rows][k/2]   two OCP E2M1 codes per byte; even k in the low nibble
+ *   scales  uint8  [groups][rows][k/16]  one OCP E4M3FN byte per 16-element K-block
+ *   global  float  [groups]              one FP32 global scale per group (per expert, or 1 for a
+ *                                         dense weight)
+ *   w[g][n][k] = e2m1(code) * e4m3(scale[g][n][k/16]) * global[g]
+ * Activations and outputs are IEEE binary16 (passed as uint16_t bit patterns); accumulation is FP32.
+ *
+ * Conventions for every entry point:
+ *   - Every pointer argument except `w` descriptors and the stream is a DEVICE pointer. The
+ *     nvfp4_weights descriptor itself is read on the host during the call; the pointers inside it
+ *     are device pointers.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls only enqueue work
+ *     on it: no host synchronisation, no device allocation, no device-to-host copy. Every call can
+ *     therefore be captured in a HIP graph.
+ *   - The caller allocates and owns every buffer (plan, workspace, outputs). The library keeps no
+ *     pointer after a call returns and holds no mutable global state, so calls from several host
+ *     threads on different streams are safe. Two calls that write the same buffer must be ordered
+ *     by the caller (for example, the same stream).
+ *   - Errors fail closed: a nonzero status is returned, nothing is enqueued, and no output is
+ *     touched. Status codes are NVFP4_* below; nvfp4_status_str() names them.
+ *   - M = 0 is a successful no-op.
+ *   - Arithmetic does not depend on M or on other tokens. A token's output is bitwise the same
+ *     whether it runs alone or in any batch (for the MoE: with the same routing row and weights).
+ */
+#ifndef NVFP4MOE_H
+#define NVFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+enum {
+    NVFP4_OK = 0,
+    NVFP4_ERR_NULL = 1,        /* a required pointer is NULL                                   */
+    NVFP4_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes                           */
+    NVFP4_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned                              */
+    NVFP4_ERR_WORKSPACE = 4,   /* plan or workspace buffer smaller than the *_bytes() size      */
+    NVFP4_ERR_UNSUPPORTED = 5, /* a valid shape for which no kernel is built (see each call)    */
+    NVFP4_ERR_LAUNCH = 6       /* the HIP runtime rejected a launch                             */
+};
+
+/* A quantized weight tensor: `groups` matrices of `rows` x `k`. */
+typedef struct nvfp4_weights {
+    const uint8_t *codes;       /* device, [groups][rows][k/2], 16-byte aligned                */
+    const uint8_t *scales;      /* device, [groups][rows][k/16], 2-byte aligned                */
+    const float *global_scale;  /* device, [groups]                                            */
+    int32_t groups, rows, k;
+} nvfp4_weights;
+
+/* ABI version of the loaded library (NVFP4_ABI_VERSION). A caller checks it before use
+ * ("native ABI capability check", DFlash2 page, "Purpose"). */
+int nvfp4_abi_version(void);
+
+/* Static, NUL-terminated name of a status code. Never NULL. */
+const char *nvfp4_status_str(int status);
+
+/* ---------------------------------------------------------------------------------------------
+ * Routing plan ("grouped W2 reusing the same integer plan", no-MTP page, "Scope and related PRs").
+ *
+ * Input topk_ids int32 [M][topk]. Pair p = t*topk + k. An id in [0, E) routes the pair to that
+ * expert. -1 means "no expert", and the pair is skipped. Any other id is also skipped and is
+ * counted in the plan's bad-id word. The plan is a stable counting sort of the valid pairs by
+ * expert (ties by ascending p), so it is unique and the device result is bit-exact.
+ *
+ * Plan layout (int32 words, from the start of `plan`; P = M*topk, A = min(E, P),
+ * T = A + ceil(P/16)):
+ *   [0] n_valid  [1] n_active  [2] n_bad  [3] n_tiles  [4] M  [5] topk  [6] E  [7] 16 (tile rows)
+ *   [8..15] reserved
+ *   counts[E]  offsets[E+1]  active[A]  tile_expert[T]  tile_row0[T]  sorted_pair[P]  pos_of_pair[P]
+ *   followed by internal scratch when P > 1024.
+ * Within each array only the first n_valid / n_active / n_tiles entries are defined. pos_of_pair[p]
+ * is the bucket-order row of pair p, or -1 if the pair was skipped. Active experts are in
+ * ascending id order, and row tiles of 16 rows are in (expert, row0) order.
+ *
+ * The plan stays valid until the caller overwrites it. W13 and W2 only read it, and must be given
+ * the same M, topk and E. Requirements: 1 <= topk <= 32, 1 <= E <= 4096, M*topk <= 2^26.
+ * --------------------------------------------------------------------------------------------- */
+size_t nvfp4_moe_plan_bytes(int32_t M, int32_t topk, int32_t E);
+int nvfp4_moe_plan(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E,
+                   void *plan, size_t plan_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Grouped W13 with fused SwiGLU (the "expert-grouped multi-row W13/SiLU", no-MTP page, "Scope and
+ * related PRs").
+ *   x    fp16 [M][K]          activations (K = w13->k)
+ *   w13  groups = E, rows = 2I, k = K
+ *        layout 0: gate rows [0, I), up rows [I, 2I)
+ *        layout 1: interleaved, row 2i is gate i and row 2i+1 is up i
+ *        (the page's "same-split W13 in both physical layouts", "Test Result")
+ *   h    fp16 [M*topk][I]      output, in bucket order: row j is pair sorted_pair[j]
+ * For bucket row j with pair p = (t, k) and expert e:
+ *   g = global[e] * sum_k x[t,k] * e2m1*e4m3 (gate row),  u = likewise (up row),
+ *   h[j][i] = fp16_rne( silu(g) * u ),  silu(g) = g / (1 + exp(-g)),  all FP32.
+ * Each active expert's weights are read once, for all of its pairs. Rows j >= n_valid are not
+ * written.
+ * Requirements: K % 128 == 0 and K <= 2048; I % 16 == 0; x, h, codes 16-byte aligned.
+ * --------------------------------------------------------------------------------------------- */
+int nvfp4_moe_w13_swiglu(const void *plan, int32_t M, int32_t topk, int32_t E,
+                         const uint16_t *x, const nvfp4_weights *w13, int32_t layout,
+                         uint16_t *h, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Grouped W2 with the top-k-weighted reduction ("W2/reduction fusion", no-MTP page, "Scope and
+ * related PRs").
+ *   h             fp16 [M*topk][I]  W13 output in bucket order
+ *   w2            groups = E, rows = K, k = I
+ *   topk_weights  fp32 [M][topk]    used exactly as given (no renormalisation)
+ *   out           fp16 [M][K]       every element is written
+ *   ws            device workspace of at least nvfp4_moe_w2_workspace_bytes(M, topk, K) bytes,
+ *                 contents ignored on entry (FP32 per-pair partials)
+ * y[j][n] = global[e] * sum_i dq(W2_e)[n][i] * h[j][i], in FP32 with no intermediate rounding. Then
+ *   out[t][n] = fp16_rne( s ),  s = 0;  for k = 0..topk-1 with a valid id: s = fmaf(w[t][k], y[pos][n], s)
+ * This is slot order. A token with no valid slot gets +0.
+ * Requirements: I % 128 == 0 and I <= 2048; K % 64 == 0; h, out, codes 16-byte aligned.
+ * --------------------------------------------------------------------------------------------- */
+size_t nvfp4_moe_w2_workspace_bytes(int32_t M, int32_t topk, int32_t K);
+int nvfp4_moe_w2_reduce(const void *plan, int32_t M, int32_t topk, int32_t E,
+                        const uint16_t *h, const nvfp4_weights *w2, const float *topk_weights,
+                        uint16_t *out, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Dense NVFP4 projection (the "QPN" projection, DFlash2 page, "Purpose" and "TP4-only NVFP4
+ * verifier follow-up"):
+ *   y[m][n] = fp16_rne( global * sum_k x[m][k] * e2m1*e4m3 ),  FP32 accumulation.
+ *   x  fp16 [M][K],  w  groups = 1, rows = N, k = K,  y  fp16 [M][N].
+ * Any M works. The streaming kernel is tuned for M <= 32, the pages' admitted range.
+ * Requirements: K % 128 == 0; N % 16 == 0; x, y, codes 16-byte aligned.
+ * --------------------------------------------------------------------------------------------- */
+int nvfp4_linear(const uint16_t *x, int32_t M, const nvfp4_weights *w, uint16_t *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4MOE_H */

@@ -64,7 +64,11 @@ def _p(a: np.ndarray):
 
 
 def _threads(n):
-    return int(n) if n else (os.cpu_count() or 1)
+    """Oracle threads: the argument, else OMP_NUM_THREADS, else the host's core count."""
+    if n:
+        return int(n)
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return int(env) if env.isdigit() and int(env) > 0 else (os.cpu_count() or 1)
 
 
 def e2m1(code: int) -> float:
