@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 grouped-MoE path on one MI355X.
+
+Headline workload: one rank's share of the 16-token grouped-MoE decode. That is 16 tokens, 512
+experts, top-10 uniform routing, hidden K = 2048, expert intermediate I = 512, NVFP4 W13/W2 and
+FP16 activations. One step is one MoE layer call: routing plan, grouped W13 + SwiGLU, grouped W2,
+and the top-k weighted reduction (4 kernels). Steps are captured in one HIP graph. They cycle
+through 48 seeded route patterns and through several distinct weight sets, so the 256 MB
+Infinity Cache cannot serve repeated weights (the rotating-weights lesson of the "[Kernel][SM70]
+Improve Qwen3.8 no-MTP concurrency" page, "Test Result").
+
+value = weight HBM GB/s: the bytes of the distinct active experts' weights (W13 1,179,648 B plus
+W2 589,824 B per expert) summed over the timed steps, divided by the timed wall time. The JSON line
+also carries:
+  - us_per_layer;
+  - the M = 1..16 sweep;
+  - the 8192-token prefill in TFLOP/s;
+  - the dense 4352x5120 projection;
+  - the roofline of the dominant kernel (grouped W13 + SwiGLU), timed with HIP events on its
+    launch stream;
+  - the fp64 CPU oracle timed on a bounded sample (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 MoE W13+W2 µs/layer + weight HBM GB/s (M=1..16), TFLOP/s at 8192 tok"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16 MFMA
+E, TOPK, K, I = 512, 10, 2048, 512
+W13_EXPERT_BYTES = 2 * I * K // 2 + 2 * I * K // 16   # 1,179,648
+W2_EXPERT_BYTES = K * I // 2 + K * I // 16            # 589,824
+EXPERT_BYTES = W13_EXPERT_BYTES + W2_EXPERT_BYTES     # 1,769,472
+FLOP_PER_PAIR = 6 * I * K                             # 2*2I*K (W13) + 2*K*I (W2)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=480)
+    p.add_argument("--warmup", type=int, default=48)
+    p.add_argument("--weight-sets", type=int, default=12)
+    p.add_argument("--patterns", type=int, default=48)
+    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+class Routes:
+    """Seeded route patterns for M tokens (device tensors + per-pattern active-expert counts)."""
+
+    def __init__(self, M, n, seed_base, routing="uniform"):
+        import torch
+        from synth import inputs as S
+        self.M, self.x, self.ids, self.tw, self.active, self.valid, self.np_ids = M, [], [], [], [], [], []
+        for p in range(n):
+            rng = S.rng_for(S.WORKLOAD_IDS["decode"] if M <= 16 else S.WORKLOAD_IDS["prefill"], 0, seed_base + p)
+            x = S.activations(rng, M, K)
+            ids = S.ROUTINGS[routing](rng, M, TOPK, E)
+            tw = S.softmax_weights(rng, M, TOPK)
+            self.np_ids.append(ids)
+            self.x.append(torch.from_numpy(x).cuda())
+            self.ids.append(torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda())
+            self.tw.append(torch.from_numpy(tw).cuda())
+            self.active.append(S.active_experts(ids, E))
+            self.valid.append(int(((ids >= 0) & (ids < E)).sum()))
+
+
+def time_graph(build_fn, steps, warmup_fn=None):
+    """Capture build_fn() (which enqueues `steps` steps) in one graph, replay once untimed, then time
+    one replay with HIP events on the replay stream. Returns elapsed ms."""
+    import torch
+    if warmup_fn is not None:
+        warmup_fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        build_fn()
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    del g
+    return ms
+
+
+def weight_sets(n, seed0=1000):
+    import gemm_nvfp4_amd as G
+    from synth import inputs as S
+    w13 = [G.NVFP4Tensor(*S.device_nvfp4_weights(seed0 + r, E, 2 * I, K)) for r in range(n)]
+    w2 = [G.NVFP4Tensor(*S.device_nvfp4_weights(seed0 + 500 + r, E, K, I)) for r in range(n)]
+    return w13, w2
+
+
+def moe_layer_timing(M, steps, warmup, W13, W2, routes):
+    """µs per MoE layer and weight GB/s over `steps` graph-captured layer calls."""
+    import gemm_nvfp4_amd as G
+    R, P = len(W13), len(routes.x)
+    layer = G.MoELayer(M, TOPK, W13[0], W2[0])
+
+    def step(i):
+        p = i % P
+        layer(routes.x[p], routes.ids[p], routes.tw[p], W13[i % R], W2[i % R])
+
+    def warm():
+        for i in range(warmup):
+            step(i)
+
+    ms = time_graph(lambda: [step(i) for i in range(steps)], steps, warm)
+    wbytes = sum(routes.active[i % P] * EXPERT_BYTES for i in range(steps))
+    pairs = sum(routes.valid[i % P] for i in range(steps))
+    us = ms * 1e3 / steps
+    return {"M": M, "us_per_layer": round(us, 3), "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tflops": round(pairs * FLOP_PER_PAIR / (ms * 1e-3) / 1e12, 2),
+            "mean_active_experts": round(float(np.mean(routes.active)), 2), "steps": steps}
+
+
+def w13_kernel_timing(M, launches, W13, routes):
+    """Average duration of the grouped W13 + SwiGLU kernel alone (HIP events around a graph of
+    back-to-back launches on the capture/replay stream) and its algorithmic bytes per launch."""
+    import torch
+    import gemm_nvfp4_amd as G
+    R, P = len(W13), len(routes.x)
+    plans, hs = [], []
+    for p in range(P):
+        plans.append(G.nvfp4_moe_plan(routes.ids[p], E))
+    h = torch.empty((M * TOPK, I), dtype=torch.float16, device="cuda")
+    torch.cuda.synchronize()
+
+    def build():
+        for i in range(launches):
+            p = i % P
+            G.nvfp4_moe_w13_swiglu(plans[p], M, TOPK, E, routes.x[p], W13[i % R], 0, h=h)
+
+    ms = time_graph(build, launches)
+    algo = [routes.active[p] * W13_EXPERT_BYTES + M * K * 2 + routes.valid[p] * I * 2 for p in range(P)]
+    bytes_per_launch = float(np.mean([algo[i % P] for i in range(launches)]))
+    us = ms * 1e3 / launches
+    return us, bytes_per_launch
+
+
+def launch_floor(launches=480):
+    import torch
+    t = torch.zeros(1, device="cuda")
+    ms = time_graph(lambda: [t.add_(1.0) for _ in range(launches)], launches)
+    return ms * 1e3 / launches
+
+
+def prefill_timing(W13, W2, steps=4):
+    import gemm_nvfp4_amd as G
+    M = 8192
+    routes = Routes(M, 2, 5000)
+    layer = G.MoELayer(M, TOPK, W13[0], W2[0])
+    R = len(W13)
+
+    def step(i):
+        layer(routes.x[i % 2], routes.ids[i % 2], routes.tw[i % 2], W13[i % R], W2[i % R])
+
+    ms = time_graph(lambda: [step(i) for i in range(steps)], steps, lambda: step(0))
+    pairs = sum(routes.valid[i % 2] for i in range(steps))
+    return {"M": M, "ms_per_layer": round(ms / steps, 3),
+            "tflops": round(pairs * FLOP_PER_PAIR / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(pairs * FLOP_PER_PAIR / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+            "gflop_per_layer": round(routes.valid[0] * FLOP_PER_PAIR / 1e9, 2)}
+
+
+def dense_timing(copies=64, launches=256):
+    import torch
+    import gemm_nvfp4_amd as G
+    from synth import inputs as S
+    N, Kd = S.DENSE_N, S.DENSE_K
+    ws = [G.NVFP4Tensor(*S.device_nvfp4_weights(7000 + c, 1, N, Kd)) for c in range(copies)]
+    wbytes = N * Kd // 2 + N * Kd // 16
+    res = []
+    for M in S.DENSE_MS:
+        x = torch.from_numpy(S.activations(S.rng_for(1, 0, 1000 + M), M, Kd)).cuda()
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        ms = time_graph(lambda: [G.nvfp4_linear(x, ws[i % copies], y=y) for i in range(launches)], launches)
+        us = ms * 1e3 / launches
+        res.append({"M": M, "us": round(us, 3), "weight_GBps": round(wbytes / (us * 1e-6) / 1e9, 1),
+                    "hbm_frac": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+    return res
+
+
+def cpu_baseline(W13, W2, seconds):
+    """The fp64 oracle (grouped form) on the headline workload's route patterns, on the host's
+    cores, for about `seconds` of CPU work; reported in the same unit (weight GB/s)."""
+    from oracle import oracle as O
+    from synth import inputs as S
+    w13 = tuple(t.cpu().numpy() for t in (W13[0].codes, W13[0].scales, W13[0].global_scale))
+    w2 = tuple(t.cpu().numpy() for t in (W2[0].codes, W2[0].scales, W2[0].global_scale))
+    threads = O._threads(None)
+    done, wbytes, t0 = 0, 0, time.perf_counter()
+    while True:
+        rng = S.rng_for(S.WORKLOAD_IDS["decode"], 0, 1000 + done)
+        case = {"shape": S.DECODE, "x": S.activations(rng, 16, K), "ids": S.routing_uniform(rng, 16, TOPK, E),
+                "topk_weights": S.softmax_weights(rng, 16, TOPK), "w13": w13, "w2": w2}
+        pl = O.plan(case["ids"], E, 16)
+        O.moe_grouped(case, pl, nthreads=threads)
+        done += 1
+        wbytes += pl["n_active"] * EXPERT_BYTES
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= 200:
+            break
+    return {"value": round(wbytes / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} route patterns of the 16-token decode layer (fp64 grouped oracle, "
+                      f"{el:.1f} s wall, {el / done * 1e3:.1f} ms per layer)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only; multi-GPU runs are not supported "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gemm_nvfp4_amd as G
+    G.lib()  # raises if the HIP library is not built
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+
+    W13, W2 = weight_sets(args.weight_sets)
+    torch.cuda.synchronize()
+    log(f"weight sets: {args.weight_sets} x {E * EXPERT_BYTES / 2**20:.0f} MiB")
+
+    routes16 = Routes(16, args.patterns, 1000)
+    head = moe_layer_timing(16, args.steps, args.warmup, W13, W2, routes16)
+    log(f"headline M=16: {head}")
+    k_us, k_bytes = w13_kernel_timing(16, args.steps, W13, routes16)
+    achieved = k_bytes / (k_us * 1e-6) / 1e9
+    log(f"w13 kernel: {k_us:.3f} us/launch, {k_bytes / 1e6:.2f} MB/launch -> {achieved:.1f} GB/s")
+    floor = launch_floor()
+    log(f"graph launch floor: {floor:.3f} us")
+
+    sweep = []
+    if not args.no_sweep:
+        for M in (1, 2, 4, 8, 16):
+            r = moe_layer_timing(M, args.steps, args.warmup, W13, W2, Routes(M, args.patterns, 3000 + 97 * M))
+            log(f"sweep: {r}")
+            sweep.append(r)
+    prefill = None
+    if not args.no_prefill:
+        prefill = prefill_timing(W13, W2)
+        log(f"prefill: {prefill}")
+    dense = None
+    if not args.no_dense:
+        dense = dense_timing()
+        log(f"dense: {dense}")
+    cpu = None if args.no_cpu else cpu_baseline(W13, W2, args.cpu_seconds)
+    if cpu:
+        log(f"cpu baseline: {cpu}")
+
+    ms_step = head["us_per_layer"] / 1e3
+    line = {
+        "metric": METRIC, "value": head["weight_GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "grouped NVFP4 MoE decode layer (plan + W13/SwiGLU + W2/reduce): 16 tokens, "
+                               "512 experts, top-10 uniform, K=2048, I=512",
+                   "tokens": 16, "experts": E, "topk": TOPK, "hidden": K, "intermediate": I,
+                   "weight_sets": args.weight_sets, "route_patterns": args.patterns},
+        "us_per_layer": head["us_per_layer"], "hbm_frac": head["hbm_frac"],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "w13_swiglu_kernel<4>", "us_per_launch": round(k_us, 3),
+                     "algorithmic_bytes_per_launch": round(k_bytes)},
+        "launch_floor_us": round(floor, 3),
+        "sweep": sweep, "prefill": prefill, "dense": dense, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -40,6 +40,8 @@ __all__ = [
     "DENSE_MS",
     "moe_case",
     "dense_case",
+    "device_nvfp4_weights",
+    "active_experts",
 ]
 
 # E4M3FN bytes of 2^u for integer u in [-8, -4]: 2^-8 and 2^-7 are E4M3 subnormals (0x02, 0x04),
@@ -178,3 +180,25 @@ def dense_case(m: int, n: int = DENSE_N, k: int = DENSE_K, weight_set: int = 0, 
     w = nvfp4_weights(rw, 1, n, k, scale_bytes, gscale)
     rx = rng_for(WORKLOAD_IDS["dense"], weight_set, 1000 + m)
     return {"x": activations(rx, m, k), "w": w}
+
+
+def device_nvfp4_weights(seed: int, groups: int, rows: int, k: int, device="cuda",
+                         scale_bytes: np.ndarray = SCALE_BYTES_POW2, gscale: float = 1.0):
+    """Bulk random NVFP4 storage drawn on the device with a seeded torch generator (for benchmark
+    weight sets, which are too large to draw on the host): uniform code bytes, scale bytes drawn
+    uniformly from ``scale_bytes``, constant global scale. Returns (codes, scales, gscale) tensors."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    codes = torch.randint(0, 256, (groups, rows, k // 2), dtype=torch.uint8, generator=g, device=device)
+    table = torch.as_tensor(np.asarray(scale_bytes, dtype=np.uint8), device=device)
+    idx = torch.randint(0, len(scale_bytes), (groups, rows, k // 16), generator=g, device=device)
+    scales = table[idx].contiguous()
+    gs = torch.full((groups,), gscale, dtype=torch.float32, device=device)
+    return codes, scales, gs
+
+
+def active_experts(ids: np.ndarray, e: int) -> int:
+    """Number of distinct valid expert ids in a routing (the experts whose weights a grouped layer reads)."""
+    v = ids[(ids >= 0) & (ids < e)]
+    return int(np.unique(v).size)
