@@ -23,7 +23,7 @@ int check_weights(const nvfp4_weights *w)
 {
     if (!w || !w->codes || !w->scales || !w->global_scale) return NVFP4_ERR_NULL;
     if (w->groups < 1 || w->rows < 1 || w->k < 16 || w->k % 16 != 0) return NVFP4_ERR_SHAPE;
-    if (!aligned(w->codes, 16) || !aligned(w->scales, 2) || !aligned(w->global_scale, 4)) return NVFP4_ERR_ALIGN;
+    if (!aligned(w->codes, 16) || !aligned(w->scales, 8) || !aligned(w->global_scale, 4)) return NVFP4_ERR_ALIGN;
     return NVFP4_OK;
 }
 
@@ -79,7 +79,7 @@ NVFP4_API int nvfp4_moe_w13_swiglu(const void *plan, int32_t M, int32_t topk, in
     if (!plan || !x || !h) return NVFP4_ERR_NULL;
     if (!aligned(plan, 16) || !aligned(x, 16) || !aligned(h, 16)) return NVFP4_ERR_ALIGN;
     const PlanLayout L = nvfp4::plan_layout(M, topk, E);
-    return nvfp4::run_w13(nvfp4::plan_view(plan, L), L.A, topk, x, *w13, layout, h, static_cast<hipStream_t>(stream));
+    return nvfp4::run_w13(nvfp4::plan_view(plan, L), L.T, topk, x, *w13, layout, h, static_cast<hipStream_t>(stream));
 }
 
 NVFP4_API size_t nvfp4_moe_w2_workspace_bytes(int32_t M, int32_t topk, int32_t K)
@@ -106,7 +106,7 @@ NVFP4_API int nvfp4_moe_w2_reduce(const void *plan, int32_t M, int32_t topk, int
         return NVFP4_ERR_ALIGN;
     if (ws_bytes < nvfp4_moe_w2_workspace_bytes(M, topk, K)) return NVFP4_ERR_WORKSPACE;
     const PlanLayout L = nvfp4::plan_layout(M, topk, E);
-    return nvfp4::run_w2(nvfp4::plan_view(plan, L), L.A, M, topk, h, *w2, topk_weights, out,
+    return nvfp4::run_w2(nvfp4::plan_view(plan, L), L.T, M, topk, h, *w2, topk_weights, out,
                          static_cast<float *>(ws), static_cast<hipStream_t>(stream));
 }
 

@@ -40,32 +40,24 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void linear_kernel(const f16 *__res
     for (int rt0 = 0; rt0 < row_tiles; rt0 += ROW_GROUP) {
         for (int c = wave; c < S; c += nwaves) {
             const int kb = c * KCHUNK;
-            const int nsb = min(KCHUNK / KSB, (K - kb) / KSB);
-            f16x8 bw[4][4];
-            RawSB raw[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                if (b < nsb) raw[b] = load_sb(cr, sr, kb + KSB * b, q);
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                if (b < nsb) decode_sb(raw[b], bw[b]);
+            const int groups = min(KCHUNK, K - kb) >> 7;  // 128-element lane groups with data
+            const bool qv = q < groups;
+            const RawChunk w = load_chunk(cr, sr, kb, qv ? q : groups - 1);
 #pragma unroll
             for (int r = 0; r < ROW_GROUP; ++r) {
                 const int rt = rt0 + r;
                 if (rt >= row_tiles) break;
                 const int m = rt * 16 + n;
-                const bool rv = m < M;
-                const f16 *xr = x + (size_t)(rv ? m : 0) * K;
+                const bool rv = m < M && qv;
+                const f16 *xr = x + (size_t)(m < M ? m : 0) * K;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    if (b < nsb) {
+                for (int b = 0; b < 4; ++b) {
+                    const f16x2 sc = chunk_scales(w, b);
 #pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            const f16x8 av = rv ? load_a(xr, kb + KSB * b, q, s) : zero8();
-                            acc = mfma_step(av, bw[b][s], acc);
-                        }
-                    }
+                    for (int s = 0; s < 4; ++s)
+                        acc = mfma_step(rv ? a_frag(xr, kb, q, b, s) : zero8(), b_frag(w, sc, b, s, qv), acc);
+                }
                 float *pc = part + ((size_t)c * ROW_GROUP + r) * 16 * LDS_ROW;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) pc[(4 * q + j) * LDS_ROW + n] = acc[j];

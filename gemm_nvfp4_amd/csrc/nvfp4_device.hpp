@@ -16,12 +16,15 @@
 // follow-up": the M-row output equals the concatenated smaller calls, bitwise.
 //   * The reduction axis is cut into chunks of KCHUNK = 512 elements. The last chunk may be
 //     shorter, always a multiple of 128.
-//   * Each chunk is one chain of v_mfma_f32_16x16x32_f16 steps, starting from +0.
+//   * Each chunk is one chain of 16 v_mfma_f32_16x16x32_f16 steps j = 4*b + s (b, s = 0..3),
+//     starting from +0.
 //   * Chunk results are added in FP32, left to right: ((c0 + c1) + c2) + ...
-//   * A chunk is a run of 128-element superblocks, each of 4 MFMA steps s = 0..3. In step s, lane
-//     group q = lane/16 feeds elements [128*b + 32*q + 8*s, +8) of superblock b. One 16-byte code
-//     load per lane per row therefore covers a whole superblock: 32 consecutive elements, one
-//     dword per step.
+//   * Lane group q = lane/16 owns the contiguous elements [128q, 128q + 128) of the chunk. In
+//     step (b, s) it feeds elements [128q + 32b + 8s, +8). Lane groups past the end of a short
+//     chunk feed exact zeros in both operands.
+//     Each lane therefore reads 64 contiguous code bytes (four 16-byte loads) and its 8 scale
+//     bytes (one 8-byte load) per row per chunk. Measured on MI355X, this beats a layout whose
+//     scales need four 2-byte loads.
 // The MFMA result for one output element depends only on its own A row, B column and C input,
 // never on its position inside the 16x16 tile (measured on MI355X). Padding rows never change
 // other rows.
@@ -39,7 +42,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KCHUNK = 512;  // elements per independent MFMA chain
-constexpr int KSB = 128;     // elements per superblock (4 MFMA steps)
 
 __host__ __device__ constexpr int num_chunks(int k) { return (k + KCHUNK - 1) / KCHUNK; }
 
@@ -71,38 +73,46 @@ __device__ __forceinline__ f16x8 decode8(uint32_t codes, f16 scale)
     return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// Raw packed data of one weight row for one superblock, as one lane loads it: 16 code bytes
-// (32 elements) and the two scale bytes that cover them.
-struct RawSB {
-    u32x4 codes;
-    uint32_t scale2;
+// One lane's packed data of one weight row for one chunk: 64 code bytes (128 elements, four
+// 16-byte loads) and the 8 E4M3 scale bytes that cover them (one 8-byte load).
+struct RawChunk {
+    u32x4 codes[4];     // codes[b].dword[s] = elements [kb + 128q + 32b + 8s, +8)
+    uint32_t scales[2]; // byte 2b + (s >> 1) scales step (b, s)
 };
 
-// Lane's share of superblock `sb` of one weight row. `row_codes` / `row_scales` point at the row's
-// first byte; `k0` is the superblock's first element (a multiple of 128); q = lane / 16.
-__device__ __forceinline__ RawSB load_sb(const uint8_t *row_codes, const uint8_t *row_scales, int k0, int q)
+// Lane's share of one weight row for the chunk starting at element kb (a multiple of 512).
+// `q_ld` is the lane group whose bytes are loaded (clamped into the chunk by the caller).
+__device__ __forceinline__ RawChunk load_chunk(const uint8_t *row_codes, const uint8_t *row_scales, int kb, int q_ld)
 {
-    RawSB r;
-    r.codes = *reinterpret_cast<const u32x4 *>(row_codes + (k0 >> 1) + 16 * q);
-    r.scale2 = *reinterpret_cast<const uint16_t *>(row_scales + (k0 >> 4) + 2 * q);
+    RawChunk r;
+    const uint8_t *c = row_codes + (kb >> 1) + 64 * q_ld;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) r.codes[b] = *reinterpret_cast<const u32x4 *>(c + 16 * b);
+    const uint2 sc = *reinterpret_cast<const uint2 *>(row_scales + (kb >> 4) + 8 * q_ld);
+    r.scales[0] = sc.x;
+    r.scales[1] = sc.y;
     return r;
 }
 
-// The four B fragments (steps 0..3) of a loaded superblock. Steps 0,1 use the first scale byte
-// (elements 32q..32q+15), steps 2,3 the second.
-__device__ __forceinline__ void decode_sb(const RawSB &r, f16x8 out[4])
+// The two block scales of load b (steps s = 0,1 and s = 2,3), as fp16.
+__device__ __forceinline__ f16x2 chunk_scales(const RawChunk &r, int b)
 {
-    const f16x2 s = e4m3_pair<false>(r.scale2);
-    out[0] = decode8(r.codes[0], s[0]);
-    out[1] = decode8(r.codes[1], s[0]);
-    out[2] = decode8(r.codes[2], s[1]);
-    out[3] = decode8(r.codes[3], s[1]);
+    const uint32_t w = r.scales[b >> 1];
+    return (b & 1) ? e4m3_pair<true>(w) : e4m3_pair<false>(w);
 }
 
-// A fragment of one activation row for superblock starting at element k0, step s.
-__device__ __forceinline__ f16x8 load_a(const f16 *row, int k0, int q, int s)
+// B fragment of step (b, s); `sc` = chunk_scales(r, b); lanes of a lane group past the chunk end
+// (qv false) give exact zeros.
+__device__ __forceinline__ f16x8 b_frag(const RawChunk &r, f16x2 sc, int b, int s, bool qv)
 {
-    return *reinterpret_cast<const f16x8 *>(row + k0 + 32 * q + 8 * s);
+    const f16x8 w = decode8(r.codes[b][s], sc[s >> 1]);
+    return qv ? w : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+}
+
+// A fragment of step (b, s) of an activation row, chunk starting at kb.
+__device__ __forceinline__ f16x8 a_frag(const f16 *row, int kb, int q, int b, int s)
+{
+    return *reinterpret_cast<const f16x8 *>(row + kb + 128 * q + 32 * b + 8 * s);
 }
 
 __device__ __forceinline__ f16x8 zero8()

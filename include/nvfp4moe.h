@@ -62,7 +62,7 @@ enum {
 /* A quantized weight tensor: `groups` matrices of `rows` x `k`. */
 typedef struct nvfp4_weights {
     const uint8_t *codes;       /* device, [groups][rows][k/2], 16-byte aligned                */
-    const uint8_t *scales;      /* device, [groups][rows][k/16], 2-byte aligned                */
+    const uint8_t *scales;      /* device, [groups][rows][k/16], 8-byte aligned                */
     const float *global_scale;  /* device, [groups]                                            */
     int32_t groups, rows, k;
 } nvfp4_weights;
