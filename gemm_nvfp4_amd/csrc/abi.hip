@@ -79,7 +79,9 @@ NVFP4_API int nvfp4_moe_w13_swiglu(const void *plan, int32_t M, int32_t topk, in
     if (!plan || !x || !h) return NVFP4_ERR_NULL;
     if (!aligned(plan, 16) || !aligned(x, 16) || !aligned(h, 16)) return NVFP4_ERR_ALIGN;
     const PlanLayout L = nvfp4::plan_layout(M, topk, E);
-    return nvfp4::run_w13(nvfp4::plan_view(plan, L), L.T, topk, x, *w13, layout, h, static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (nvfp4::use_prefill(L.P, E)) return nvfp4::run_w13_prefill(nvfp4::plan_view(plan, L), L.A, topk, x, *w13, layout, h, s);
+    return nvfp4::run_w13(nvfp4::plan_view(plan, L), L.T, topk, x, *w13, layout, h, s);
 }
 
 NVFP4_API size_t nvfp4_moe_w2_workspace_bytes(int32_t M, int32_t topk, int32_t K)
@@ -106,8 +108,14 @@ NVFP4_API int nvfp4_moe_w2_reduce(const void *plan, int32_t M, int32_t topk, int
         return NVFP4_ERR_ALIGN;
     if (ws_bytes < nvfp4_moe_w2_workspace_bytes(M, topk, K)) return NVFP4_ERR_WORKSPACE;
     const PlanLayout L = nvfp4::plan_layout(M, topk, E);
-    return nvfp4::run_w2(nvfp4::plan_view(plan, L), L.T, M, topk, h, *w2, topk_weights, out,
-                         static_cast<float *>(ws), static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const nvfp4::PlanView pv = nvfp4::plan_view(plan, L);
+    if (nvfp4::use_prefill(L.P, E)) {
+        const int st = nvfp4::run_w2_prefill(pv, L.A, h, *w2, static_cast<float *>(ws), s);
+        if (st != NVFP4_OK) return st;
+        return nvfp4::run_reduce(pv, M, topk, w2->rows, topk_weights, static_cast<const float *>(ws), out, s);
+    }
+    return nvfp4::run_w2(pv, L.T, M, topk, h, *w2, topk_weights, out, static_cast<float *>(ws), s);
 }
 
 NVFP4_API int nvfp4_linear(const uint16_t *x, int32_t M, const nvfp4_weights *w, uint16_t *y, void *stream)

@@ -347,9 +347,15 @@ int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uin
     default: st = launch(w2_stream_kernel<4>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws); break;
     }
     if (st != NVFP4_OK) return st;
+    return run_reduce(pv, M, topk, K, topk_weights, ws, out, s);
+}
+
+int run_reduce(const PlanView &pv, int32_t M, int32_t topk, int32_t K, const float *topk_weights, const float *ws,
+               uint16_t *out, hipStream_t s)
+{
     const int bpt = (K / 4 + 255) / 256;
     return launch(reduce_kernel, dim3((unsigned)((int64_t)M * bpt)), dim3(256), 0, s, pv.pos_of_pair, topk_weights,
-                  (const float *)ws, topk, K, bpt, reinterpret_cast<f16 *>(out));
+                  ws, topk, K, bpt, reinterpret_cast<f16 *>(out));
 }
 
 }  // namespace nvfp4

@@ -1,0 +1,80 @@
+"""GPU parity of the prefill (MFMA-tiled) regime of the grouped MoE against the fp64 oracle.
+
+The workload is the 8192-token, top-10 W13/W2 route of the "[Perf][SM70] Optimize Qwen3.8 Flash
+Next prefill" page ("SM70 QSA indexer hotspot update"), with synthetic weights. The library picks
+its MFMA-tiled kernels once experts average at least 16 pairs (M*topk >= 16*E). Every regime uses
+one reduction order. So besides matching the oracle, a token's output from a prefill-size batch
+must be bitwise equal to the same token run alone, which goes through the streaming kernels.
+"""
+import numpy as np
+import pytest
+import torch
+
+from synth import inputs as S
+from tests.parity import assert_rows_close, dev_moe, half_bits, run_moe, to_np64
+
+pytestmark = pytest.mark.gpu
+
+
+def _single_token_out(case, d, t, layout):
+    sh = case["shape"]
+    one = dict(case)
+    one["shape"] = S.MoEShape(m=1, e=sh.e, topk=sh.topk, k=sh.k, i=sh.i)
+    one["x"], one["ids"], one["topk_weights"] = case["x"][t:t + 1], case["ids"][t:t + 1], case["topk_weights"][t:t + 1]
+    dd = {"x": d["x"][t:t + 1].contiguous(), "ids": d["ids"][t:t + 1].contiguous(), "tw": d["tw"][t:t + 1].contiguous(),
+          "w13": d["w13"], "w2": d["w2"]}
+    return run_moe(one, layout, dev=dd)["out"][0]
+
+
+@pytest.mark.parametrize("routing,layout", [("uniform", 0), ("zipf", 1)])
+def test_prefill_medium_multi_pass(orc, routing, layout):
+    """8 experts x 600 tokens x top-2: about 150 rows per expert, i.e. several 96-row passes."""
+    sh = S.MoEShape(m=600, e=8, topk=2, k=512, i=128)
+    case = S.moe_case(sh, routing=routing, workload="prefill", route_pattern=7, gscale13=0.37)
+    res = run_moe(case, layout)
+    pl = orc.plan(case["ids"], sh.e, 16)
+    h_ref, out_ref = orc.moe_grouped(case, pl, layout=layout)
+    assert_rows_close(to_np64(res["h"][: pl["n_valid"]]), h_ref, "prefill medium h")
+    assert_rows_close(to_np64(res["out"]), out_ref, "prefill medium out")
+    for t in (0, 1, 299, 599):
+        single = _single_token_out(case, res["dev"], t, layout)
+        assert torch.equal(single.view(torch.int16), res["out"][t].view(torch.int16)), f"token {t}"
+
+
+def test_prefill_ragged_k_and_i(orc):
+    """K = 640 (a 128-element tail chunk), I = 384 (a partial last block of i slices)."""
+    sh = S.MoEShape(m=200, e=4, topk=3, k=640, i=384)
+    case = S.moe_case(sh, routing="repeat_invalid", workload="prefill", route_pattern=8)
+    res = run_moe(case, 0)
+    pl = orc.plan(case["ids"], sh.e, 16)
+    h_ref, out_ref = orc.moe_grouped(case, pl)
+    assert_rows_close(to_np64(res["h"][: pl["n_valid"]]), h_ref, "prefill ragged h")
+    assert_rows_close(to_np64(res["out"]), out_ref, "prefill ragged out")
+    assert np.all(half_bits(res["h"][pl["n_valid"]:]) == 0x7E00)
+    for t in (0, 57, 199):
+        single = _single_token_out(case, res["dev"], t, 0)
+        assert torch.equal(single.view(torch.int16), res["out"][t].view(torch.int16)), f"token {t}"
+
+
+def test_prefill_8192_tokens_sampled(orc):
+    """Full prefill size: the plan must be bit-exact. Sampled tokens' h and out rows must match the
+    oracle's per-token form. Sampled tokens must be bitwise equal to single-token runs."""
+    case = S.moe_case(S.PREFILL, workload="prefill")
+    res = run_moe(case, 0)
+    import gemm_nvfp4_amd as G
+    got = G.plan_fields(res["plan"], S.PREFILL.m, S.PREFILL.topk, S.PREFILL.e)
+    pl = orc.plan(case["ids"], S.PREFILL.e, 16)
+    assert np.array_equal(got["sorted_pair"], pl["sorted_pair"])
+    assert np.array_equal(got["pos_of_pair"], pl["pos_of_pair"])
+    tokens = np.random.default_rng(4).choice(S.PREFILL.m, size=24, replace=False).astype(np.int32)
+    out_ref, h_ref = orc.moe_token(case, tokens=tokens, want_h=True)
+    out = to_np64(res["out"])[tokens]
+    assert_rows_close(out, out_ref, "prefill out")
+    h = to_np64(res["h"])
+    for qi, t in enumerate(tokens):
+        for k in range(S.PREFILL.topk):
+            j = pl["pos_of_pair"][t * S.PREFILL.topk + k]
+            assert_rows_close(h[j][None], h_ref[qi, k][None], f"prefill h t={t} k={k}")
+    for t in tokens[:6]:
+        single = _single_token_out(case, res["dev"], int(t), 0)
+        assert torch.equal(single.view(torch.int16), res["out"][int(t)].view(torch.int16)), f"token {t}"
