@@ -80,7 +80,8 @@ NVFP4_API int nvfp4_moe_w13_swiglu(const void *plan, int32_t M, int32_t topk, in
     if (!aligned(plan, 16) || !aligned(x, 16) || !aligned(h, 16)) return NVFP4_ERR_ALIGN;
     const PlanLayout L = nvfp4::plan_layout(M, topk, E);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (nvfp4::use_prefill(L.P, E)) return nvfp4::run_w13_prefill(nvfp4::plan_view(plan, L), L.A, topk, x, *w13, layout, h, s);
+    if (nvfp4::use_prefill(M, L.P, E, K, I))
+        return nvfp4::run_w13_prefill(nvfp4::plan_view(plan, L), L.A, M, topk, x, *w13, layout, h, s);
     return nvfp4::run_w13(nvfp4::plan_view(plan, L), L.T, topk, x, *w13, layout, h, s);
 }
 
@@ -110,8 +111,8 @@ NVFP4_API int nvfp4_moe_w2_reduce(const void *plan, int32_t M, int32_t topk, int
     const PlanLayout L = nvfp4::plan_layout(M, topk, E);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const nvfp4::PlanView pv = nvfp4::plan_view(plan, L);
-    if (nvfp4::use_prefill(L.P, E)) {
-        const int st = nvfp4::run_w2_prefill(pv, L.A, h, *w2, static_cast<float *>(ws), s);
+    if (nvfp4::use_prefill(M, L.P, E, K, I)) {
+        const int st = nvfp4::run_w2_prefill(pv, L.A, L.P, h, *w2, static_cast<float *>(ws), s);
         if (st != NVFP4_OK) return st;
         return nvfp4::run_reduce(pv, M, topk, w2->rows, topk_weights, static_cast<const float *>(ws), out, s);
     }

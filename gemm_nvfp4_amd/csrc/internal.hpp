@@ -88,16 +88,22 @@ int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, 
 int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uint16_t *h, const nvfp4_weights &w,
            const float *topk_weights, uint16_t *out, float *ws, hipStream_t s);
 int run_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, uint16_t *y, hipStream_t s);
-int run_w13_prefill(const PlanView &pv, int64_t a_max, int32_t topk, const uint16_t *x, const nvfp4_weights &w,
-                    int32_t layout, uint16_t *h, hipStream_t s);
-int run_w2_prefill(const PlanView &pv, int64_t a_max, const uint16_t *h, const nvfp4_weights &w, float *ws,
+int run_w13_prefill(const PlanView &pv, int64_t a_max, int32_t M, int32_t topk, const uint16_t *x,
+                    const nvfp4_weights &w, int32_t layout, uint16_t *h, hipStream_t s);
+int run_w2_prefill(const PlanView &pv, int64_t a_max, int64_t P, const uint16_t *h, const nvfp4_weights &w, float *ws,
                    hipStream_t s);
+// The prefill kernels address x, h and one expert's weights with 32-bit byte offsets.
+bool prefill_offsets_fit(int64_t M, int64_t P, int32_t K, int32_t I);
 int run_reduce(const PlanView &pv, int32_t M, int32_t topk, int32_t K, const float *topk_weights, const float *ws,
                uint16_t *out, hipStream_t s);
 
 // Regime switch (performance only: every kernel uses the same reduction order, so results are
 // bitwise identical either way). The MFMA-tiled prefill kernels pay off once experts average at
-// least 16 pairs, i.e. M*topk >= 16*E; below that the streaming kernels win.
-inline bool use_prefill(int64_t P, int32_t E) { return P >= 16 * (int64_t)E; }
+// least 16 pairs, i.e. M*topk >= 16*E; below that the streaming kernels win. They also need every
+// byte offset to fit in 31 bits; larger problems stay on the streaming kernels.
+inline bool use_prefill(int64_t M, int64_t P, int32_t E, int32_t K, int32_t I)
+{
+    return P >= 16 * (int64_t)E && prefill_offsets_fit(M, P, K, I);
+}
 
 }  // namespace nvfp4

@@ -4,16 +4,21 @@
 //
 // With hundreds of pairs per expert the layer is a dense contraction (about 570 FLOP per weight
 // byte), so the design goal is MFMA throughput. gfx950 design:
-//   * A block owns one active expert and a slice of its output columns: 64 i values (gate and up
-//     rows) for W13, or 128 output rows for W2. It walks the expert's bucket rows in passes of 96.
-//     Blocks of one expert are numbered consecutively and mapped to the same XCD, so they share
-//     the expert's activation rows in that XCD's L2.
-//   * Each wave owns two 16-wide weight tiles (W13: gate and up of one i slice; W2: two output
-//     tiles) and 6 row tiles. Per 512-element chunk it decodes its weights once (gfx950 fp4/fp8
-//     converts plus one exact fp16 multiply) and reuses each B fragment for all 6 row tiles.
-//   * Activation rows are staged in LDS a quarter chunk at a time: lane group q's 32 elements
-//     for step group b, for every row. Staging is double-buffered, so the global loads of the next
-//     quarter overlap the MFMAs of the current one.
+//   * A block owns one active expert and a slice of its output columns: 128 i values (their gate
+//     and up rows) for W13, or 256 output rows for W2. It walks the expert's bucket rows in passes
+//     of 80. Blocks of one expert are numbered consecutively and mapped to the same XCD, so they
+//     share the expert's activation rows in that XCD's L2.
+//   * One wave per SIMD, up to 512 registers. Each wave owns four 16-wide weight tiles (W13: gate
+//     and up of two i slices; W2: four output tiles) and up to five row tiles: 20 independent
+//     accumulator chains keep the matrix pipe busy. Each A fragment read from LDS feeds 4 MFMAs.
+//   * Per 512-element chunk a wave decodes its weights once (gfx950 fp4/fp8 converts plus one
+//     exact fp16 multiply) and reuses each B fragment for all row tiles. Packed weights are loaded
+//     one chunk ahead, a quarter at a time, into the registers the current chunk has finished with.
+//   * Activation rows are staged in LDS a quarter chunk at a time (lane group q's 32 elements of one
+//     step group, for every row), a quarter ahead of their use.
+//   * Global memory is read through buffer resources: a uniform base in scalar registers and a
+//     32-bit per-lane offset, so a lane keeps one register per stream instead of a 64-bit pointer,
+//     and out-of-range reads return zero. The host only picks this regime when every offset fits.
 //   * The reduction order is the library-wide one of nvfp4_device.hpp: 512-element chunks, each
 //     a chain of 16 MFMA steps from +0, chunk results added in order, global scale last. Results
 //     are bitwise identical to the streaming (decode) kernels, so batch invariance holds across
@@ -27,17 +32,37 @@
 namespace nvfp4 {
 namespace {
 
-constexpr int PF_R = 6;                 // row tiles per wave
+constexpr int PF_R = 5;                 // row tiles per wave (and per pass)
 constexpr int PF_ROWS = 16 * PF_R;      // bucket rows per pass
-constexpr int AQ = 32;                  // elements of one lane group per step group (4 steps x 8)
-constexpr int A_ROW = 4 * AQ + 8;       // staged halves per row: 4 lane groups + 16 bytes of bank padding
-constexpr int STAGE_PIECES = PF_ROWS * 16;  // 16-byte pieces per staged quarter chunk
-constexpr int PIECES_PER_THREAD = (STAGE_PIECES + 255) / 256;
+constexpr int PF_T = 4;                 // weight tiles per wave
+constexpr int AQ = 32;                  // elements of one lane group per quarter chunk (one step group)
+constexpr int A_ROW = 4 * AQ + 8;       // staged quarter per row: 4 lane groups + 16 bytes of bank padding
+constexpr int NBUF = 3;                 // ring of quarter buffers
+constexpr int PPT = PF_ROWS * 16 / 256; // 16-byte pieces of a staged quarter per thread
 
-struct PrefillShared {
-    f16 a[2][PF_ROWS][A_ROW];  // double-buffered activation quarter chunks
-    int arow[PF_ROWS];         // activation row (token or bucket row) of each pass row
+struct __attribute__((aligned(16))) PrefillShared {
+    f16 a[NBUF][PF_ROWS][A_ROW];  // activation quarters: [buffer][row][lane group q: 32 elements]
+    int arow[PF_ROWS];            // activation row (token or bucket row) of each pass row
 };
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over [base, base + bytes). Dword 3 = 0x00020000 selects the 32-bit data
+// format that gfx9 untyped buffer loads require. Reads at offsets >= bytes return zero.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
 
 // Logical block index with blocks of one expert kept on one XCD: the hardware deals block ids to
 // the 8 XCDs round-robin, so logical = xcd * ceil(G/8) + slot puts consecutive logical blocks on the
@@ -49,77 +74,183 @@ __device__ __forceinline__ int xcd_logical_block(int G)
     return logical < G ? logical : -1;
 }
 
-// Global loads of one quarter chunk (step group b of chunk kb) for `rows` rows into registers:
-// piece = row * 16 + q * 4 + p covers elements [kb + 128q + 32b + 8p, +8) of the row.
 struct StageRegs {
-    u32x4 v[PIECES_PER_THREAD];
+    u32x4 v[PPT];
 };
 
-__device__ __forceinline__ void stage_load(StageRegs &s, const f16 *src, int L, const int *arow, int rows, int kb,
-                                           int b, int groups)
+// Scheduling hints for one MFMA step (row tile outer, weight tile inner): each MFMA is followed by
+// up to two VALU ops (the next step's B decode), and each row tile's four MFMAs by the LDS read
+// of that row tile's next A fragment, which reuses the fragment's registers.
+template <int NR>
+__device__ __forceinline__ void interleave_step()
 {
 #pragma unroll
-    for (int i = 0; i < PIECES_PER_THREAD; ++i) {
-        const int idx = threadIdx.x + 256 * i;
-        const int r = idx >> 4, q = (idx >> 2) & 3, p = idx & 3;
-        if (r < rows && q < groups)
-            s.v[i] = *reinterpret_cast<const u32x4 *>(src + (size_t)arow[r] * L + kb + 128 * q + AQ * b + 8 * p);
+    for (int r = 0; r < NR; ++r) {
+#pragma unroll
+        for (int t = 0; t < PF_T; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
 }
 
-__device__ __forceinline__ void stage_store(const StageRegs &s, f16 (*a)[A_ROW], int rows, int groups)
-{
-#pragma unroll
-    for (int i = 0; i < PIECES_PER_THREAD; ++i) {
-        const int idx = threadIdx.x + 256 * i;
-        const int r = idx >> 4, q = (idx >> 2) & 3, p = idx & 3;
-        if (r < rows && q < groups) *reinterpret_cast<u32x4 *>(&a[r][AQ * q + 8 * p]) = s.v[i];
-    }
-}
+// Where one pass reads its operands.
+struct PassSrc {
+    rsrc_t act;           // activation rows (x for W13, h for W2)
+    uint32_t row_bytes;   // bytes per activation row
+    rsrc_t codes, scales; // this expert's packed weights
+    int red;              // reduction length (K for W13, I for W2)
+};
 
-// One chunk of two weight rows against the pass's staged activation rows.
-// acc[r][t]: row tile r, weight tile t. Staging of quarter b+1 overlaps the MFMAs of quarter b.
-__device__ __forceinline__ void chunk_pass(PrefillShared &sh, const f16 *src, int L, int rows, int kb, int groups,
-                                           const RawChunk &w0, const RawChunk &w1, bool working, int n, int q,
-                                           f32x4 acc[PF_R][2])
+// All chunks of one pass: tot = ((c0 + c1) + c2) + ..., each chunk a chain of 16 MFMA steps
+// j = 4b + s from +0, every accumulator seeing its steps in ascending order.
+//
+// Software pipeline, per wave:
+//   * MFMA steps: while step j's NR x 4 MFMAs run, the B fragments of step j + 1 are decoded
+//     from packed registers, and as soon as a row tile's four MFMAs have issued, its A fragment
+//     for step j + 1 is read from LDS. Each B fragment feeds NR MFMAs and each A fragment feeds 4.
+//   * Activations move through LDS a quarter chunk at a time (quarter g = 4c + b: lane group q's
+//     32 elements of step group b, for every row), in a ring of three buffers. Quarter g + 2 is
+//     loaded into registers when quarter g starts and stored to LDS when it ends, so quarter g + 1
+//     is in LDS a whole quarter before it is needed and the A reads for its first step are issued
+//     during the last step of quarter g. A buffer is rewritten only after the barrier that ends
+//     its last reader's quarter.
+//   * Weights: packed registers for one chunk. Right after quarter b of chunk c has been decoded
+//     for the last time, its registers are refilled with quarter b of chunk c + 1.
+// Vector memory ops retire in issue order; every wait is for loads issued at least a quarter
+// earlier. Barriers order LDS only, so they never wait for loads in flight.
+//
+// Loads are unconditional, so they need no branches: rows past `rows` re-read the pass's first row
+// and compute results that are never stored (MFMA rows are independent). Lane groups past a
+// short chunk's end are staged as exact zeros in A and get zero block scales in B, so their
+// products are +-0 and cannot change a sum.
+//
+// wo[t] is the byte offset of the lane's share of weight tile t inside the expert's codes (row *
+// red/2 + 64q); the matching scale offset is wo[t] / 8.
+template <int NR, class Epi>
+__device__ __forceinline__ void pass_chunks(PrefillShared &sh, const PassSrc &src, int rows, const uint32_t (&wo)[PF_T],
+                                            bool working, int n, int q, Epi &&epi)
 {
-    const bool qv = q < groups;
+    const int red = src.red, S = num_chunks(red), G = 4 * S;
+    const int qs = (threadIdx.x >> 2) & 3, ps = threadIdx.x & 3, srow = threadIdx.x >> 4;  // staged piece
+    uint32_t vo[PPT];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int r = srow + 16 * i;
+        vo[i] = (uint32_t)sh.arow[r < rows ? r : 0] * src.row_bytes + 256 * qs + 16 * ps;
+    }
+    auto groups_of = [&](int c) { return min(KCHUNK, red - c * KCHUNK) >> 7; };
+    auto stage_load = [&](StageRegs &st, int g) {
+        g = g < G ? g : G - 1;  // quarters past the end re-read the last one; they are never used
+        const uint32_t so = (uint32_t)((g >> 2) * KCHUNK + AQ * (g & 3)) * 2;
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) st.v[i] = bload16(src.act, vo[i], so);
+    };
+    auto stage_store = [&](const StageRegs &st, int buf, int g) {
+        g = g < G ? g : G - 1;
+        const bool ok = qs < groups_of(g >> 2);
+#pragma unroll
+        for (int i = 0; i < PPT; ++i)
+            *reinterpret_cast<u32x4 *>(&sh.a[buf][srow + 16 * i][AQ * qs + 8 * ps]) = ok ? st.v[i] : u32x4{0, 0, 0, 0};
+    };
+    RawChunk w[PF_T];
+    auto load_quarter = [&](int c, int b) {
+        c = c < S ? c : S - 1;  // the last chunk refills itself: cache hits, never used
+#pragma unroll
+        for (int t = 0; t < PF_T; ++t) {
+            w[t].codes[b] = bload16(src.codes, wo[t] + 16 * b, (uint32_t)c * (KCHUNK / 2));
+            if (b & 1) w[t].scales[b >> 1] = bload4(src.scales, (wo[t] >> 3) + 4 * (b >> 1), (uint32_t)c * (KCHUNK / 16));
+        }
+    };
+    auto buf_next = [](int x) { return x == NBUF - 1 ? 0 : x + 1; };
+
     StageRegs st;
-    stage_load(st, src, L, sh.arow, rows, kb, 0, groups);
-    stage_store(st, sh.a[0], rows, groups);
-    __syncthreads();
+    // Prologue: quarters 0 and 1 in LDS, chunk 0's weights in registers.
+    stage_load(st, 0);
+    stage_store(st, 0, 0);
+    stage_load(st, 1);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        if (b < 3) stage_load(st, src, L, sh.arow, rows, kb, b + 1, groups);
-        if (working) {
-            const f16x2 sc0 = chunk_scales(w0, b), sc1 = chunk_scales(w1, b);
-            f16x8 b0[4], b1[4];
+    for (int b = 0; b < 4; ++b) load_quarter(0, b);
+    stage_store(st, 1, 1);
+    lds_barrier();
+
+    f32x4 tot[PF_R][PF_T], ca[PF_R][PF_T];
+    f16x8 bf[2][PF_T], av[NR];
+    f16x2 sc[PF_T];
+    int cur = 0;  // LDS buffer of the current quarter
+    // B fragments of step (b, s) of chunk c into pipeline slot `slot`.
+    auto decode = [&](int slot, int c, int b, int s) {
+        if (s == 0) {
+            const bool qv = q < groups_of(c < S ? c : S - 1);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                b0[s] = b_frag(w0, sc0, b, s, qv);
-                b1[s] = b_frag(w1, sc1, b, s, qv);
+            for (int t = 0; t < PF_T; ++t) sc[t] = qv ? chunk_scales(w[t], b) : f16x2{0, 0};
+        }
+#pragma unroll
+        for (int t = 0; t < PF_T; ++t) bf[slot][t] = decode8(w[t].codes[b][s], sc[t][s >> 1]);
+    };
+    auto a_read = [&](int r, int s, int buf) {
+        return *reinterpret_cast<const f16x8 *>(&sh.a[buf][16 * r + n][AQ * q + 8 * s]);
+    };
+    decode(0, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) av[r] = a_read(r, 0, 0);
+    for (int c = 0; c < S; ++c) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int b = j >> 2, s = j & 3, g = 4 * c + b, slot = j & 1;
+            if (s == 0) stage_load(st, g + 2);
+            // Operands of step j + 1. The last step's successor is the next chunk's first step:
+            // quarter g + 1, already in LDS (after the last chunk this reads a stale buffer and the
+            // refilled registers; never used).
+            const int sn = (j + 1) & 3, bn = ((j + 1) >> 2) & 3, bufn = s == 3 ? buf_next(cur) : cur;
+            decode(slot ^ 1, j < 15 ? c : c + 1, bn, sn);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+#pragma unroll
+                for (int t = 0; t < PF_T; ++t)
+                    ca[r][t] = mfma_step(av[r], bf[slot][t], j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : ca[r][t]);
+                av[r] = a_read(r, sn, bufn);
             }
-            const f16(*a)[A_ROW] = sh.a[b & 1];
-#pragma unroll
-            for (int r = 0; r < PF_R; ++r) {
-                if (16 * r >= rows) break;
-                const int row = 16 * r + n;
-                const bool rv = row < rows && qv;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const f16x8 av = rv ? *reinterpret_cast<const f16x8 *>(&a[row][AQ * q + 8 * s]) : zero8();
-                    acc[r][0] = mfma_step(av, b0[s], acc[r][0]);
-                    acc[r][1] = mfma_step(av, b1[s], acc[r][1]);
-                }
+            interleave_step<NR>();
+            __builtin_amdgcn_sched_barrier(0);
+            if (s == 3) {
+                // Quarter b of this chunk is fully decoded: refill it with the next chunk's bytes.
+                load_quarter(c + 1, b);
+                stage_store(st, buf_next(buf_next(cur)), g + 2);
+                lds_barrier();
+                cur = buf_next(cur);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (b < 3) stage_store(st, sh.a[(b + 1) & 1], rows, groups);
-        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int t = 0; t < PF_T; ++t) tot[r][t] = c == 0 ? ca[r][t] : tot[r][t] + ca[r][t];
+    }
+    if (working) epi(tot, NR);
+}
+
+// One pass with the row-tile count as a compile-time constant, so the MFMA loops have no
+// per-tile branches. Only 1, 3 and 5 row tiles are instantiated (a pass of 2 or 4 tiles runs one
+// tile of padding rows): more variants in one kernel made the register allocator spill.
+// epi(tot, NR) stores the results; nothing stays live across the switch.
+template <class Epi>
+__device__ __forceinline__ void pass_dispatch(PrefillShared &sh, const PassSrc &src, int rows, const uint32_t (&wo)[PF_T],
+                                              bool working, int n, int q, Epi &&epi)
+{
+    switch ((rows + 15) >> 4) {
+    case 1: pass_chunks<1>(sh, src, rows, wo, working, n, q, epi); break;
+    case 2:
+    case 3: pass_chunks<3>(sh, src, rows, wo, working, n, q, epi); break;
+    default: pass_chunks<5>(sh, src, rows, wo, working, n, q, epi); break;
     }
 }
 
 // ---- W13 + SwiGLU ---------------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void w13_swiglu_prefill_kernel(PlanView pv, int topk, const f16 *__restrict__ x,
+// Wave w of block slice nb owns i slices 8*nb + 2w and +1: tiles {gate0, up0, gate1, up1}.
+__global__ __launch_bounds__(256, 1) void w13_swiglu_prefill_kernel(PlanView pv, int topk, const f16 *__restrict__ x,
+                                                                     uint32_t x_bytes,
                                                                      const uint8_t *__restrict__ codes,
                                                                      const uint8_t *__restrict__ scales,
                                                                      const float *__restrict__ gscale, int K, int I,
@@ -127,139 +258,139 @@ __global__ __launch_bounds__(256, 2) void w13_swiglu_prefill_kernel(PlanView pv,
 {
     __shared__ PrefillShared sh;
     const int itiles = I >> 4;
-    const int nblk = (itiles + 3) >> 2;  // 4 i slices (one per wave) per block
+    const int nblk = (itiles + 7) >> 3;  // 8 i slices per block
     const int lb = xcd_logical_block(a_max * nblk);
     if (lb < 0) return;
     const int a = lb / nblk, nb = lb - a * nblk;
     if (a >= pv.hdr[1]) return;  // block-uniform
     const int e = pv.active[a], cnt = pv.counts[e], base = pv.offsets[e];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, q = lane >> 4;
-    const int it = nb * 4 + wave;
-    const bool working = it < itiles;
-    const int itc = working ? it : itiles - 1;
-    const int i_row = itc * 16 + n;
-    const size_t eb = (size_t)e * 2 * I, crow = (size_t)K >> 1, srow = (size_t)K >> 4;
-    const size_t rg = eb + (layout ? 2 * i_row : i_row), ru = eb + (layout ? 2 * i_row + 1 : I + i_row);
+    const int it0 = nb * 8 + 2 * wave;
+    const bool working = it0 < itiles;  // the second slice may be missing (odd itiles): guarded below
+    const uint32_t ebytes = (uint32_t)(2 * I) * (uint32_t)(K >> 1);  // one expert's codes
+    PassSrc src;
+    src.act = make_rsrc(x, x_bytes);
+    src.row_bytes = (uint32_t)K * 2;
+    src.codes = make_rsrc(codes + (size_t)e * ebytes, ebytes);
+    src.scales = make_rsrc(scales + (size_t)e * (ebytes >> 3), ebytes >> 3);
+    src.red = K;
+    uint32_t wo[PF_T];
+#pragma unroll
+    for (int t = 0; t < PF_T; ++t) {
+        const int it = min(it0 + (t >> 1), itiles - 1);
+        const int i_row = it * 16 + n;
+        const int row = (t & 1) == 0 ? (layout ? 2 * i_row : i_row) : (layout ? 2 * i_row + 1 : I + i_row);
+        wo[t] = (uint32_t)row * (uint32_t)(K >> 1) + 64 * q;
+    }
     const float gs = gscale[e];
-    const int S = num_chunks(K);
 
     for (int rp = 0; rp < cnt; rp += PF_ROWS) {
         const int rows = min(PF_ROWS, cnt - rp);
-        __syncthreads();  // the previous pass is done with sh.arow
+        lds_barrier();  // the previous pass is done with sh.arow
         for (int r = threadIdx.x; r < rows; r += 256) sh.arow[r] = pv.sorted_pair[base + rp + r] / topk;
-        __syncthreads();
-        f32x4 tot[PF_R][2];
-        for (int c = 0; c < S; ++c) {
-            const int kb = c * KCHUNK;
-            const int groups = min(KCHUNK, K - kb) >> 7;
-            const int q_ld = q < groups ? q : groups - 1;
-            const RawChunk wg = load_chunk(codes + rg * crow, scales + rg * srow, kb, q_ld);
-            const RawChunk wu = load_chunk(codes + ru * crow, scales + ru * srow, kb, q_ld);
-            f32x4 ca[PF_R][2];
+        lds_barrier();
+        pass_dispatch(sh, src, rows, wo, working, n, q, [&](const f32x4 (&tot)[PF_R][PF_T], int nr) {
 #pragma unroll
-            for (int r = 0; r < PF_R; ++r) ca[r][0] = ca[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-            chunk_pass(sh, x, K, rows, kb, groups, wg, wu, working, n, q, ca);
-#pragma unroll
-            for (int r = 0; r < PF_R; ++r)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) tot[r][t] = c == 0 ? ca[r][t] : tot[r][t] + ca[r][t];
-        }
-        if (working) {
-#pragma unroll
-            for (int r = 0; r < PF_R; ++r)
+            for (int r = 0; r < PF_R; ++r) {
+                if (r >= nr) break;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int row = 16 * r + 4 * q + j;
-                    if (row < rows)
-                        h[(size_t)(base + rp + row) * I + it * 16 + n] = (f16)swiglu(tot[r][0][j] * gs, tot[r][1][j] * gs);
+                    if (row < rows) {
+                        f16 *hr = h + (size_t)(base + rp + row) * I + it0 * 16 + n;
+                        hr[0] = (f16)swiglu(tot[r][0][j] * gs, tot[r][1][j] * gs);
+                        if (it0 + 1 < itiles) hr[16] = (f16)swiglu(tot[r][2][j] * gs, tot[r][3][j] * gs);
+                    }
                 }
-        }
+            }
+        });
     }
 }
 
 // ---- W2: per-pair FP32 results -----------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void w2_prefill_kernel(PlanView pv, const f16 *__restrict__ hin,
+// Wave w of block slice nb owns output tiles 16*nb + 4w .. +3 (64 output rows).
+__global__ __launch_bounds__(256, 1) void w2_prefill_kernel(PlanView pv, const f16 *__restrict__ hin, uint32_t h_bytes,
                                                              const uint8_t *__restrict__ codes,
                                                              const uint8_t *__restrict__ scales,
                                                              const float *__restrict__ gscale, int K, int I,
                                                              float *__restrict__ ws, int a_max)
 {
     __shared__ PrefillShared sh;
-    const int npairs = K >> 5;             // pairs of 16-row output tiles
-    const int nblk = (npairs + 3) >> 2;    // 4 tile pairs (one per wave) per block
+    const int ntiles = K >> 4;
+    const int nblk = (ntiles + 15) >> 4;  // 16 output tiles per block
     const int lb = xcd_logical_block(a_max * nblk);
     if (lb < 0) return;
     const int a = lb / nblk, nb = lb - a * nblk;
     if (a >= pv.hdr[1]) return;
     const int e = pv.active[a], cnt = pv.counts[e], base = pv.offsets[e];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, q = lane >> 4;
-    const int tp = nb * 4 + wave;
-    const bool working = tp < npairs;
-    const int tpc = working ? tp : npairs - 1;
-    const size_t r0 = (size_t)e * K + tpc * 32 + n, r1 = r0 + 16;
-    const size_t crow = (size_t)I >> 1, srow = (size_t)I >> 4;
+    const int nt0 = nb * 16 + 4 * wave;
+    const bool working = nt0 < ntiles;
+    const uint32_t ebytes = (uint32_t)K * (uint32_t)(I >> 1);
+    PassSrc src;
+    src.act = make_rsrc(hin, h_bytes);
+    src.row_bytes = (uint32_t)I * 2;
+    src.codes = make_rsrc(codes + (size_t)e * ebytes, ebytes);
+    src.scales = make_rsrc(scales + (size_t)e * (ebytes >> 3), ebytes >> 3);
+    src.red = I;
+    uint32_t wo[PF_T];
+#pragma unroll
+    for (int t = 0; t < PF_T; ++t) wo[t] = (uint32_t)(min(nt0 + t, ntiles - 1) * 16 + n) * (uint32_t)(I >> 1) + 64 * q;
     const float gs = gscale[e];
-    const int S = num_chunks(I);
 
     for (int rp = 0; rp < cnt; rp += PF_ROWS) {
         const int rows = min(PF_ROWS, cnt - rp);
-        __syncthreads();
+        lds_barrier();
         for (int r = threadIdx.x; r < rows; r += 256) sh.arow[r] = base + rp + r;
-        __syncthreads();
-        f32x4 tot[PF_R][2];
-        for (int c = 0; c < S; ++c) {
-            const int kb = c * KCHUNK;
-            const int groups = min(KCHUNK, I - kb) >> 7;
-            const int q_ld = q < groups ? q : groups - 1;
-            const RawChunk w0 = load_chunk(codes + r0 * crow, scales + r0 * srow, kb, q_ld);
-            const RawChunk w1 = load_chunk(codes + r1 * crow, scales + r1 * srow, kb, q_ld);
-            f32x4 ca[PF_R][2];
+        lds_barrier();
+        pass_dispatch(sh, src, rows, wo, working, n, q, [&](const f32x4 (&tot)[PF_R][PF_T], int nr) {
 #pragma unroll
-            for (int r = 0; r < PF_R; ++r) ca[r][0] = ca[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-            chunk_pass(sh, hin, I, rows, kb, groups, w0, w1, working, n, q, ca);
-#pragma unroll
-            for (int r = 0; r < PF_R; ++r)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) tot[r][t] = c == 0 ? ca[r][t] : tot[r][t] + ca[r][t];
-        }
-        if (working) {
-#pragma unroll
-            for (int r = 0; r < PF_R; ++r)
+            for (int r = 0; r < PF_R; ++r) {
+                if (r >= nr) break;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int row = 16 * r + 4 * q + j;
                     if (row < rows) {
-                        float *y = ws + (size_t)(base + rp + row) * K + tp * 32 + n;
-                        y[0] = tot[r][0][j] * gs;
-                        y[16] = tot[r][1][j] * gs;
+                        float *y = ws + (size_t)(base + rp + row) * K + nt0 * 16 + n;
+#pragma unroll
+                        for (int t = 0; t < PF_T; ++t)
+                            if (nt0 + t < ntiles) y[16 * t] = tot[r][t][j] * gs;
                     }
                 }
-        }
+            }
+        });
     }
 }
 
 }  // namespace
 
-int run_w13_prefill(const PlanView &pv, int64_t a_max, int32_t topk, const uint16_t *x, const nvfp4_weights &w,
-                    int32_t layout, uint16_t *h, hipStream_t s)
+bool prefill_offsets_fit(int64_t M, int64_t P, int32_t K, int32_t I)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    return M * K * 2 < lim && P * I * 2 < lim && (int64_t)K * I < lim;
+}
+
+int run_w13_prefill(const PlanView &pv, int64_t a_max, int32_t M, int32_t topk, const uint16_t *x,
+                    const nvfp4_weights &w, int32_t layout, uint16_t *h, hipStream_t s)
 {
     const int K = w.k, I = w.rows / 2;
-    const int nblk = (I / 16 + 3) / 4;
+    const int nblk = (I / 16 + 7) / 8;
     const int64_t G = a_max * nblk;
     const unsigned grid = (unsigned)((G + 7) / 8 * 8);
     return launch(w13_swiglu_prefill_kernel, dim3(grid), dim3(256), 0, s, pv, topk, reinterpret_cast<const f16 *>(x),
-                  w.codes, w.scales, w.global_scale, K, I, layout, reinterpret_cast<f16 *>(h), (int)a_max);
+                  (uint32_t)((int64_t)M * K * 2), w.codes, w.scales, w.global_scale, K, I, layout,
+                  reinterpret_cast<f16 *>(h), (int)a_max);
 }
 
-int run_w2_prefill(const PlanView &pv, int64_t a_max, const uint16_t *h, const nvfp4_weights &w, float *ws,
+int run_w2_prefill(const PlanView &pv, int64_t a_max, int64_t P, const uint16_t *h, const nvfp4_weights &w, float *ws,
                    hipStream_t s)
 {
     const int K = w.rows, I = w.k;
-    const int nblk = (K / 32 + 3) / 4;
+    const int nblk = (K / 16 + 15) / 16;
     const int64_t G = a_max * nblk;
     const unsigned grid = (unsigned)((G + 7) / 8 * 8);
-    return launch(w2_prefill_kernel, dim3(grid), dim3(256), 0, s, pv, reinterpret_cast<const f16 *>(h), w.codes,
-                  w.scales, w.global_scale, K, I, ws, (int)a_max);
+    return launch(w2_prefill_kernel, dim3(grid), dim3(256), 0, s, pv, reinterpret_cast<const f16 *>(h),
+                  (uint32_t)(P * I * 2), w.codes, w.scales, w.global_scale, K, I, ws, (int)a_max);
 }
 
 }  // namespace nvfp4

@@ -120,6 +120,16 @@ __device__ __forceinline__ f16x8 zero8()
     return f16x8{0, 0, 0, 0, 0, 0, 0, 0};
 }
 
+// Block barrier that orders LDS only. __syncthreads() also fences global memory, and on gfx9 that
+// means s_waitcnt vmcnt(0): it would wait for loads still in flight (a prefetch). Kernels that pass
+// no global data between the waves of a block use this instead.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // SiLU(g) * u in FP32, as fixed for every regime: g / (1 + e^-g) * u.
 __device__ __forceinline__ float swiglu(float g, float u)
 {
