@@ -215,13 +215,17 @@ def plan_fields(plan: torch.Tensor, M: int, topk: int, E: int) -> dict:
     o = 16
     f = {}
     for name, n in (("counts", E), ("offsets", E + 1), ("active", A), ("tile_expert", T), ("tile_row0", T),
-                    ("sorted_pair", P), ("pos_of_pair", P)):
+                    ("tile_base", T), ("tile_rows", T), ("tile_pair", T * 16), ("sorted_pair", P), ("pos_of_pair", P)):
         f[name] = p[o:o + n]
         o += n
+    f["tile_pair"] = f["tile_pair"].reshape(T, 16)
     nv, na, nb, nt = (int(v) for v in p[0:4])
     f.update(n_valid=nv, n_active=na, n_bad=nb, n_tiles=nt, hdr=p[:16])
     f["sorted_pair"] = f["sorted_pair"][:nv]
     f["active"] = f["active"][:na]
     f["tile_expert"] = f["tile_expert"][:nt]
     f["tile_row0"] = f["tile_row0"][:nt]
+    f["tile_base"] = f["tile_base"][:nt]
+    f["tile_rows"] = f["tile_rows"][:nt]
+    f["tile_pair"] = f["tile_pair"][:nt]
     return f

@@ -14,7 +14,8 @@ namespace nvfp4 {
 // Word offsets of the routing plan's arrays inside the caller's plan buffer; the layout is the one
 // documented with nvfp4_moe_plan in nvfp4moe.h. P = M*topk pairs, A = min(E, P) active-expert
 // bound, T = A + ceil(P/16) row-tile bound. Plans with P > SMALL_PLAN_PAIRS also carry scratch:
-// per-chunk expert histograms hist[E][G] (G = ceil(P/PLAN_CHUNK)) and per-chunk bad-id counts.
+// per-chunk expert histograms hist[E][G] (G = ceil(P/PLAN_CHUNK)), per-chunk bad-id counts and
+// each expert's first row-tile index.
 constexpr int PLAN_HDR_WORDS = 16;
 constexpr int PLAN_TILE_ROWS = 16;
 constexpr int SMALL_PLAN_PAIRS = 1024;
@@ -28,7 +29,8 @@ constexpr int MAX_LINEAR_K = 32768;
 
 struct PlanLayout {
     int64_t P, A, T, G;
-    int64_t hdr, counts, offsets, active, tile_expert, tile_row0, sorted_pair, pos_of_pair, hist, badc, words;
+    int64_t hdr, counts, offsets, active, tile_expert, tile_row0, tile_base, tile_rows, tile_pair, sorted_pair,
+        pos_of_pair, hist, badc, tile_first, words;
 };
 
 inline PlanLayout plan_layout(int32_t M, int32_t topk, int32_t E)
@@ -45,24 +47,30 @@ inline PlanLayout plan_layout(int32_t M, int32_t topk, int32_t E)
     L.active = o;      o += L.A;
     L.tile_expert = o; o += L.T;
     L.tile_row0 = o;   o += L.T;
+    L.tile_base = o;   o += L.T;
+    L.tile_rows = o;   o += L.T;
+    L.tile_pair = o;    o += L.T * PLAN_TILE_ROWS;
     L.sorted_pair = o; o += L.P;
     L.pos_of_pair = o; o += L.P;
     L.hist = o;        o += (int64_t)E * L.G;
     L.badc = o;        o += L.G;
+    L.tile_first = o;  o += L.G > 0 ? E : 0;
     L.words = (o + 63) & ~(int64_t)63;  // whole 256-byte lines
     return L;
 }
 
 // Read-only device view of a built plan.
 struct PlanView {
-    const int32_t *hdr, *counts, *offsets, *active, *tile_expert, *tile_row0, *sorted_pair, *pos_of_pair;
+    const int32_t *hdr, *counts, *offsets, *active, *tile_expert, *tile_row0, *tile_base, *tile_rows, *tile_pair,
+        *sorted_pair, *pos_of_pair;
 };
 
 inline PlanView plan_view(const void *plan, const PlanLayout &L)
 {
     const int32_t *p = static_cast<const int32_t *>(plan);
-    return PlanView{p + L.hdr, p + L.counts, p + L.offsets, p + L.active, p + L.tile_expert,
-                    p + L.tile_row0, p + L.sorted_pair, p + L.pos_of_pair};
+    return PlanView{p + L.hdr,       p + L.counts,    p + L.offsets,   p + L.active,
+                    p + L.tile_expert, p + L.tile_row0, p + L.tile_base, p + L.tile_rows,
+                    p + L.tile_pair,  p + L.sorted_pair, p + L.pos_of_pair};
 }
 
 // Launch `kernel` through hipLaunchKernel, so a rejected launch is reported as a status instead

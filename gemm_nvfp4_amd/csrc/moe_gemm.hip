@@ -13,8 +13,8 @@
 //     contiguous ranges, one per persistent block (three 256-thread blocks per CU, at most 168
 //     VGPRs per lane, so 12 waves per CU). Blocks past the device-side unit count leave at once,
 //     so no device-to-host read is ever needed.
-//   * Block start: the block stages its range's tile metadata (expert, rows, first bucket row,
-//     activation-row index of each row) in LDS. That is one dependent-load chain per block.
+//   * Block start: the block stages its range's tile descriptors from the plan (expert, rows, first
+//     bucket row, activation row of each row) in LDS: one load after the tile count.
 //   * Inside a block the four waves split the reduction axis into its 512-element chunks
 //     (intra-block split-K) when there are several. Otherwise each takes its own tiles. A wave
 //     always owns two 16-row weight tiles: W13's gate and up rows of one 16-wide i slice, or two
@@ -37,12 +37,14 @@ constexpr int LDS_ROW = 20;  // padded row of 16 floats: rows 4 apart land on di
 constexpr int MAX_RANGE_TILES = 16;
 
 // Per-block staging of the row tiles its unit range touches: expert id, row count, first bucket
-// row and the activation row index of each row (token for W13, bucket row for W2).
+// row, the activation row index of each row (token for W13, bucket row for W2) and, for W2, each
+// row's pair index (where its result goes).
 struct TileStage {
     int e[MAX_RANGE_TILES];
     int cnt[MAX_RANGE_TILES];
     int base[MAX_RANGE_TILES];
     int arow[MAX_RANGE_TILES][16];
+    int pair[MAX_RANGE_TILES][16];
 };
 
 // Contiguous unit range of this block out of U units; returns false if empty.
@@ -53,31 +55,47 @@ __device__ __forceinline__ bool unit_range(int64_t U, int64_t &u0, int64_t &u1)
     return u0 < u1;
 }
 
-// Stage tiles [t_lo, t_lo + ntl): expert ids, row counts, first bucket rows, then each row's
-// activation row: the token (pair / topk) when topk > 0, else the bucket row itself.
+// Stage tiles [t_lo, t_lo + ntl) from the plan's tile descriptors: expert id, row count, first
+// bucket row, each row's pair, and its activation row: the pair's token when topk > 0 (W13), else
+// the bucket row itself (W2). All of it is one dependent load away from the tile index.
 __device__ __forceinline__ void stage_tiles(const PlanView &pv, TileStage &st, int t_lo, int ntl, int topk)
 {
     if ((int)threadIdx.x < ntl) {
-        const int e = pv.tile_expert[t_lo + threadIdx.x];
-        const int r0 = pv.tile_row0[t_lo + threadIdx.x];
-        st.e[threadIdx.x] = e;
-        st.cnt[threadIdx.x] = min(16, pv.counts[e] - r0);
-        st.base[threadIdx.x] = pv.offsets[e] + r0;
+        const int t = t_lo + threadIdx.x;
+        st.e[threadIdx.x] = pv.tile_expert[t];
+        st.cnt[threadIdx.x] = pv.tile_rows[t];
+        st.base[threadIdx.x] = pv.tile_base[t];
     }
-    __syncthreads();
     if ((int)threadIdx.x < ntl * 16) {
-        const int i = threadIdx.x >> 4, r = threadIdx.x & 15;
-        const int j = st.base[i] + r;
-        st.arow[i][r] = r < st.cnt[i] ? (topk > 0 ? pv.sorted_pair[j] / topk : j) : 0;
+        const int i = threadIdx.x >> 4, r = threadIdx.x & 15, t = t_lo + i;
+        const int n = pv.tile_rows[t];
+        const int p = r < n ? pv.tile_pair[(int64_t)t * 16 + r] : 0;  // padding rows: pair 0, never stored
+        st.pair[i][r] = p;
+        st.arow[i][r] = topk > 0 ? p / topk : pv.tile_base[t] + (r < n ? r : 0);
     }
     __syncthreads();
 }
 
-// Geometry shared by both kernels: SPLIT waves per tile pair (parallel chunks), 4/SPLIT tile pairs
-// per unit; `red` is the reduction length.
+// Tuning of the streaming kernels: TP 16-row weight-tile pairs per wave per unit, OCC resident
+// 256-thread blocks per CU.
+#ifndef NVFP4_W13_TP
+#define NVFP4_W13_TP 1
+#endif
+#ifndef NVFP4_W2_TP
+#define NVFP4_W2_TP 1
+#endif
+#ifndef NVFP4_STREAM_OCC
+#define NVFP4_STREAM_OCC 3
+#endif
+constexpr int W13_TP = NVFP4_W13_TP;
+constexpr int W2_TP = NVFP4_W2_TP;
+constexpr int STREAM_OCC = NVFP4_STREAM_OCC;
+
+// Geometry shared by both kernels: SPLIT waves per wave group (parallel chunks), 4/SPLIT wave
+// groups per unit; `red` is the reduction length.
 template <int SPLIT>
 struct Geo {
-    static constexpr int PAIRS = 4 / SPLIT;
+    static constexpr int GROUPS = 4 / SPLIT;
     int lane, wave, n, q, sub, c, S, kb, kb_ld, q_ld;
     bool chunk, qv;  // this wave has a chunk; this lane group has data in it
     __device__ Geo(int red)
@@ -108,36 +126,38 @@ __device__ __forceinline__ void load_a_chunk(f16x8 af[4][4], const f16 *row, boo
         for (int s = 0; s < 4; ++s) af[b][s] = valid ? a_frag(row, kb, q, b, s) : zero8();
 }
 
-// One chunk of two weight rows (tiles) against the resident A fragments.
-__device__ __forceinline__ void mma_chunk2(const RawChunk &w0, const RawChunk &w1, const f16x8 af[4][4], bool qv,
-                                           f32x4 &acc0, f32x4 &acc1)
+// One chunk of NW weight rows (tiles) against the resident A fragments.
+template <int NW>
+__device__ __forceinline__ void mma_chunk(const RawChunk (&w)[NW], const f16x8 af[4][4], bool qv, f32x4 (&acc)[NW])
 {
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        const f16x2 sc0 = chunk_scales(w0, b), sc1 = chunk_scales(w1, b);
+        f16x2 sc[NW];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            acc0 = mfma_step(af[b][s], b_frag(w0, sc0, b, s, qv), acc0);
-            acc1 = mfma_step(af[b][s], b_frag(w1, sc1, b, s, qv), acc1);
-        }
+        for (int t = 0; t < NW; ++t) sc[t] = chunk_scales(w[t], b);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int t = 0; t < NW; ++t) acc[t] = mfma_step(af[b][s], b_frag(w[t], sc[t], b, s, qv), acc[t]);
     }
 }
 
 // ---- W13 + SwiGLU ---------------------------------------------------------------------------------
-// Unit = (row tile, PAIRS consecutive 16-wide i slices); wave (sub, c) owns the gate and up rows of
-// slice PAIRS*unit_index + sub for chunk c.
-template <int SPLIT>
-__global__ __launch_bounds__(256, 3) void w13_swiglu_stream_kernel(PlanView pv, int topk, const f16 *__restrict__ x,
-                                                                    const uint8_t *__restrict__ codes,
-                                                                    const uint8_t *__restrict__ scales,
-                                                                    const float *__restrict__ gscale, int K, int I,
-                                                                    int layout, f16 *__restrict__ h)
+// Unit = (row tile, GROUPS*TP consecutive 16-wide i slices); wave (sub, c) owns the gate and up rows
+// of slices (GROUPS*unit_index + sub)*TP .. +TP-1 for chunk c.
+template <int SPLIT, int TP>
+__global__ __launch_bounds__(256, STREAM_OCC) void w13_swiglu_stream_kernel(PlanView pv, int topk, const f16 *__restrict__ x,
+                                                                             const uint8_t *__restrict__ codes,
+                                                                             const uint8_t *__restrict__ scales,
+                                                                             const float *__restrict__ gscale, int K, int I,
+                                                                             int layout, f16 *__restrict__ h)
 {
     using G = Geo<SPLIT>;
-    __shared__ float part[4][2][16][LDS_ROW];
+    constexpr int SL = G::GROUPS * TP;  // i slices per unit
+    __shared__ float part[4][2 * TP][16][LDS_ROW];
     __shared__ TileStage st;
     const int itiles = I >> 4;
-    const int upt = (itiles + G::PAIRS - 1) / G::PAIRS;  // units per row tile
+    const int upt = (itiles + SL - 1) / SL;  // units per row tile
     int64_t u0, u1;
     if (!unit_range((int64_t)pv.hdr[3] * upt, u0, u1)) return;  // block-uniform
     const int t_lo = (int)(u0 / upt);
@@ -149,62 +169,72 @@ __global__ __launch_bounds__(256, 3) void w13_swiglu_stream_kernel(PlanView pv, 
     f16x8 af[4][4];
     for (int64_t u = u0; u < u1; ++u) {
         const int ti = (int)(u / upt) - t_lo;
-        const int it = (int)(u % upt) * G::PAIRS + g.sub;
+        const int it0 = (int)(u % upt) * SL + g.sub * TP;
         const int e = st.e[ti], cnt = st.cnt[ti], base = st.base[ti];
-        f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-        if (g.chunk && it < itiles) {
-            const int i_row = it * 16 + g.n;
-            const int rg = layout ? 2 * i_row : i_row;
-            const int ru = layout ? 2 * i_row + 1 : I + i_row;
+        f32x4 acc[2 * TP];
+#pragma unroll
+        for (int t = 0; t < 2 * TP; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (g.chunk && it0 < itiles) {
             const size_t eb = (size_t)e * 2 * I;
-            const RawChunk wg = load_chunk(codes + (eb + rg) * crow, scales + (eb + rg) * srow, g.kb_ld, g.q_ld);
-            const RawChunk wu = load_chunk(codes + (eb + ru) * crow, scales + (eb + ru) * srow, g.kb_ld, g.q_ld);
+            RawChunk w[2 * TP];
+#pragma unroll
+            for (int p = 0; p < TP; ++p) {
+                const int i_row = min(it0 + p, itiles - 1) * 16 + g.n;  // a missing last slice re-reads a valid one
+                const int rg = layout ? 2 * i_row : i_row;
+                const int ru = layout ? 2 * i_row + 1 : I + i_row;
+                w[2 * p] = load_chunk(codes + (eb + rg) * crow, scales + (eb + rg) * srow, g.kb_ld, g.q_ld);
+                w[2 * p + 1] = load_chunk(codes + (eb + ru) * crow, scales + (eb + ru) * srow, g.kb_ld, g.q_ld);
+            }
             if (ti != cur) {  // A of this tile's rows, reused by every unit of the tile
                 cur = ti;
                 load_a_chunk(af, x + (size_t)st.arow[ti][g.n] * K, g.qv && g.n < cnt, g.kb, g.q);
             }
-            mma_chunk2(wg, wu, af, g.qv, accg, accu);
+            mma_chunk<2 * TP>(w, af, g.qv, acc);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            part[g.wave][0][4 * g.q + j][g.n] = accg[j];
-            part[g.wave][1][4 * g.q + j][g.n] = accu[j];
-        }
+        for (int t = 0; t < 2 * TP; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) part[g.wave][t][4 * g.q + j][g.n] = acc[t][j];
         __syncthreads();
         const float gs = gscale[e];
         const int row = threadIdx.x >> 4, col = threadIdx.x & 15;
 #pragma unroll
-        for (int p = 0; p < G::PAIRS; ++p) {
-            const int itx = (int)(u % upt) * G::PAIRS + p;
-            if (itx < itiles && row < cnt) {
-                float Gs = part[p * SPLIT][0][row][col];
-                float Us = part[p * SPLIT][1][row][col];
-                for (int cc = 1; cc < g.S; ++cc) {
-                    Gs += part[p * SPLIT + cc][0][row][col];
-                    Us += part[p * SPLIT + cc][1][row][col];
+        for (int gp = 0; gp < G::GROUPS; ++gp)
+#pragma unroll
+            for (int p = 0; p < TP; ++p) {
+                const int itx = (int)(u % upt) * SL + gp * TP + p;
+                if (itx < itiles && row < cnt) {
+                    float Gs = part[gp * SPLIT][2 * p][row][col];
+                    float Us = part[gp * SPLIT][2 * p + 1][row][col];
+                    for (int cc = 1; cc < g.S; ++cc) {
+                        Gs += part[gp * SPLIT + cc][2 * p][row][col];
+                        Us += part[gp * SPLIT + cc][2 * p + 1][row][col];
+                    }
+                    h[(size_t)(base + row) * I + itx * 16 + col] = (f16)swiglu(Gs * gs, Us * gs);
                 }
-                h[(size_t)(base + row) * I + itx * 16 + col] = (f16)swiglu(Gs * gs, Us * gs);
             }
-        }
         __syncthreads();
     }
 }
 
-// ---- W2: per-pair FP32 results y[j][n] = global * sum_i dq(W2)[n][i] * h[j][i] -------------------------
-// Unit = (row tile, 2*PAIRS consecutive 16-row output tiles); wave (sub, c) owns output tiles
-// 2*(PAIRS*unit_index + sub) and +1 for chunk c. With one chunk (I <= 512) the waves never meet.
-template <int SPLIT>
-__global__ __launch_bounds__(256, 3) void w2_stream_kernel(PlanView pv, const f16 *__restrict__ hin,
-                                                            const uint8_t *__restrict__ codes,
-                                                            const uint8_t *__restrict__ scales,
-                                                            const float *__restrict__ gscale, int K, int I,
-                                                            float *__restrict__ ws)
+// ---- W2: per-pair FP32 results y[p][n] = global * sum_i dq(W2)[n][i] * h[j][i], stored in pair order -----
+// Unit = (row tile, 2*GROUPS*TP consecutive 16-row output tiles); wave (sub, c) owns output tiles
+// 2*TP*(GROUPS*unit_index + sub) .. +2*TP-1 for chunk c. With one chunk (I <= 512) the waves never
+// meet.
+template <int SPLIT, int TP>
+__global__ __launch_bounds__(256, STREAM_OCC) void w2_stream_kernel(PlanView pv, const f16 *__restrict__ hin,
+                                                                     const uint8_t *__restrict__ codes,
+                                                                     const uint8_t *__restrict__ scales,
+                                                                     const float *__restrict__ gscale, int K, int I,
+                                                                     float *__restrict__ ws)
 {
     using G = Geo<SPLIT>;
-    __shared__ float part[SPLIT > 1 ? 4 : 1][2][16][LDS_ROW];
+    constexpr int NT = 2 * TP;            // output tiles per wave
+    constexpr int UT = G::GROUPS * NT;    // output tiles per unit
+    __shared__ float part[SPLIT > 1 ? 4 : 1][NT][16][LDS_ROW];
     __shared__ TileStage st;
-    const int npairs = K >> 5;  // K is a multiple of 64 (host check)
-    const int upt = (npairs + G::PAIRS - 1) / G::PAIRS;
+    const int ntiles = K >> 4;
+    const int upt = (ntiles + UT - 1) / UT;
     int64_t u0, u1;
     if (!unit_range((int64_t)pv.hdr[3] * upt, u0, u1)) return;
     const int t_lo = (int)(u0 / upt);
@@ -216,19 +246,24 @@ __global__ __launch_bounds__(256, 3) void w2_stream_kernel(PlanView pv, const f1
     f16x8 af[4][4];
     for (int64_t u = u0; u < u1; ++u) {
         const int ti = (int)(u / upt) - t_lo;
-        const int tp = (int)(u % upt) * G::PAIRS + g.sub;
+        const int nt0 = (int)(u % upt) * UT + g.sub * NT;
         const int e = st.e[ti], cnt = st.cnt[ti], base = st.base[ti];
-        const bool working = g.chunk && tp < npairs;
-        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+        const bool working = g.chunk && nt0 < ntiles;
+        f32x4 acc[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (working) {
-            const size_t r0 = (size_t)e * K + tp * 32 + g.n, r1 = r0 + 16;
-            const RawChunk w0 = load_chunk(codes + r0 * crow, scales + r0 * srow, g.kb_ld, g.q_ld);
-            const RawChunk w1 = load_chunk(codes + r1 * crow, scales + r1 * srow, g.kb_ld, g.q_ld);
+            RawChunk w[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const size_t r = (size_t)e * K + min(nt0 + t, ntiles - 1) * 16 + g.n;
+                w[t] = load_chunk(codes + r * crow, scales + r * srow, g.kb_ld, g.q_ld);
+            }
             if (ti != cur) {
                 cur = ti;
                 load_a_chunk(af, hin + (size_t)st.arow[ti][g.n] * I, g.qv && g.n < cnt, g.kb, g.q);
             }
-            mma_chunk2(w0, w1, af, g.qv, acc0, acc1);
+            mma_chunk<NT>(w, af, g.qv, acc);
         }
         const float gs = gscale[e];
         if constexpr (SPLIT == 1) {
@@ -237,39 +272,40 @@ __global__ __launch_bounds__(256, 3) void w2_stream_kernel(PlanView pv, const f1
                 for (int j = 0; j < 4; ++j) {
                     const int row = 4 * g.q + j;
                     if (row < cnt) {
-                        float *y = ws + (size_t)(base + row) * K + tp * 32 + g.n;
-                        y[0] = acc0[j] * gs;
-                        y[16] = acc1[j] * gs;
+                        float *y = ws + (size_t)st.pair[ti][row] * K + nt0 * 16 + g.n;
+#pragma unroll
+                        for (int t = 0; t < NT; ++t)
+                            if (nt0 + t < ntiles) y[16 * t] = acc[t][j] * gs;
                     }
                 }
             }
         } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                part[g.wave][0][4 * g.q + j][g.n] = acc0[j];
-                part[g.wave][1][4 * g.q + j][g.n] = acc1[j];
-            }
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) part[g.wave][t][4 * g.q + j][g.n] = acc[t][j];
             __syncthreads();
             const int row = threadIdx.x >> 4, col = threadIdx.x & 15;
 #pragma unroll
-            for (int p = 0; p < G::PAIRS; ++p) {
-                const int tpx = (int)(u % upt) * G::PAIRS + p;
-                if (tpx < npairs && row < cnt) {
+            for (int gp = 0; gp < G::GROUPS; ++gp)
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        float Y = part[p * SPLIT][t][row][col];
-                        for (int cc = 1; cc < g.S; ++cc) Y += part[p * SPLIT + cc][t][row][col];
-                        ws[(size_t)(base + row) * K + tpx * 32 + 16 * t + col] = Y * gs;
+                for (int t = 0; t < NT; ++t) {
+                    const int ntx = (int)(u % upt) * UT + gp * NT + t;
+                    if (ntx < ntiles && row < cnt) {
+                        float Y = part[gp * SPLIT][t][row][col];
+                        for (int cc = 1; cc < g.S; ++cc) Y += part[gp * SPLIT + cc][t][row][col];
+                        ws[(size_t)st.pair[ti][row] * K + ntx * 16 + col] = Y * gs;
                     }
                 }
-            }
             __syncthreads();
         }
     }
 }
 
 // ---- slot-order weighted reduction: out[t][n] = fp16( fmaf chain over valid slots ) -----------------
-// Each thread owns 4 consecutive columns of one token.
+// ws holds y in pair order (row p = t*topk + k), so the y loads do not wait for the plan; a slot
+// is valid when the plan placed its pair (pos_of_pair >= 0). Rows of invalid pairs are never
+// written and never used. Each thread owns 4 consecutive columns of one token.
 __global__ __launch_bounds__(256) void reduce_kernel(const int32_t *__restrict__ pos_of_pair, const float *__restrict__ tw,
                                                      const float *__restrict__ ws, int topk, int K, int blocks_per_token,
                                                      f16 *__restrict__ out)
@@ -280,14 +316,16 @@ __global__ __launch_bounds__(256) void reduce_kernel(const int32_t *__restrict__
     if (n >= K) return;
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
     for (int k = 0; k < topk; ++k) {
-        const int j = pos_of_pair[(size_t)t * topk + k];
-        if (j < 0) continue;
-        const float w = tw[(size_t)t * topk + k];
-        const float4 y = *reinterpret_cast<const float4 *>(ws + (size_t)j * K + n);
-        s0 = fmaf(w, y.x, s0);
-        s1 = fmaf(w, y.y, s1);
-        s2 = fmaf(w, y.z, s2);
-        s3 = fmaf(w, y.w, s3);
+        const size_t p = (size_t)t * topk + k;
+        const bool valid = pos_of_pair[p] >= 0;
+        const float w = tw[p];
+        const float4 y = *reinterpret_cast<const float4 *>(ws + p * K + n);
+        if (valid) {
+            s0 = fmaf(w, y.x, s0);
+            s1 = fmaf(w, y.y, s1);
+            s2 = fmaf(w, y.z, s2);
+            s3 = fmaf(w, y.w, s3);
+        }
     }
     typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
     *reinterpret_cast<f16x4 *>(out + (size_t)t * K + n) = f16x4{(f16)s0, (f16)s1, (f16)s2, (f16)s3};
@@ -299,13 +337,14 @@ int split_for(int k)
     return s <= 1 ? 1 : (s <= 2 ? 2 : 4);
 }
 
-// Persistent grid: three 256-thread blocks per CU, never more blocks than units, and enough blocks
-// that no block's unit range spans more than MAX_RANGE_TILES row tiles (range <= t_max/G + 2).
+// Persistent grid: STREAM_OCC 256-thread blocks per CU, never more blocks than units, and enough
+// blocks that no block's unit range spans more than MAX_RANGE_TILES row tiles
+// (range <= t_max/G + 2).
 unsigned stream_grid(int64_t units_max, int64_t t_max)
 {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    int64_t g = 3 * (int64_t)cus;
+    int64_t g = STREAM_OCC * (int64_t)cus;
     const int64_t g_min = (t_max + MAX_RANGE_TILES - 3) / (MAX_RANGE_TILES - 2);
     if (g < g_min) g = g_min;
     if (g > units_max) g = units_max;
@@ -319,15 +358,15 @@ int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, 
 {
     const int K = w.k, I = w.rows / 2;
     const int split = split_for(K);
-    const int pairs = 4 / split;
-    const int upt = (I / 16 + pairs - 1) / pairs;
+    const int sl = (4 / split) * W13_TP;
+    const int upt = (I / 16 + sl - 1) / sl;
     const dim3 grid(stream_grid(t_max * upt, t_max)), block(256);
     const f16 *xp = reinterpret_cast<const f16 *>(x);
     f16 *hp = reinterpret_cast<f16 *>(h);
     switch (split) {
-    case 1: return launch(w13_swiglu_stream_kernel<1>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp);
-    case 2: return launch(w13_swiglu_stream_kernel<2>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp);
-    default: return launch(w13_swiglu_stream_kernel<4>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp);
+    case 1: return launch(w13_swiglu_stream_kernel<1, W13_TP>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp);
+    case 2: return launch(w13_swiglu_stream_kernel<2, W13_TP>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp);
+    default: return launch(w13_swiglu_stream_kernel<4, W13_TP>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp);
     }
 }
 
@@ -336,15 +375,15 @@ int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uin
 {
     const int K = w.rows, I = w.k;
     const int split = split_for(I);
-    const int pairs = 4 / split;
-    const int upt = (K / 32 + pairs - 1) / pairs;
+    const int ut = (4 / split) * 2 * W2_TP;
+    const int upt = (K / 16 + ut - 1) / ut;
     const dim3 grid(stream_grid(t_max * upt, t_max)), block(256);
     const f16 *hp = reinterpret_cast<const f16 *>(h);
     int st;
     switch (split) {
-    case 1: st = launch(w2_stream_kernel<1>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws); break;
-    case 2: st = launch(w2_stream_kernel<2>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws); break;
-    default: st = launch(w2_stream_kernel<4>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws); break;
+    case 1: st = launch(w2_stream_kernel<1, W2_TP>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws); break;
+    case 2: st = launch(w2_stream_kernel<2, W2_TP>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws); break;
+    default: st = launch(w2_stream_kernel<4, W2_TP>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws); break;
     }
     if (st != NVFP4_OK) return st;
     return run_reduce(pv, M, topk, K, topk_weights, ws, out, s);

@@ -7,7 +7,9 @@
 // ascending pair index p = t*topk + k. That makes it unique, and every path below produces it
 // bit-exactly.
 //   - Small path, P <= 1024 pairs (the decode regime): one 1024-thread block builds everything
-//     in LDS in one launch. At M = 1 the number of launches dominates the cost.
+//     in LDS in one launch. A pair takes a ticket in its expert's group while counting; once the
+//     offsets are known, the group's pairs are listed and each pair's stable rank is the number
+//     of group members with a smaller index.
 //   - Large path (prefill): pairs are cut into chunks of 256, each with its own expert histogram.
 //     A per-expert scan over chunks gives every (expert, chunk) its start. Within a chunk a
 //     pair's rank counts the earlier pairs of the same expert, so the scatter is stable with no
@@ -48,28 +50,79 @@ __device__ __forceinline__ int block_excl_scan(int v, int *wsum, int nwaves, int
     return pre + incl - v;
 }
 
-// Writes counts, offsets, the active list, the row-tile list and header words 0,1,3 from per-expert
-// counts `cnt` (LDS or global). Also leaves offsets in `off_lds` (E+1 ints of LDS) for the
-// caller. Runs on a 1024-thread block; E <= 4096, so each thread owns up to 4 consecutive experts.
-__device__ void build_lists(const int *cnt, int E, int32_t *plan, const PlanLayout &L, int *off_lds, int *wsum)
+// Three exclusive scans at once over a 1024-thread block (one pair of barriers). `wsum` is LDS
+// scratch of 48 ints.
+__device__ __forceinline__ int3 block_excl_scan3(int3 v, int *wsum, int3 *total)
+{
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int ix = wave_incl_scan(v.x), iy = wave_incl_scan(v.y), iz = wave_incl_scan(v.z);
+    if (lane == 63) {
+        wsum[wid] = ix;
+        wsum[16 + wid] = iy;
+        wsum[32 + wid] = iz;
+    }
+    __syncthreads();
+    int3 pre{0, 0, 0}, tot{0, 0, 0};
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        const int sx = wsum[w], sy = wsum[16 + w], sz = wsum[32 + w];
+        if (w < wid) {
+            pre.x += sx;
+            pre.y += sy;
+            pre.z += sz;
+        }
+        tot.x += sx;
+        tot.y += sy;
+        tot.z += sz;
+    }
+    __syncthreads();
+    *total = tot;
+    return int3{pre.x + ix - v.x, pre.y + iy - v.y, pre.z + iz - v.z};
+}
+
+// Stable rank of this thread's pair among the block's earlier pairs: how many of ids4[0 .. tid)
+// equal `id` (id >= 0). ids4 holds the block's ids, four per int4, padded to the wave's end with
+// values that match no id. The loop bound is uniform per wave and eight 16-byte LDS reads are in
+// flight at a time (every lane reads the same address: a broadcast).
+__device__ __forceinline__ int stable_rank(const int4 *ids4, int tid, int id)
+{
+    const int n4 = ((tid | 63) + 1) >> 2;
+    int rank = 0;
+#pragma unroll 8
+    for (int j4 = 0; j4 < n4; ++j4) {
+        const int4 v = ids4[j4];
+        const int j = 4 * j4;
+        rank += (v.x == id && j < tid) + (v.y == id && j + 1 < tid) + (v.z == id && j + 2 < tid) +
+                (v.w == id && j + 3 < tid);
+    }
+    return rank;
+}
+
+// Writes counts, offsets, the active list, the row-tile lists (expert, first row, first bucket row,
+// row count) and header words 0,1,3 from per-expert counts `cnt` (LDS or global). Also leaves offsets in `off_lds` (E+1 ints of LDS) and
+// each expert's first tile index in `tile_first` (E ints, LDS or global) for the caller. Runs on a
+// 1024-thread block; E <= 4096, so each thread owns up to 4 consecutive experts.
+__device__ void build_lists(const int *cnt, int E, int32_t *plan, const PlanLayout &L, int *off_lds, int *tile_first,
+                            int *wsum)
 {
     const int ept = (E + 1023) / 1024;
     const int e0 = threadIdx.x * ept;
-    int c[4], csum = 0, asum = 0, tsum = 0;
+    int c[4];
+    int3 sums{0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = e0 + i;
         c[i] = (i < ept && e < E) ? cnt[e] : 0;
-        csum += c[i];
-        asum += c[i] > 0;
-        tsum += (c[i] + PLAN_TILE_ROWS - 1) / PLAN_TILE_ROWS;
+        sums.x += c[i];
+        sums.y += c[i] > 0;
+        sums.z += (c[i] + PLAN_TILE_ROWS - 1) / PLAN_TILE_ROWS;
     }
-    int ctot, atot, ttot;
-    int cpre = block_excl_scan(csum, wsum, 16, &ctot);
-    int apre = block_excl_scan(asum, wsum, 16, &atot);
-    int tpre = block_excl_scan(tsum, wsum, 16, &ttot);
+    int3 tot;
+    const int3 pre = block_excl_scan3(sums, wsum, &tot);
+    int cpre = pre.x, apre = pre.y, tpre = pre.z;
     int32_t *counts = plan + L.counts, *offsets = plan + L.offsets, *active = plan + L.active;
-    int32_t *tile_e = plan + L.tile_expert, *tile_r = plan + L.tile_row0;
+    int32_t *tile_e = plan + L.tile_expert, *tile_r = plan + L.tile_row0, *tile_b = plan + L.tile_base;
+    int32_t *tile_n = plan + L.tile_rows;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = e0 + i;
@@ -77,24 +130,38 @@ __device__ void build_lists(const int *cnt, int E, int32_t *plan, const PlanLayo
         counts[e] = c[i];
         offsets[e] = cpre;
         off_lds[e] = cpre;
+        tile_first[e] = tpre;
         if (c[i] > 0) {
             active[apre++] = e;
             for (int r = 0; r < c[i]; r += PLAN_TILE_ROWS) {
+                const int rows = min(PLAN_TILE_ROWS, c[i] - r);
                 tile_e[tpre] = e;
                 tile_r[tpre] = r;
+                tile_b[tpre] = cpre + r;
+                tile_n[tpre] = rows;
                 ++tpre;
             }
         }
         cpre += c[i];
     }
     if (threadIdx.x == 0) {
-        offsets[E] = ctot;
-        off_lds[E] = ctot;
+        offsets[E] = tot.x;
+        off_lds[E] = tot.x;
         int32_t *hdr = plan + L.hdr;
-        hdr[0] = ctot;
-        hdr[1] = atot;
-        hdr[3] = ttot;
+        hdr[0] = tot.x;
+        hdr[1] = tot.y;
+        hdr[3] = tot.z;
     }
+}
+
+// Records a valid pair's place: sorted_pair, pos_of_pair and its row in its tile's pair list.
+__device__ __forceinline__ void place_pair(int32_t *plan, const PlanLayout &L, int64_t p, int pos, int row_in_expert,
+                                           int first_tile)
+{
+    plan[L.sorted_pair + pos] = (int32_t)p;
+    plan[L.pos_of_pair + p] = pos;
+    const int64_t t = first_tile + row_in_expert / PLAN_TILE_ROWS;
+    plan[L.tile_pair + t * PLAN_TILE_ROWS + row_in_expert % PLAN_TILE_ROWS] = (int32_t)p;
 }
 
 __device__ __forceinline__ void write_header_tail(int32_t *plan, const PlanLayout &L, int n_bad, int M, int topk, int E)
@@ -113,36 +180,40 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(const int32_t *__restr
 {
     __shared__ int cnt[MAX_EXPERTS];
     __shared__ int off[MAX_EXPERTS + 1];
-    __shared__ int id_s[SMALL_PLAN_PAIRS];
-    __shared__ int wsum[16];
+    __shared__ int first[MAX_EXPERTS];
+    __shared__ int slot[SMALL_PLAN_PAIRS];
+    __shared__ int wsum[48];
     __shared__ int bad;
     const int tid = threadIdx.x;
     const int P = (int)L.P;
+    const int raw = tid < P ? ids[tid] : -1;  // issued first: the only load of the kernel
     for (int e = tid; e < E; e += 1024) cnt[e] = 0;
     if (tid == 0) bad = 0;
     __syncthreads();
-    int id = -1;
+    // Count, and take a ticket inside the expert's group (arrival order, not yet stable).
+    int id = -1, ticket = 0;
     if (tid < P) {
-        const int raw = ids[tid];
-        const bool valid = raw >= 0 && raw < E;
-        id = valid ? raw : -1;
-        id_s[tid] = id;
-        if (valid) atomicAdd(&cnt[raw], 1);
-        else if (raw != -1) atomicAdd(&bad, 1);
+        if (raw >= 0 && raw < E) {
+            id = raw;
+            ticket = atomicAdd(&cnt[raw], 1);
+        } else if (raw != -1) {
+            atomicAdd(&bad, 1);
+        }
     }
     __syncthreads();
-    build_lists(cnt, E, plan, L, off, wsum);
+    build_lists(cnt, E, plan, L, off, first, wsum);
+    __syncthreads();
+    if (id >= 0) slot[off[id] + ticket] = tid;  // the group's pairs, in arrival order
     __syncthreads();
     if (tid < P) {
-        int32_t *sorted_pair = plan + L.sorted_pair, *pos_of_pair = plan + L.pos_of_pair;
         if (id >= 0) {
+            // Stable rank: pairs of the same group with a smaller index (groups are small at decode).
+            const int o = off[id], n = cnt[id];
             int rank = 0;
-            for (int j = 0; j < tid; ++j) rank += (id_s[j] == id);
-            const int pos = off[id] + rank;
-            sorted_pair[pos] = tid;
-            pos_of_pair[tid] = pos;
+            for (int i = 0; i < n; ++i) rank += slot[o + i] < tid;
+            place_pair(plan, L, tid, o + rank, rank, first[id]);
         } else {
-            pos_of_pair[tid] = -1;
+            plan[L.pos_of_pair + tid] = -1;
         }
     }
     if (tid == 0) write_header_tail(plan, L, bad, M, topk, E);
@@ -193,13 +264,13 @@ __global__ __launch_bounds__(256) void plan_scan_chunks_kernel(int E, int32_t *_
 __global__ __launch_bounds__(1024) void plan_lists_kernel(int M, int topk, int E, int32_t *__restrict__ plan, PlanLayout L)
 {
     __shared__ int off[MAX_EXPERTS + 1];
-    __shared__ int wsum[16];
+    __shared__ int wsum[48];
     __shared__ int cnt[MAX_EXPERTS];
     for (int e = threadIdx.x; e < E; e += 1024) cnt[e] = plan[L.counts + e];
     int bad = 0;
     for (int64_t g = threadIdx.x; g < L.G; g += 1024) bad += plan[L.badc + g];
     __syncthreads();
-    build_lists(cnt, E, plan, L, off, wsum);
+    build_lists(cnt, E, plan, L, off, plan + L.tile_first, wsum);
     int total_bad;
     block_excl_scan(bad, wsum, 16, &total_bad);
     if (threadIdx.x == 0) write_header_tail(plan, L, total_bad, M, topk, E);
@@ -210,7 +281,7 @@ __global__ __launch_bounds__(1024) void plan_lists_kernel(int M, int topk, int E
 __global__ __launch_bounds__(PLAN_CHUNK) void plan_scatter_kernel(const int32_t *__restrict__ ids, int E,
                                                                   int32_t *__restrict__ plan, PlanLayout L)
 {
-    __shared__ int id_s[PLAN_CHUNK];
+    __shared__ __attribute__((aligned(16))) int id_s[PLAN_CHUNK];
     const int g = blockIdx.x, tid = threadIdx.x;
     const int64_t p = (int64_t)g * PLAN_CHUNK + tid;
     int id = -1;
@@ -225,11 +296,9 @@ __global__ __launch_bounds__(PLAN_CHUNK) void plan_scatter_kernel(const int32_t 
         plan[L.pos_of_pair + p] = -1;
         return;
     }
-    int rank = 0;
-    for (int j = 0; j < tid; ++j) rank += (id_s[j] == id);
-    const int pos = plan[L.offsets + id] + plan[L.hist + (int64_t)id * L.G + g] + rank;
-    plan[L.sorted_pair + pos] = (int32_t)p;
-    plan[L.pos_of_pair + p] = pos;
+    const int rank = stable_rank(reinterpret_cast<const int4 *>(id_s), tid, id);
+    const int before = plan[L.hist + (int64_t)id * L.G + g] + rank;  // earlier pairs of expert id
+    place_pair(plan, L, p, plan[L.offsets + id] + before, before, plan[L.tile_first + id]);
 }
 
 }  // namespace

@@ -43,6 +43,7 @@ constexpr int PPT = PF_ROWS * 16 / 256; // 16-byte pieces of a staged quarter pe
 struct __attribute__((aligned(16))) PrefillShared {
     f16 a[NBUF][PF_ROWS][A_ROW];  // activation quarters: [buffer][row][lane group q: 32 elements]
     int arow[PF_ROWS];            // activation row (token or bucket row) of each pass row
+    int pair[PF_ROWS];            // pair index of each pass row (W2: where its result goes)
 };
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(256, 1) void w13_swiglu_prefill_kernel(PlanView pv,
     }
 }
 
-// ---- W2: per-pair FP32 results -----------------------------------------------------------------------
+// ---- W2: per-pair FP32 results, in pair order -----------------------------------------------------------------------
 // Wave w of block slice nb owns output tiles 16*nb + 4w .. +3 (64 output rows).
 __global__ __launch_bounds__(256, 1) void w2_prefill_kernel(PlanView pv, const f16 *__restrict__ hin, uint32_t h_bytes,
                                                              const uint8_t *__restrict__ codes,
@@ -341,8 +342,11 @@ __global__ __launch_bounds__(256, 1) void w2_prefill_kernel(PlanView pv, const f
     for (int rp = 0; rp < cnt; rp += PF_ROWS) {
         const int rows = min(PF_ROWS, cnt - rp);
         lds_barrier();
-        for (int r = threadIdx.x; r < rows; r += 256) sh.arow[r] = base + rp + r;
-        lds_barrier();
+        for (int r = threadIdx.x; r < rows; r += 256) {
+            sh.arow[r] = base + rp + r;
+            sh.pair[r] = pv.sorted_pair[base + rp + r];
+        }
+        __syncthreads();
         pass_dispatch(sh, src, rows, wo, working, n, q, [&](const f32x4 (&tot)[PF_R][PF_T], int nr) {
 #pragma unroll
             for (int r = 0; r < PF_R; ++r) {
@@ -351,7 +355,7 @@ __global__ __launch_bounds__(256, 1) void w2_prefill_kernel(PlanView pv, const f
                 for (int j = 0; j < 4; ++j) {
                     const int row = 16 * r + 4 * q + j;
                     if (row < rows) {
-                        float *y = ws + (size_t)(base + rp + row) * K + nt0 * 16 + n;
+                        float *y = ws + (size_t)sh.pair[row] * K + nt0 * 16 + n;
 #pragma unroll
                         for (int t = 0; t < PF_T; ++t)
                             if (nt0 + t < ntiles) y[16 * t] = tot[r][t][j] * gs;

@@ -86,11 +86,15 @@ const char *nvfp4_status_str(int status);
  * T = A + ceil(P/16)):
  *   [0] n_valid  [1] n_active  [2] n_bad  [3] n_tiles  [4] M  [5] topk  [6] E  [7] 16 (tile rows)
  *   [8..15] reserved
- *   counts[E]  offsets[E+1]  active[A]  tile_expert[T]  tile_row0[T]  sorted_pair[P]  pos_of_pair[P]
+ *   counts[E]  offsets[E+1]  active[A]  tile_expert[T]  tile_row0[T]  tile_base[T]  tile_rows[T]
+ *   tile_pair[T][16]  sorted_pair[P]  pos_of_pair[P]
  *   followed by internal scratch when P > 1024.
  * Within each array only the first n_valid / n_active / n_tiles entries are defined. pos_of_pair[p]
  * is the bucket-order row of pair p, or -1 if the pair was skipped. Active experts are in
- * ascending id order, and row tiles of 16 rows are in (expert, row0) order.
+ * ascending id order, and row tiles of 16 rows are in (expert, row0) order. Row tile t covers
+ * bucket rows tile_base[t] = offsets[e] + tile_row0[t] .. + tile_rows[t] - 1 of its expert e;
+ * tile_pair[t][r] is the pair of its row r (undefined for r >= tile_rows[t]). These are redundant with
+ * sorted_pair; they let a kernel reach a tile's rows with one dependent load.
  *
  * The plan stays valid until the caller overwrites it. W13 and W2 only read it, and must be given
  * the same M, topk and E. Requirements: 1 <= topk <= 32, 1 <= E <= 4096, M*topk <= 2^26.
@@ -127,7 +131,7 @@ int nvfp4_moe_w13_swiglu(const void *plan, int32_t M, int32_t topk, int32_t E,
  *   topk_weights  fp32 [M][topk]    used exactly as given (no renormalisation)
  *   out           fp16 [M][K]       every element is written
  *   ws            device workspace of at least nvfp4_moe_w2_workspace_bytes(M, topk, K) bytes,
- *                 contents ignored on entry (FP32 per-pair partials)
+ *                 contents ignored on entry (FP32 per-pair results, row p = t*topk + k)
  * y[j][n] = global[e] * sum_i dq(W2_e)[n][i] * h[j][i], in FP32 with no intermediate rounding. Then
  *   out[t][n] = fp16_rne( s ),  s = 0;  for k = 0..topk-1 with a valid id: s = fmaf(w[t][k], y[pos][n], s)
  * This is slot order. A token with no valid slot gets +0.

@@ -48,6 +48,18 @@ def test_plan_bit_exact(orc, M, topk, E, kind):
     for key in ("counts", "offsets", "active", "tile_expert", "tile_row0", "sorted_pair", "pos_of_pair"):
         assert np.array_equal(got[key], ref[key]), key
     assert list(got["hdr"][4:8]) == [M, topk, E, 16]
+    _check_tile_descriptors(got, ref)
+
+
+def _check_tile_descriptors(got, ref):
+    """tile_base / tile_rows / tile_pair restate the oracle's tiles and sorted order (header doc)."""
+    e, r0 = ref["tile_expert"], ref["tile_row0"]
+    base = ref["offsets"][e] + r0
+    rows = np.minimum(16, ref["counts"][e] - r0)
+    assert np.array_equal(got["tile_base"], base)
+    assert np.array_equal(got["tile_rows"], rows)
+    for t in range(len(e)):
+        assert np.array_equal(got["tile_pair"][t, :rows[t]], ref["sorted_pair"][base[t]:base[t] + rows[t]]), t
 
 
 def test_plan_rebuild_overwrites_stale_plan(orc):
