@@ -62,6 +62,9 @@ def parse():
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--traffic", action="store_true",
+                   help="counter-collection mode: a 256 MiB device copy (calibration), then 12 eager launches "
+                        "of the headline W13 kernel; prints nothing else")
     return p.parse_args()
 
 
@@ -163,6 +166,51 @@ def w13_kernel_timing(M, launches, W13, routes):
     return us, bytes_per_launch
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w13_swiglu_stream_decode16_traffic.txt")
+KERNEL_SOURCES = ("gemm_nvfp4_amd/csrc/moe_gemm.hip", "gemm_nvfp4_amd/csrc/nvfp4_device.hpp",
+                  "gemm_nvfp4_amd/csrc/internal.hpp")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline W13 kernel from the committed counter summary, or None
+    when the kernel sources changed since the counters were taken."""
+    try:
+        kv = dict(l.split(":", 1) for l in open(TRAFFIC_FILE).read().splitlines() if ":" in l and not l.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("source_hash", "").strip() != kernel_source_hash():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def traffic_mode(W13):
+    """Eager launches for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs: a device copy of known size
+    first (the calibration kernel), then the headline W13 kernel on 12 weight sets."""
+    import torch
+    import gemm_nvfp4_amd as G
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    routes = Routes(16, 12, 1000)
+    plans = [G.nvfp4_moe_plan(routes.ids[p], E) for p in range(12)]
+    h = torch.empty((16 * TOPK, I), dtype=torch.float16, device="cuda")
+    for i in range(12):
+        G.nvfp4_moe_w13_swiglu(plans[i], 16, TOPK, E, routes.x[i], W13[i % len(W13)], 0, h=h)
+    torch.cuda.synchronize()
+    algo = [routes.active[p] * W13_EXPERT_BYTES + 16 * K * 2 + routes.valid[p] * I * 2 for p in range(12)]
+    log(f"traffic mode done: copy 268435456 B x3; W13 x12, algorithmic bytes/launch {np.mean(algo):.0f}")
+
+
 def launch_floor(launches=480):
     import torch
     t = torch.zeros(1, device="cuda")
@@ -248,6 +296,9 @@ def main():
     W13, W2 = weight_sets(args.weight_sets)
     torch.cuda.synchronize()
     log(f"weight sets: {args.weight_sets} x {E * EXPERT_BYTES / 2**20:.0f} MiB")
+    if args.traffic:
+        traffic_mode(W13)
+        return
 
     routes16 = Routes(16, args.patterns, 1000)
     head = moe_layer_timing(16, args.steps, args.warmup, W13, W2, routes16)
@@ -287,8 +338,8 @@ def main():
                    "weight_sets": args.weight_sets, "route_patterns": args.patterns},
         "us_per_layer": head["us_per_layer"], "hbm_frac": head["hbm_frac"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "w13_swiglu_kernel<4>", "us_per_launch": round(k_us, 3),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "kernel": "w13_swiglu_stream_kernel<4, 1>", "us_per_launch": round(k_us, 3),
                      "algorithmic_bytes_per_launch": round(k_bytes)},
         "launch_floor_us": round(floor, 3),
         "sweep": sweep, "prefill": prefill, "dense": dense, "cpu_baseline": cpu,

@@ -76,7 +76,7 @@ __device__ __forceinline__ void stage_tiles(const PlanView &pv, TileStage &st, i
     __syncthreads();
 }
 
-// Tuning of the streaming kernels: TP 16-row weight-tile pairs per wave per unit, OCC resident
+// Tuning of the streaming kernels: TP 16-row weight-tile pairs per wave per unit, *_OCC resident
 // 256-thread blocks per CU.
 #ifndef NVFP4_W13_TP
 #define NVFP4_W13_TP 1
@@ -84,12 +84,16 @@ __device__ __forceinline__ void stage_tiles(const PlanView &pv, TileStage &st, i
 #ifndef NVFP4_W2_TP
 #define NVFP4_W2_TP 1
 #endif
-#ifndef NVFP4_STREAM_OCC
-#define NVFP4_STREAM_OCC 3
+#ifndef NVFP4_W13_OCC
+#define NVFP4_W13_OCC 2
+#endif
+#ifndef NVFP4_W2_OCC
+#define NVFP4_W2_OCC 3
 #endif
 constexpr int W13_TP = NVFP4_W13_TP;
 constexpr int W2_TP = NVFP4_W2_TP;
-constexpr int STREAM_OCC = NVFP4_STREAM_OCC;
+constexpr int W13_OCC = NVFP4_W13_OCC;
+constexpr int W2_OCC = NVFP4_W2_OCC;
 
 // Geometry shared by both kernels: SPLIT waves per wave group (parallel chunks), 4/SPLIT wave
 // groups per unit; `red` is the reduction length.
@@ -144,9 +148,10 @@ __device__ __forceinline__ void mma_chunk(const RawChunk (&w)[NW], const f16x8 a
 
 // ---- W13 + SwiGLU ---------------------------------------------------------------------------------
 // Unit = (row tile, GROUPS*TP consecutive 16-wide i slices); wave (sub, c) owns the gate and up rows
-// of slices (GROUPS*unit_index + sub)*TP .. +TP-1 for chunk c.
+// of slices (GROUPS*unit_index + sub)*TP .. +TP-1 for chunk c. A wave loads unit u+1's weights
+// while unit u computes; barriers order LDS only, so they do not wait for those loads.
 template <int SPLIT, int TP>
-__global__ __launch_bounds__(256, STREAM_OCC) void w13_swiglu_stream_kernel(PlanView pv, int topk, const f16 *__restrict__ x,
+__global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanView pv, int topk, const f16 *__restrict__ x,
                                                                              const uint8_t *__restrict__ codes,
                                                                              const uint8_t *__restrict__ scales,
                                                                              const float *__restrict__ gscale, int K, int I,
@@ -167,35 +172,46 @@ __global__ __launch_bounds__(256, STREAM_OCC) void w13_swiglu_stream_kernel(Plan
 
     int cur = -1;
     f16x8 af[4][4];
-    for (int64_t u = u0; u < u1; ++u) {
+    // Packed weights of unit u into w. Loads are unconditional (idle waves and missing slices
+    // re-read valid rows), so no branch separates them from the waits.
+    auto load_unit = [&](int64_t u, RawChunk (&w)[2 * TP]) {
+        const int ti = (int)(u / upt) - t_lo;
+        const int it0 = (int)(u % upt) * SL + g.sub * TP;
+        const size_t eb = (size_t)st.e[ti] * 2 * I;
+#pragma unroll
+        for (int p = 0; p < TP; ++p) {
+            const int i_row = min(it0 + p, itiles - 1) * 16 + g.n;
+            const int rg = layout ? 2 * i_row : i_row;
+            const int ru = layout ? 2 * i_row + 1 : I + i_row;
+            w[2 * p] = load_chunk(codes + (eb + rg) * crow, scales + (eb + rg) * srow, g.kb_ld, g.q_ld);
+            w[2 * p + 1] = load_chunk(codes + (eb + ru) * crow, scales + (eb + ru) * srow, g.kb_ld, g.q_ld);
+        }
+    };
+    // One unit: math on `w` (already loading), next unit's weights into `wn`. Called with the two
+    // buffers alternating, so no register copy ever waits on a load in flight.
+    auto step = [&](int64_t u, RawChunk (&w)[2 * TP], RawChunk (&wn)[2 * TP]) {
         const int ti = (int)(u / upt) - t_lo;
         const int it0 = (int)(u % upt) * SL + g.sub * TP;
         const int e = st.e[ti], cnt = st.cnt[ti], base = st.base[ti];
+        if (ti != cur) {  // A of this tile's rows, reused by every unit of the tile
+            cur = ti;
+            load_a_chunk(af, x + (size_t)st.arow[ti][g.n] * K, g.qv && g.n < cnt, g.kb, g.q);
+        }
+        load_unit(u + 1 < u1 ? u + 1 : u, wn);  // next unit's weights (the last unit re-reads itself)
+        __builtin_amdgcn_sched_barrier(0);      // keep those loads ahead of this unit's math
         f32x4 acc[2 * TP];
 #pragma unroll
         for (int t = 0; t < 2 * TP; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (g.chunk && it0 < itiles) {
-            const size_t eb = (size_t)e * 2 * I;
-            RawChunk w[2 * TP];
+        mma_chunk<2 * TP>(w, af, g.qv, acc);
+        if (!(g.chunk && it0 < itiles)) {
 #pragma unroll
-            for (int p = 0; p < TP; ++p) {
-                const int i_row = min(it0 + p, itiles - 1) * 16 + g.n;  // a missing last slice re-reads a valid one
-                const int rg = layout ? 2 * i_row : i_row;
-                const int ru = layout ? 2 * i_row + 1 : I + i_row;
-                w[2 * p] = load_chunk(codes + (eb + rg) * crow, scales + (eb + rg) * srow, g.kb_ld, g.q_ld);
-                w[2 * p + 1] = load_chunk(codes + (eb + ru) * crow, scales + (eb + ru) * srow, g.kb_ld, g.q_ld);
-            }
-            if (ti != cur) {  // A of this tile's rows, reused by every unit of the tile
-                cur = ti;
-                load_a_chunk(af, x + (size_t)st.arow[ti][g.n] * K, g.qv && g.n < cnt, g.kb, g.q);
-            }
-            mma_chunk<2 * TP>(w, af, g.qv, acc);
+            for (int t = 0; t < 2 * TP; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int t = 0; t < 2 * TP; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j) part[g.wave][t][4 * g.q + j][g.n] = acc[t][j];
-        __syncthreads();
+        lds_barrier();
         const float gs = gscale[e];
         const int row = threadIdx.x >> 4, col = threadIdx.x & 15;
 #pragma unroll
@@ -213,20 +229,26 @@ __global__ __launch_bounds__(256, STREAM_OCC) void w13_swiglu_stream_kernel(Plan
                     h[(size_t)(base + row) * I + itx * 16 + col] = (f16)swiglu(Gs * gs, Us * gs);
                 }
             }
-        __syncthreads();
+        lds_barrier();
+    };
+    RawChunk wa[2 * TP], wb[2 * TP];
+    load_unit(u0, wa);
+    for (int64_t u = u0; u < u1; u += 2) {
+        step(u, wa, wb);
+        if (u + 1 < u1) step(u + 1, wb, wa);
     }
 }
 
 // ---- W2: per-pair FP32 results y[p][n] = global * sum_i dq(W2)[n][i] * h[j][i], stored in pair order -----
 // Unit = (row tile, 2*GROUPS*TP consecutive 16-row output tiles); wave (sub, c) owns output tiles
 // 2*TP*(GROUPS*unit_index + sub) .. +2*TP-1 for chunk c. With one chunk (I <= 512) the waves never
-// meet.
+// meet. As in W13, unit u+1's weights load while unit u computes.
 template <int SPLIT, int TP>
-__global__ __launch_bounds__(256, STREAM_OCC) void w2_stream_kernel(PlanView pv, const f16 *__restrict__ hin,
-                                                                     const uint8_t *__restrict__ codes,
-                                                                     const uint8_t *__restrict__ scales,
-                                                                     const float *__restrict__ gscale, int K, int I,
-                                                                     float *__restrict__ ws)
+__global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, const f16 *__restrict__ hin,
+                                                                 const uint8_t *__restrict__ codes,
+                                                                 const uint8_t *__restrict__ scales,
+                                                                 const float *__restrict__ gscale, int K, int I,
+                                                                 float *__restrict__ ws)
 {
     using G = Geo<SPLIT>;
     constexpr int NT = 2 * TP;            // output tiles per wave
@@ -244,27 +266,33 @@ __global__ __launch_bounds__(256, STREAM_OCC) void w2_stream_kernel(PlanView pv,
 
     int cur = -1;
     f16x8 af[4][4];
-    for (int64_t u = u0; u < u1; ++u) {
+    // Packed weights of unit u into w; unconditional (idle waves re-read valid rows).
+    auto load_unit = [&](int64_t u, RawChunk (&w)[NT]) {
         const int ti = (int)(u / upt) - t_lo;
         const int nt0 = (int)(u % upt) * UT + g.sub * NT;
-        const int e = st.e[ti], cnt = st.cnt[ti], base = st.base[ti];
+        const size_t eb = (size_t)st.e[ti] * K;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const size_t r = eb + min(nt0 + t, ntiles - 1) * 16 + g.n;
+            w[t] = load_chunk(codes + r * crow, scales + r * srow, g.kb_ld, g.q_ld);
+        }
+    };
+    // One unit: math on `w`, next unit's weights into `wn` (the buffers alternate).
+    auto step = [&](int64_t u, RawChunk (&w)[NT], RawChunk (&wn)[NT]) {
+        const int ti = (int)(u / upt) - t_lo;
+        const int nt0 = (int)(u % upt) * UT + g.sub * NT;
+        const int e = st.e[ti], cnt = st.cnt[ti];
         const bool working = g.chunk && nt0 < ntiles;
+        if (ti != cur) {
+            cur = ti;
+            load_a_chunk(af, hin + (size_t)st.arow[ti][g.n] * I, g.qv && g.n < cnt, g.kb, g.q);
+        }
+        load_unit(u + 1 < u1 ? u + 1 : u, wn);  // the last unit re-reads itself
+        __builtin_amdgcn_sched_barrier(0);      // keep those loads ahead of this unit's math
         f32x4 acc[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (working) {
-            RawChunk w[NT];
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const size_t r = (size_t)e * K + min(nt0 + t, ntiles - 1) * 16 + g.n;
-                w[t] = load_chunk(codes + r * crow, scales + r * srow, g.kb_ld, g.q_ld);
-            }
-            if (ti != cur) {
-                cur = ti;
-                load_a_chunk(af, hin + (size_t)st.arow[ti][g.n] * I, g.qv && g.n < cnt, g.kb, g.q);
-            }
-            mma_chunk<NT>(w, af, g.qv, acc);
-        }
+        mma_chunk<NT>(w, af, g.qv, acc);
         const float gs = gscale[e];
         if constexpr (SPLIT == 1) {
             if (working) {
@@ -280,11 +308,15 @@ __global__ __launch_bounds__(256, STREAM_OCC) void w2_stream_kernel(PlanView pv,
                 }
             }
         } else {
+            if (!working) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) part[g.wave][t][4 * g.q + j][g.n] = acc[t][j];
-            __syncthreads();
+            lds_barrier();
             const int row = threadIdx.x >> 4, col = threadIdx.x & 15;
 #pragma unroll
             for (int gp = 0; gp < G::GROUPS; ++gp)
@@ -297,8 +329,14 @@ __global__ __launch_bounds__(256, STREAM_OCC) void w2_stream_kernel(PlanView pv,
                         ws[(size_t)st.pair[ti][row] * K + ntx * 16 + col] = Y * gs;
                     }
                 }
-            __syncthreads();
+            lds_barrier();
         }
+    };
+    RawChunk wa[NT], wb[NT];
+    load_unit(u0, wa);
+    for (int64_t u = u0; u < u1; u += 2) {
+        step(u, wa, wb);
+        if (u + 1 < u1) step(u + 1, wb, wa);
     }
 }
 
@@ -337,14 +375,14 @@ int split_for(int k)
     return s <= 1 ? 1 : (s <= 2 ? 2 : 4);
 }
 
-// Persistent grid: STREAM_OCC 256-thread blocks per CU, never more blocks than units, and enough
+// Persistent grid: `occ` 256-thread blocks per CU, never more blocks than units, and enough
 // blocks that no block's unit range spans more than MAX_RANGE_TILES row tiles
 // (range <= t_max/G + 2).
-unsigned stream_grid(int64_t units_max, int64_t t_max)
+unsigned stream_grid(int occ, int64_t units_max, int64_t t_max)
 {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    int64_t g = STREAM_OCC * (int64_t)cus;
+    int64_t g = occ * (int64_t)cus;
     const int64_t g_min = (t_max + MAX_RANGE_TILES - 3) / (MAX_RANGE_TILES - 2);
     if (g < g_min) g = g_min;
     if (g > units_max) g = units_max;
@@ -360,7 +398,7 @@ int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, 
     const int split = split_for(K);
     const int sl = (4 / split) * W13_TP;
     const int upt = (I / 16 + sl - 1) / sl;
-    const dim3 grid(stream_grid(t_max * upt, t_max)), block(256);
+    const dim3 grid(stream_grid(W13_OCC, t_max * upt, t_max)), block(256);
     const f16 *xp = reinterpret_cast<const f16 *>(x);
     f16 *hp = reinterpret_cast<f16 *>(h);
     switch (split) {
@@ -377,7 +415,7 @@ int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uin
     const int split = split_for(I);
     const int ut = (4 / split) * 2 * W2_TP;
     const int upt = (K / 16 + ut - 1) / ut;
-    const dim3 grid(stream_grid(t_max * upt, t_max)), block(256);
+    const dim3 grid(stream_grid(W2_OCC, t_max * upt, t_max)), block(256);
     const f16 *hp = reinterpret_cast<const f16 *>(h);
     int st;
     switch (split) {
