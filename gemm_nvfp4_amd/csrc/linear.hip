@@ -49,14 +49,28 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void linear_kernel(const f16 *__res
                 if (rt >= row_tiles) break;
                 const int m = rt * 16 + n;
                 const bool rv = m < M && qv;
+                // All 16 A fragments are loaded before the chain, unconditionally (rows past M and
+                // lane groups past K re-read valid data of row 0 / lane group 0, then become zeros),
+                // so their latencies overlap instead of adding up.
                 const f16 *xr = x + (size_t)(m < M ? m : 0) * K;
+                const int qa = qv ? q : 0;
+                f16x8 af[4][4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) af[b][s] = a_frag(xr, kb, qa, b, s);
+                __builtin_amdgcn_sched_barrier(0);  // every load (weights, then A) is issued before the math
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        if (!rv) af[b][s] = zero8();
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const f16x2 sc = chunk_scales(w, b);
 #pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        acc = mfma_step(rv ? a_frag(xr, kb, q, b, s) : zero8(), b_frag(w, sc, b, s, qv), acc);
+                    for (int s = 0; s < 4; ++s) acc = mfma_step(af[b][s], b_frag(w, sc, b, s, qv), acc);
                 }
                 float *pc = part + ((size_t)c * ROW_GROUP + r) * 16 * LDS_ROW;
 #pragma unroll
