@@ -39,6 +39,10 @@ constexpr int AQ = 32;                  // elements of one lane group per quarte
 constexpr int A_ROW = 4 * AQ + 8;       // staged quarter per row: 4 lane groups + 16 bytes of bank padding
 constexpr int NBUF = 3;                 // ring of quarter buffers
 constexpr int PPT = PF_ROWS * 16 / 256; // 16-byte pieces of a staged quarter per thread
+#ifndef NVFP4_W2S1_R
+#define NVFP4_W2S1_R 6
+#endif
+constexpr int W2S1_R = NVFP4_W2S1_R;   // row tiles per pass of the one-chunk W2 kernel
 
 struct __attribute__((aligned(16))) PrefillShared {
     f16 a[NBUF][PF_ROWS][A_ROW];  // activation quarters: [buffer][row][lane group q: 32 elements]
@@ -366,6 +370,162 @@ __global__ __launch_bounds__(256, 1) void w2_prefill_kernel(PlanView pv, const f
     }
 }
 
+// ---- W2 with one reduction chunk (I <= 512) ----------------------------------------------------------
+// Same block geometry as w2_prefill_kernel (16 output tiles per block, 4 per wave), specialised
+// for a single 512-element chunk:
+//   * the block's packed weights are loaded once and stay in registers for all of its passes;
+//   * bucket rows of an expert are contiguous, so the activation quarters of every pass form one
+//     stream (quarter g = 4*pass + b) and the next pass's first quarters load while this pass
+//     finishes;
+//   * each pass's accumulators are its results (one chain from +0, no chunk sum); they are stored
+//     in pair order right after the pass's last step.
+// Rows past the expert's end re-read its last row and are never stored.
+template <int NR>
+struct S1Shared {
+    f16 a[NBUF][16 * NR][A_ROW];
+    int pair[2][16 * NR];  // pair index of each row of pass p, in pair[p & 1]
+};
+
+template <int NR>
+__global__ __launch_bounds__(256, 1) void w2_prefill_s1_kernel(PlanView pv, const f16 *__restrict__ hin, uint32_t h_bytes,
+                                                               const uint8_t *__restrict__ codes,
+                                                               const uint8_t *__restrict__ scales,
+                                                               const float *__restrict__ gscale, int K, int I,
+                                                               float *__restrict__ ws, int a_max)
+{
+    constexpr int ROWS = 16 * NR;
+    constexpr int PIECES = ROWS * 16 / 256;  // 16-byte pieces of a staged quarter per thread
+    __shared__ __attribute__((aligned(16))) S1Shared<NR> sh;
+    const int ntiles = K >> 4;
+    const int nblk = (ntiles + 15) >> 4;
+    const int lb = xcd_logical_block(a_max * nblk);
+    if (lb < 0) return;
+    const int a = lb / nblk, nb = lb - a * nblk;
+    if (a >= pv.hdr[1]) return;
+    const int e = pv.active[a], cnt = pv.counts[e], base = pv.offsets[e];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, q = lane >> 4;
+    const int nt0 = nb * 16 + 4 * wave;
+    const bool working = nt0 < ntiles;
+    const uint32_t ebytes = (uint32_t)K * (uint32_t)(I >> 1);
+    const rsrc_t act = make_rsrc(hin, h_bytes);
+    const rsrc_t rc = make_rsrc(codes + (size_t)e * ebytes, ebytes);
+    const rsrc_t rs = make_rsrc(scales + (size_t)e * (ebytes >> 3), ebytes >> 3);
+    const int groups = I >> 7;  // 128-element lane groups with data (1..4)
+    const bool qv = q < groups;
+    const float gs = gscale[e];
+    const int npass = (cnt + ROWS - 1) / ROWS, G = 4 * npass;
+
+    // The whole reduction axis of the block's four weight tiles, once.
+    RawChunk w[PF_T];
+#pragma unroll
+    for (int t = 0; t < PF_T; ++t) {
+        const uint32_t wo = (uint32_t)(min(nt0 + t, ntiles - 1) * 16 + n) * (uint32_t)(I >> 1) + 64 * (qv ? q : 0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) w[t].codes[b] = bload16(rc, wo + 16 * b, 0);
+        w[t].scales[0] = bload4(rs, wo >> 3, 0);
+        w[t].scales[1] = bload4(rs, (wo >> 3) + 4, 0);
+    }
+
+    const int qs = (threadIdx.x >> 2) & 3, ps = threadIdx.x & 3, srow = threadIdx.x >> 4;
+    const bool qs_ok = qs < groups;
+    struct Stage {
+        u32x4 v[PIECES];
+    };
+    auto stage_load = [&](Stage &st, int g) {
+        g = g < G ? g : G - 1;
+        const int r0 = (g >> 2) * ROWS;
+#pragma unroll
+        for (int i = 0; i < PIECES; ++i) {
+            const int row = base + min(r0 + srow + 16 * i, cnt - 1);
+            st.v[i] = bload16(act, (uint32_t)row * (uint32_t)(I * 2) + 256 * (qs_ok ? qs : 0) + 16 * ps, AQ * 2 * (g & 3));
+        }
+    };
+    auto stage_store = [&](const Stage &st, int buf) {
+#pragma unroll
+        for (int i = 0; i < PIECES; ++i)
+            *reinterpret_cast<u32x4 *>(&sh.a[buf][srow + 16 * i][AQ * qs + 8 * ps]) = qs_ok ? st.v[i] : u32x4{0, 0, 0, 0};
+    };
+    auto pairs_load = [&](int p) {  // pair indices of pass p's rows, one per thread
+        const int r = p * ROWS + (int)threadIdx.x;
+        return (int)threadIdx.x < ROWS && p < npass && r < cnt ? pv.sorted_pair[base + r] : 0;
+    };
+    auto buf_next = [](int x) { return x == NBUF - 1 ? 0 : x + 1; };
+
+    // Prologue: quarters 0 and 1 in LDS, quarter 2 loading; pass 0's pair list in LDS.
+    Stage st[2];
+    stage_load(st[0], 0);
+    stage_load(st[1], 1);
+    const int pr0 = pairs_load(0);
+    stage_store(st[0], 0);
+    stage_store(st[1], 1);
+    if ((int)threadIdx.x < ROWS) sh.pair[0][threadIdx.x] = pr0;
+    stage_load(st[0], 2);
+    __syncthreads();
+
+    f16x2 sc[PF_T][4];  // block scales of every step group, decoded once
+#pragma unroll
+    for (int t = 0; t < PF_T; ++t)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) sc[t][b] = qv ? chunk_scales(w[t], b) : f16x2{0, 0};
+    f32x4 ca[NR][PF_T];
+    f16x8 bf[2][PF_T], av[NR];
+    auto decode = [&](int slot, int b, int s) {
+#pragma unroll
+        for (int t = 0; t < PF_T; ++t) bf[slot][t] = decode8(w[t].codes[b][s], sc[t][b][s >> 1]);
+    };
+    auto a_read = [&](int r, int s, int buf) {
+        return *reinterpret_cast<const f16x8 *>(&sh.a[buf][16 * r + n][AQ * q + 8 * s]);
+    };
+    int cur = 0;
+    decode(0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) av[r] = a_read(r, 0, 0);
+    for (int p = 0; p < npass; ++p) {
+        int pr_next = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int b = j >> 2, s = j & 3, g = 4 * p + b, slot = j & 1;
+            if (s == 0) stage_load(st[(b + 1) & 1], g + 3);
+            if (j == 4) pr_next = pairs_load(p + 1);
+            const int sn = (j + 1) & 3, bn = ((j + 1) >> 2) & 3, bufn = s == 3 ? buf_next(cur) : cur;
+            decode(slot ^ 1, bn, sn);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+#pragma unroll
+                for (int t = 0; t < PF_T; ++t)
+                    ca[r][t] = mfma_step(av[r], bf[slot][t], j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : ca[r][t]);
+                av[r] = a_read(r, sn, bufn);
+            }
+            interleave_step<NR>();
+            __builtin_amdgcn_sched_barrier(0);
+            if (s == 3) {
+                stage_store(st[b & 1], buf_next(buf_next(cur)));
+                if (j == 15 && (int)threadIdx.x < ROWS) sh.pair[(p + 1) & 1][threadIdx.x] = pr_next;
+                lds_barrier();
+                cur = buf_next(cur);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // This pass's results. sh.pair[p & 1] was written before the barrier that ended the
+        // previous pass (or in the prologue), and is rewritten only after the next pass's barrier.
+        if (working) {
+            const int rows = min(ROWS, cnt - p * ROWS);
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int row = 16 * r + 4 * q + jj;
+                    if (row < rows) {
+                        float *y = ws + (size_t)sh.pair[p & 1][row] * K + nt0 * 16 + n;
+#pragma unroll
+                        for (int t = 0; t < PF_T; ++t)
+                            if (nt0 + t < ntiles) y[16 * t] = ca[r][t][jj] * gs;
+                    }
+                }
+        }
+    }
+}
+
 }  // namespace
 
 bool prefill_offsets_fit(int64_t M, int64_t P, int32_t K, int32_t I)
@@ -393,6 +553,9 @@ int run_w2_prefill(const PlanView &pv, int64_t a_max, int64_t P, const uint16_t 
     const int nblk = (K / 16 + 15) / 16;
     const int64_t G = a_max * nblk;
     const unsigned grid = (unsigned)((G + 7) / 8 * 8);
+    if (I <= KCHUNK)
+        return launch(w2_prefill_s1_kernel<W2S1_R>, dim3(grid), dim3(256), 0, s, pv, reinterpret_cast<const f16 *>(h),
+                      (uint32_t)(P * I * 2), w.codes, w.scales, w.global_scale, K, I, ws, (int)a_max);
     return launch(w2_prefill_kernel, dim3(grid), dim3(256), 0, s, pv, reinterpret_cast<const f16 *>(h),
                   (uint32_t)(P * I * 2), w.codes, w.scales, w.global_scale, K, I, ws, (int)a_max);
 }
