@@ -215,7 +215,8 @@ def plan_fields(plan: torch.Tensor, M: int, topk: int, E: int) -> dict:
     o = 16
     f = {}
     for name, n in (("counts", E), ("offsets", E + 1), ("active", A), ("tile_expert", T), ("tile_row0", T),
-                    ("tile_base", T), ("tile_rows", T), ("tile_pair", T * 16), ("sorted_pair", P), ("pos_of_pair", P)):
+                    ("tile_base", T), ("tile_rows", T), ("tile_pair", T * 16), ("sorted_pair", P), ("pos_of_pair", P),
+                    ("pair_expert", P)):
         f[name] = p[o:o + n]
         o += n
     f["tile_pair"] = f["tile_pair"].reshape(T, 16)

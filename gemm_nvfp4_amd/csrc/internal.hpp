@@ -30,7 +30,7 @@ constexpr int MAX_LINEAR_K = 32768;
 struct PlanLayout {
     int64_t P, A, T, G;
     int64_t hdr, counts, offsets, active, tile_expert, tile_row0, tile_base, tile_rows, tile_pair, sorted_pair,
-        pos_of_pair, hist, badc, tile_first, words;
+        pos_of_pair, pair_expert, hist, badc, tile_first, words;
 };
 
 inline PlanLayout plan_layout(int32_t M, int32_t topk, int32_t E)
@@ -52,6 +52,7 @@ inline PlanLayout plan_layout(int32_t M, int32_t topk, int32_t E)
     L.tile_pair = o;    o += L.T * PLAN_TILE_ROWS;
     L.sorted_pair = o; o += L.P;
     L.pos_of_pair = o; o += L.P;
+    L.pair_expert = o; o += L.P;
     L.hist = o;        o += (int64_t)E * L.G;
     L.badc = o;        o += L.G;
     L.tile_first = o;  o += L.G > 0 ? E : 0;
@@ -62,7 +63,7 @@ inline PlanLayout plan_layout(int32_t M, int32_t topk, int32_t E)
 // Read-only device view of a built plan.
 struct PlanView {
     const int32_t *hdr, *counts, *offsets, *active, *tile_expert, *tile_row0, *tile_base, *tile_rows, *tile_pair,
-        *sorted_pair, *pos_of_pair;
+        *sorted_pair, *pos_of_pair, *pair_expert;
 };
 
 inline PlanView plan_view(const void *plan, const PlanLayout &L)
@@ -70,7 +71,7 @@ inline PlanView plan_view(const void *plan, const PlanLayout &L)
     const int32_t *p = static_cast<const int32_t *>(plan);
     return PlanView{p + L.hdr,       p + L.counts,    p + L.offsets,   p + L.active,
                     p + L.tile_expert, p + L.tile_row0, p + L.tile_base, p + L.tile_rows,
-                    p + L.tile_pair,  p + L.sorted_pair, p + L.pos_of_pair};
+                    p + L.tile_pair,  p + L.sorted_pair, p + L.pos_of_pair, p + L.pair_expert};
 }
 
 // Launch `kernel` through hipLaunchKernel, so a rejected launch is reported as a status instead
@@ -109,6 +110,16 @@ int run_reduce(const PlanView &pv, int32_t M, int32_t topk, int32_t K, const flo
 // bitwise identical either way). The MFMA-tiled prefill kernels pay off once experts average at
 // least 16 pairs, i.e. M*topk >= 16*E; below that the streaming kernels win. They also need every
 // byte offset to fit in 31 bits; larger problems stay on the streaming kernels.
+// Small batches run W2 token-major with the slot reduction fused (one block per token and 16
+// output rows). Each pair then reads its expert's rows itself, so this pays while pairs rarely
+// share an expert. Measured on MI355X at E=512, top-10 (W2 + reduce, µs, token-major vs
+// expert-major): M=2 8.3 vs 14.6, M=8 19.2 vs 22.0, M=12 22.8 vs 26.4, M=16 30.2 vs 28.8; hence
+// P <= E/4.
+#ifndef NVFP4_TOKEN_W2_DIV
+#define NVFP4_TOKEN_W2_DIV 4
+#endif
+inline bool use_token_w2(int64_t P, int32_t E) { return NVFP4_TOKEN_W2_DIV * P <= (int64_t)E; }
+
 inline bool use_prefill(int64_t M, int64_t P, int32_t E, int32_t K, int32_t I)
 {
     return P >= 16 * (int64_t)E && prefill_offsets_fit(M, P, K, I);

@@ -369,6 +369,114 @@ __global__ __launch_bounds__(256) void reduce_kernel(const int32_t *__restrict__
     *reinterpret_cast<f16x4 *>(out + (size_t)t * K + n) = f16x4{(f16)s0, (f16)s1, (f16)s2, (f16)s3};
 }
 
+// ---- W2 + reduction, token-major (small batches) -----------------------------------------------------
+// One block per (token t, 16 output rows n-tile); its four waves take the token's slots k = w,
+// w+4, ... For each valid slot the wave runs the same MFMA chain as w2_stream_kernel on a
+// one-row A (the pair's h row) and that slot's expert rows, so y[p][n] is bitwise the streaming
+// kernel's value. The slot results meet in LDS and one fmaf chain per column, in slot order, gives
+// out[t][n] directly: no FP32 workspace round trip and no second launch. Each pair's expert rows
+// are read once per pair instead of once per expert, which costs little when pairs rarely share
+// an expert (P << E); blocks of one n-tile are numbered consecutively per XCD so that shared rows
+// meet in its L2.
+__global__ __launch_bounds__(256, 3) void w2_token_kernel(PlanView pv, int M, int topk, const f16 *__restrict__ hin,
+                                                          const uint8_t *__restrict__ codes,
+                                                          const uint8_t *__restrict__ scales,
+                                                          const float *__restrict__ gscale, int K, int I,
+                                                          const float *__restrict__ tw, f16 *__restrict__ out)
+{
+    __shared__ float yk[MAX_TOPK][16];
+    __shared__ int s_row[MAX_TOPK], s_e[MAX_TOPK];
+    __shared__ float s_w[MAX_TOPK];
+    __shared__ __attribute__((aligned(16))) f16 s_h[MAX_TOPK][KCHUNK];  // the slots' h rows (one-chunk case)
+    const int ntiles = K >> 4;
+    const int G = M * ntiles;
+    const int per = (G + 7) >> 3;
+    const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);  // XCD-aware numbering
+    if (item >= G) return;
+    const int nt = item / M, t = item - nt * M;
+    if ((int)threadIdx.x < topk) {
+        const int p = t * topk + threadIdx.x;
+        const int j = pv.pos_of_pair[p];
+        s_row[threadIdx.x] = j;
+        s_e[threadIdx.x] = j >= 0 ? pv.pair_expert[p] : -1;
+        s_w[threadIdx.x] = tw[p];
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, q = lane >> 4;
+    const int S = num_chunks(I);
+    const size_t crow = (size_t)I >> 1, srow = (size_t)I >> 4;
+    if (S == 1) {
+        // One chunk (I <= 512). Stage the valid slots' h rows in LDS (16-byte pieces), and load
+        // each wave's packed rows for up to three slots at once, so the latencies overlap.
+        const int pieces = I >> 3;
+        for (int idx = threadIdx.x; idx < topk * pieces; idx += 256) {
+            const int k = idx / pieces, pc = idx - k * pieces;
+            if (s_e[k] >= 0)
+                *reinterpret_cast<u32x4 *>(&s_h[k][8 * pc]) =
+                    *reinterpret_cast<const u32x4 *>(hin + (size_t)s_row[k] * I + 8 * pc);
+        }
+        const int groups = I >> 7;
+        const bool qv = q < groups;
+        const int q_ld = qv ? q : groups - 1;
+        const int ngroups = (topk + 11) / 12;  // block-uniform trip count (the loop holds a barrier)
+        for (int gi = 0; gi < ngroups; ++gi) {
+            const int k0 = wave + 12 * gi;
+            RawChunk w[3];
+#pragma unroll
+            for (int g = 0; g < 3; ++g) {
+                const int k = k0 + 4 * g;
+                const int e = (k < topk && s_e[k] >= 0) ? s_e[k] : 0;  // idle slots read expert 0, unused
+                const size_t wr = (size_t)e * K + nt * 16 + n;
+                w[g] = load_chunk(codes + wr * crow, scales + wr * srow, 0, q_ld);
+            }
+            if (gi == 0) __syncthreads();  // s_h staged; it is not written again
+#pragma unroll
+            for (int g = 0; g < 3; ++g) {
+                const int k = k0 + 4 * g;
+                if (k >= topk || s_e[k] < 0) continue;  // wave-uniform
+                f16x8 af[4][4];
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+                    for (int ss = 0; ss < 4; ++ss) {
+                        const f16x8 v = *reinterpret_cast<const f16x8 *>(&s_h[k][128 * q_ld + 32 * bb + 8 * ss]);
+                        af[bb][ss] = (n == 0 && qv) ? v : zero8();  // row 0 of the tile is the pair
+                    }
+                f32x4 ca[1] = {{0.f, 0.f, 0.f, 0.f}};
+                mma_chunk<1>(reinterpret_cast<const RawChunk(&)[1]>(w[g]), af, qv, ca);
+                if (q == 0) yk[k][n] = ca[0][0] * gscale[s_e[k]];
+            }
+        }
+    } else {
+        for (int k = wave; k < topk; k += 4) {
+            const int e = s_e[k];
+            if (e < 0) continue;  // wave-uniform
+            const size_t wr = (size_t)e * K + nt * 16 + n;
+            const f16 *hr = hin + (size_t)s_row[k] * I;
+            f32x4 tot = {-0.f, -0.f, -0.f, -0.f};  // -0 + x == x: chunk 0 needs no special case
+            for (int c = 0; c < S; ++c) {
+                const int kb = c * KCHUNK;
+                const int groups = min(KCHUNK, I - kb) >> 7;
+                const bool qv = q < groups;
+                const RawChunk w = load_chunk(codes + wr * crow, scales + wr * srow, kb, qv ? q : groups - 1);
+                f16x8 af[4][4];
+                load_a_chunk(af, hr, n == 0 && qv, kb, q);  // the pair's h row in row 0 of the tile
+                f32x4 ca[1] = {{0.f, 0.f, 0.f, 0.f}};
+                mma_chunk<1>(reinterpret_cast<const RawChunk(&)[1]>(w), af, qv, ca);
+                tot += ca[0];
+            }
+            if (q == 0) yk[k][n] = tot[0] * gscale[e];  // row 0 of the tile: lanes 0..15, register 0
+        }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < 16) {
+        float acc = 0.f;
+        for (int k = 0; k < topk; ++k)
+            if (s_e[k] >= 0) acc = fmaf(s_w[k], yk[k][threadIdx.x], acc);
+        out[(size_t)t * K + nt * 16 + threadIdx.x] = (f16)acc;
+    }
+}
+
 int split_for(int k)
 {
     const int s = num_chunks(k);
@@ -412,6 +520,12 @@ int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uin
            const float *topk_weights, uint16_t *out, float *ws, hipStream_t s)
 {
     const int K = w.rows, I = w.k;
+    if (use_token_w2((int64_t)M * topk, w.groups)) {
+        const int64_t G = (int64_t)M * (K / 16);
+        return launch(w2_token_kernel, dim3((unsigned)((G + 7) / 8 * 8)), dim3(256), 0, s, pv, M, topk,
+                      reinterpret_cast<const f16 *>(h), w.codes, w.scales, w.global_scale, K, I, topk_weights,
+                      reinterpret_cast<f16 *>(out));
+    }
     const int split = split_for(I);
     const int ut = (4 / split) * 2 * W2_TP;
     const int upt = (K / 16 + ut - 1) / ut;

@@ -154,12 +154,14 @@ __device__ void build_lists(const int *cnt, int E, int32_t *plan, const PlanLayo
     }
 }
 
-// Records a valid pair's place: sorted_pair, pos_of_pair and its row in its tile's pair list.
-__device__ __forceinline__ void place_pair(int32_t *plan, const PlanLayout &L, int64_t p, int pos, int row_in_expert,
-                                           int first_tile)
+// Records a valid pair's place: sorted_pair, pos_of_pair, its expert and its row in its tile's pair
+// list.
+__device__ __forceinline__ void place_pair(int32_t *plan, const PlanLayout &L, int64_t p, int e, int pos,
+                                           int row_in_expert, int first_tile)
 {
     plan[L.sorted_pair + pos] = (int32_t)p;
     plan[L.pos_of_pair + p] = pos;
+    plan[L.pair_expert + p] = e;
     const int64_t t = first_tile + row_in_expert / PLAN_TILE_ROWS;
     plan[L.tile_pair + t * PLAN_TILE_ROWS + row_in_expert % PLAN_TILE_ROWS] = (int32_t)p;
 }
@@ -211,9 +213,10 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(const int32_t *__restr
             const int o = off[id], n = cnt[id];
             int rank = 0;
             for (int i = 0; i < n; ++i) rank += slot[o + i] < tid;
-            place_pair(plan, L, tid, o + rank, rank, first[id]);
+            place_pair(plan, L, tid, id, o + rank, rank, first[id]);
         } else {
             plan[L.pos_of_pair + tid] = -1;
+            plan[L.pair_expert + tid] = -1;
         }
     }
     if (tid == 0) write_header_tail(plan, L, bad, M, topk, E);
@@ -294,11 +297,12 @@ __global__ __launch_bounds__(PLAN_CHUNK) void plan_scatter_kernel(const int32_t 
     if (p >= L.P) return;
     if (id < 0) {
         plan[L.pos_of_pair + p] = -1;
+        plan[L.pair_expert + p] = -1;
         return;
     }
     const int rank = stable_rank(reinterpret_cast<const int4 *>(id_s), tid, id);
     const int before = plan[L.hist + (int64_t)id * L.G + g] + rank;  // earlier pairs of expert id
-    place_pair(plan, L, p, plan[L.offsets + id] + before, before, plan[L.tile_first + id]);
+    place_pair(plan, L, p, id, plan[L.offsets + id] + before, before, plan[L.tile_first + id]);
 }
 
 }  // namespace

@@ -87,10 +87,11 @@ const char *nvfp4_status_str(int status);
  *   [0] n_valid  [1] n_active  [2] n_bad  [3] n_tiles  [4] M  [5] topk  [6] E  [7] 16 (tile rows)
  *   [8..15] reserved
  *   counts[E]  offsets[E+1]  active[A]  tile_expert[T]  tile_row0[T]  tile_base[T]  tile_rows[T]
- *   tile_pair[T][16]  sorted_pair[P]  pos_of_pair[P]
+ *   tile_pair[T][16]  sorted_pair[P]  pos_of_pair[P]  pair_expert[P]
  *   followed by internal scratch when P > 1024.
  * Within each array only the first n_valid / n_active / n_tiles entries are defined. pos_of_pair[p]
- * is the bucket-order row of pair p, or -1 if the pair was skipped. Active experts are in
+ * is the bucket-order row of pair p, or -1 if the pair was skipped; pair_expert[p] is its expert,
+ * or -1. Active experts are in
  * ascending id order, and row tiles of 16 rows are in (expert, row0) order. Row tile t covers
  * bucket rows tile_base[t] = offsets[e] + tile_row0[t] .. + tile_rows[t] - 1 of its expert e;
  * tile_pair[t][r] is the pair of its row r (undefined for r >= tile_rows[t]). These are redundant with

@@ -122,3 +122,25 @@ def test_moe_all_slots_invalid_gives_zero():
     res = run_moe(case, 0)
     o = half_bits(res["out"])
     assert np.all(o == 0)
+
+
+@pytest.mark.parametrize("i", [384, 640])
+def test_moe_token_major_and_expert_major_w2_agree(orc, i):
+    """W2 + reduce runs token-major with the reduction fused when pairs rarely share an expert
+    (P <= E/4), expert-major with an FP32 workspace otherwise. A 5-token batch (P = 70 > 16) takes
+    the second path, each token alone (P = 14) the first: the outputs must match bitwise, and the
+    batch must match the oracle. topk = 14 leaves the four waves uneven slot counts; I = 384 is a
+    short single chunk, I = 640 needs two chunks."""
+    sh = S.MoEShape(m=5, e=64, topk=14, k=256, i=i)
+    case = S.moe_case(sh, routing="repeat_invalid", workload="stress", route_pattern=31 + i)
+    res = run_moe(case, 0)
+    _check_against_oracle(orc, case, 0, res, f"w2 paths i={i}")
+    d = res["dev"]
+    for t in range(sh.m):
+        one = dict(case)
+        one["shape"] = S.MoEShape(m=1, e=sh.e, topk=sh.topk, k=sh.k, i=sh.i)
+        one["x"], one["ids"], one["topk_weights"] = case["x"][t:t + 1], case["ids"][t:t + 1], case["topk_weights"][t:t + 1]
+        dd = {"x": d["x"][t:t + 1].contiguous(), "ids": d["ids"][t:t + 1].contiguous(),
+              "tw": d["tw"][t:t + 1].contiguous(), "w13": d["w13"], "w2": d["w2"]}
+        single = run_moe(one, 0, dev=dd)["out"][0]
+        assert torch.equal(single.view(torch.int16), res["out"][t].view(torch.int16)), f"token {t}"

@@ -49,6 +49,9 @@ def test_plan_bit_exact(orc, M, topk, E, kind):
         assert np.array_equal(got[key], ref[key]), key
     assert list(got["hdr"][4:8]) == [M, topk, E, 16]
     _check_tile_descriptors(got, ref)
+    # pair_expert: the routed id of every placed pair, -1 for skipped ones
+    want = np.where(ref["pos_of_pair"] >= 0, ids.reshape(-1), -1)
+    assert np.array_equal(got["pair_expert"], want)
 
 
 def _check_tile_descriptors(got, ref):
