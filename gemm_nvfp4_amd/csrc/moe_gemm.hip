@@ -88,8 +88,12 @@ __device__ __forceinline__ void stage_tiles(const PlanView &pv, TileStage &st, i
 #define NVFP4_W13_OCC 2
 #endif
 #ifndef NVFP4_W2_OCC
-#define NVFP4_W2_OCC 3
+#define NVFP4_W2_OCC 1
 #endif
+#ifndef NVFP4_W2T_OCC
+#define NVFP4_W2T_OCC 3
+#endif
+constexpr int W2T_OCC = NVFP4_W2T_OCC;
 constexpr int W13_TP = NVFP4_W13_TP;
 constexpr int W2_TP = NVFP4_W2_TP;
 constexpr int W13_OCC = NVFP4_W13_OCC;
@@ -378,7 +382,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(const int32_t *__restrict__
 // are read once per pair instead of once per expert, which costs little when pairs rarely share
 // an expert (P << E); blocks of one n-tile are numbered consecutively per XCD so that shared rows
 // meet in its L2.
-__global__ __launch_bounds__(256, 3) void w2_token_kernel(PlanView pv, int M, int topk, const f16 *__restrict__ hin,
+__global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int M, int topk, const f16 *__restrict__ hin,
                                                           const uint8_t *__restrict__ codes,
                                                           const uint8_t *__restrict__ scales,
                                                           const float *__restrict__ gscale, int K, int I,
