@@ -130,10 +130,14 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// SiLU(g) * u in FP32, as fixed for every regime: g / (1 + e^-g) * u.
+// SiLU(g) * u in FP32, the same in every regime: g * (1 / (1 + e^-g)) * u. e^-g is taken as
+// 2^(-g * log2 e) by the hardware base-2 exponential (v_exp_f32) and the reciprocal by v_rcp_f32,
+// each within about one FP32 ulp, far below the fp16 rounding of h. Overflow behaves as in the
+// plain formula: e^-g = inf gives a signed zero, and g = -inf gives NaN.
 __device__ __forceinline__ float swiglu(float g, float u)
 {
-    return g / (1.0f + expf(-g)) * u;
+    const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 }  // namespace nvfp4
