@@ -357,16 +357,30 @@ __global__ __launch_bounds__(256) void reduce_kernel(const int32_t *__restrict__
     const int n = (nb * 256 + threadIdx.x) * 4;
     if (n >= K) return;
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-    for (int k = 0; k < topk; ++k) {
-        const size_t p = (size_t)t * topk + k;
-        const bool valid = pos_of_pair[p] >= 0;
-        const float w = tw[p];
-        const float4 y = *reinterpret_cast<const float4 *>(ws + p * K + n);
-        if (valid) {
-            s0 = fmaf(w, y.x, s0);
-            s1 = fmaf(w, y.y, s1);
-            s2 = fmaf(w, y.z, s2);
-            s3 = fmaf(w, y.w, s3);
+    // Slots go in batches of 16: a batch's rows are all loaded before the first fmaf, so their
+    // latencies overlap, then folded in slot order.
+    constexpr int BATCH = 16;
+    for (int k0 = 0; k0 < topk; k0 += BATCH) {
+        float4 y[BATCH];
+        float wk[BATCH];
+        int pos[BATCH];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i)
+            if (k0 + i < topk) {
+                const size_t p = (size_t)t * topk + k0 + i;
+                y[i] = *reinterpret_cast<const float4 *>(ws + p * K + n);
+                pos[i] = pos_of_pair[p];
+                wk[i] = tw[p];
+            }
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+            if (k0 + i < topk && pos[i] >= 0) {
+                const float w = wk[i];
+                s0 = fmaf(w, y[i].x, s0);
+                s1 = fmaf(w, y[i].y, s1);
+                s2 = fmaf(w, y[i].z, s2);
+                s3 = fmaf(w, y[i].w, s3);
+            }
         }
     }
     typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
