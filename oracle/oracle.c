@@ -198,6 +198,49 @@ void orc_plan(const int32_t *ids, int64_t M, int64_t topk, int64_t E, int64_t BM
     summary[3] = nt;
 }
 
+/* ---- router ------------------------------------------------------------------------------
+ * Top-k routing from router logits, the "router" step the no-MTP page lists among the fused MoE
+ * parts ("Scope and related PRs"). The pages print no formula; the plainest reading is used:
+ *   - token t takes the experts of its topk largest logits, largest first;
+ *   - equal logits (+0 and -0 are equal) go in ascending expert order;
+ *   - a NaN logit ranks below every number (NaNs among themselves by expert order);
+ *   - the slot weights are the softmax of the selected logits,
+ *       w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0),  l_0 the first (largest) selected logit,
+ *     which equals the full softmax over all experts renormalised over the selection.
+ * The selection keeps a sorted list of at most topk experts and inserts each expert in turn; the
+ * weights are computed in double from the fp32 logits. */
+static int route_before(float a, int32_t ia, float b, int32_t ib)
+{
+    int an = isnan(a), bn = isnan(b);
+    if (an || bn) return (an && bn) ? ia < ib : bn;
+    if (a != b) return a > b;
+    return ia < ib;
+}
+
+void orc_route(const float *logits, int64_t M, int64_t E, int64_t topk, int32_t *ids, double *w)
+{
+    for (int64_t t = 0; t < M; ++t) {
+        const float *x = logits + t * E;
+        int32_t *sel = ids + t * topk;
+        int64_t n = 0;
+        for (int32_t e = 0; e < E; ++e) {
+            if (n == topk && !route_before(x[e], e, x[sel[n - 1]], sel[n - 1])) continue;
+            int64_t j = n < topk ? n++ : topk - 1;
+            while (j > 0 && route_before(x[e], e, x[sel[j - 1]], sel[j - 1])) {
+                sel[j] = sel[j - 1];
+                --j;
+            }
+            sel[j] = e;
+        }
+        double *wt = w + t * topk, l0 = (double)x[sel[0]], s = 0.0;
+        for (int64_t k = 0; k < topk; ++k) {
+            wt[k] = exp((double)x[sel[k]] - l0);
+            s += wt[k];
+        }
+        for (int64_t k = 0; k < topk; ++k) wt[k] /= s;
+    }
+}
+
 /* ---- grouped MoE ------------------------------------------------------------------------- */
 
 typedef struct {

@@ -51,6 +51,8 @@ def lib():
         L.orc_moe_grouped.restype = None
         L.orc_moe_grouped.argtypes = ([_vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i32,
                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int])
+        L.orc_route.restype = None
+        L.orc_route.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp]
         L.orc_w2_reduce.restype = None
         L.orc_w2_reduce.argtypes = ([_vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp,
                                      _vp, _vp, _vp, _vp, C.c_int])
@@ -189,3 +191,14 @@ def w2_reduce(h16: np.ndarray, case: dict, pl: dict, nthreads=None) -> np.ndarra
     lib().orc_w2_reduce(_p(hb), _p(tw), sh.m, sh.topk, sh.e, sh.k, sh.i, _p(c2), _p(s2), _p(g2),
                         _p(pl["offsets"]), _p(sp), _p(pl["pos_of_pair"]), _p(out), _threads(nthreads))
     return out
+
+
+def route(logits: np.ndarray, topk: int):
+    """Top-k routing of fp32 logits [M, E] (oracle.c: orc_route). Returns (ids int32 [M, topk],
+    weights float64 [M, topk])."""
+    x = np.ascontiguousarray(logits, dtype=np.float32)
+    M, E = x.shape
+    ids = np.zeros((M, topk), dtype=np.int32)
+    w = np.zeros((M, topk), dtype=np.float64)
+    lib().orc_route(_p(x), M, E, topk, _p(ids), _p(w))
+    return ids, w

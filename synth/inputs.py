@@ -42,6 +42,7 @@ __all__ = [
     "dense_case",
     "device_nvfp4_weights",
     "active_experts",
+    "router_logits",
 ]
 
 # E4M3FN bytes of 2^u for integer u in [-8, -4]: 2^-8 and 2^-7 are E4M3 subnormals (0x02, 0x04),
@@ -153,7 +154,7 @@ PREFILL = MoEShape(m=8192, e=512, topk=10, k=2048, i=512)
 DENSE_N, DENSE_K = 4352, 5120
 DENSE_MS = (1, 2, 4, 8, 16, 32)
 
-WORKLOAD_IDS = {"tiny": 0, "dense": 1, "decode": 2, "stress": 3, "prefill": 4}
+WORKLOAD_IDS = {"tiny": 0, "dense": 1, "decode": 2, "stress": 3, "prefill": 4, "route": 5}
 
 
 def moe_case(shape: MoEShape, routing: str = "uniform", weight_set: int = 0, route_pattern: int = 0,
@@ -202,3 +203,27 @@ def active_experts(ids: np.ndarray, e: int) -> int:
     """Number of distinct valid expert ids in a routing (the experts whose weights a grouped layer reads)."""
     v = ids[(ids >= 0) & (ids < e)]
     return int(np.unique(v).size)
+
+
+def router_logits(rng: np.random.Generator, m: int, e: int, kind: str = "normal") -> np.ndarray:
+    """Router logits float32 [m, e].
+      normal   N(0,1)
+      ties     integers in [-2, 2], each zero given a random sign (many equal values, +0 and -0)
+      special  N(0,1) with about 2% NaN, 2% +inf, 2% -inf and 2% signed zeros per row"""
+    if kind == "normal":
+        return rng.standard_normal((m, e)).astype(np.float32)
+    if kind == "ties":
+        x = rng.integers(-2, 3, size=(m, e)).astype(np.float32)
+        neg = rng.random((m, e)) < 0.5
+        x[(x == 0) & neg] = np.float32(-0.0)
+        return x
+    if kind == "special":
+        x = rng.standard_normal((m, e)).astype(np.float32)
+        u = rng.random((m, e))
+        x[u < 0.02] = np.nan
+        x[(u >= 0.02) & (u < 0.04)] = np.inf
+        x[(u >= 0.04) & (u < 0.06)] = -np.inf
+        x[(u >= 0.06) & (u < 0.07)] = np.float32(0.0)
+        x[(u >= 0.07) & (u < 0.08)] = np.float32(-0.0)
+        return x
+    raise ValueError(kind)
