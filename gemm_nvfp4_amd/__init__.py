@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     nvfp4_linear,
     nvfp4_moe_plan,
     nvfp4_moe_plan_bytes,
+    nvfp4_moe_route,
     nvfp4_moe_w13_swiglu,
     nvfp4_moe_w2_reduce,
     nvfp4_moe_w2_workspace_bytes,

@@ -39,6 +39,7 @@ _SIGS = {
     "nvfp4_status_str": (C.c_char_p, [C.c_int]),
     "nvfp4_moe_plan_bytes": (_sz, [_i32, _i32, _i32]),
     "nvfp4_moe_plan": (C.c_int, [_vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "nvfp4_moe_route": (C.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_moe_w13_swiglu": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _i32, _vp, _vp]),
     "nvfp4_moe_w2_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "nvfp4_moe_w2_reduce": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _vp, _vp, _vp, _sz, _vp]),
@@ -136,6 +137,24 @@ def nvfp4_moe_plan(topk_ids: torch.Tensor, E: int, plan: torch.Tensor | None = N
     _check("nvfp4_moe_plan", lib().nvfp4_moe_plan(_dev(topk_ids, "topk_ids", torch.int32), M, topk, E,
                                                   _dev(plan, "plan", torch.int32), plan.numel() * 4, _stream(stream)))
     return plan
+
+
+def nvfp4_moe_route(logits: torch.Tensor, topk: int, ids: torch.Tensor | None = None,
+                    weights: torch.Tensor | None = None, plan: torch.Tensor | None = None, stream=None):
+    """Top-k routing of fp32 logits [M, E] fused with the plan. Returns (ids int32 [M, topk],
+    weights fp32 [M, topk], plan)."""
+    M, E = logits.shape
+    dev = logits.device
+    if ids is None:
+        ids = torch.empty((M, topk), dtype=torch.int32, device=dev)
+    if weights is None:
+        weights = torch.empty((M, topk), dtype=torch.float32, device=dev)
+    if plan is None:
+        plan = torch.empty(max(nvfp4_moe_plan_bytes(M, topk, E), 4) // 4, dtype=torch.int32, device=dev)
+    _check("nvfp4_moe_route", lib().nvfp4_moe_route(
+        _dev(logits, "logits", torch.float32), M, E, topk, _dev(ids, "ids", torch.int32),
+        _dev(weights, "weights", torch.float32), _dev(plan, "plan", torch.int32), plan.numel() * 4, _stream(stream)))
+    return ids, weights, plan
 
 
 def nvfp4_moe_w13_swiglu(plan: torch.Tensor, M: int, topk: int, E: int, x: torch.Tensor, w13: NVFP4Tensor,

@@ -64,6 +64,21 @@ NVFP4_API int nvfp4_moe_plan(const int32_t *topk_ids, int32_t M, int32_t topk, i
     return nvfp4::run_plan(topk_ids, M, topk, E, static_cast<int32_t *>(plan), L, static_cast<hipStream_t>(stream));
 }
 
+NVFP4_API int nvfp4_moe_route(const float *logits, int32_t M, int32_t E, int32_t topk, int32_t *topk_ids,
+                              float *topk_weights, void *plan, size_t plan_bytes, void *stream)
+{
+    if (!plan_shape_ok(M, topk, E) || topk > E) return NVFP4_ERR_SHAPE;
+    if (E > nvfp4::MAX_EXPERTS) return NVFP4_ERR_UNSUPPORTED;
+    if (M == 0) return NVFP4_OK;
+    if (!logits || !topk_ids || !topk_weights || !plan) return NVFP4_ERR_NULL;
+    if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) || !aligned(plan, 16))
+        return NVFP4_ERR_ALIGN;
+    const PlanLayout L = nvfp4::plan_layout(M, topk, E);
+    if (plan_bytes < (size_t)L.words * sizeof(int32_t)) return NVFP4_ERR_WORKSPACE;
+    return nvfp4::run_route(logits, M, E, topk, topk_ids, topk_weights, static_cast<int32_t *>(plan), L,
+                            static_cast<hipStream_t>(stream));
+}
+
 NVFP4_API int nvfp4_moe_w13_swiglu(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16_t *x,
                                    const nvfp4_weights *w13, int32_t layout, uint16_t *h, void *stream)
 {

@@ -92,6 +92,8 @@ inline int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
 // Kernel launchers, one per translation unit. Arguments are validated by the caller (abi.hip).
 int run_plan(const int32_t *ids, int32_t M, int32_t topk, int32_t E, int32_t *plan, const PlanLayout &L,
              hipStream_t s);
+int run_route(const float *logits, int32_t M, int32_t E, int32_t topk, int32_t *ids, float *weights, int32_t *plan,
+              const PlanLayout &L, hipStream_t s);
 int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, const nvfp4_weights &w,
             int32_t layout, uint16_t *h, hipStream_t s);
 int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uint16_t *h, const nvfp4_weights &w,

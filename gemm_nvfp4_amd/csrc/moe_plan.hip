@@ -14,6 +14,9 @@
 //     A per-expert scan over chunks gives every (expert, chunk) its start. Within a chunk a
 //     pair's rank counts the earlier pairs of the same expert, so the scatter is stable with no
 //     atomics on positions. Four launches, none of which is serial over the pairs.
+//
+// The router (top-k selection and softmax weights from router logits) runs one wave per token. At
+// decode sizes it shares the small path's block, so routing and planning are one launch.
 #include "internal.hpp"
 
 namespace nvfp4 {
@@ -177,8 +180,8 @@ __device__ __forceinline__ void write_header_tail(int32_t *plan, const PlanLayou
 }
 
 // ---- small path: P <= 1024, one block -----------------------------------------------------------
-__global__ __launch_bounds__(1024) void plan_small_kernel(const int32_t *__restrict__ ids, int M, int topk, int E,
-                                                          int32_t *__restrict__ plan, PlanLayout L)
+// The whole plan from one 1024-thread block; thread p holds pair p's raw id (-1 past P).
+__device__ void plan_small_body(int raw, int M, int topk, int E, int32_t *__restrict__ plan, const PlanLayout &L)
 {
     __shared__ int cnt[MAX_EXPERTS];
     __shared__ int off[MAX_EXPERTS + 1];
@@ -188,7 +191,6 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(const int32_t *__restr
     __shared__ int bad;
     const int tid = threadIdx.x;
     const int P = (int)L.P;
-    const int raw = tid < P ? ids[tid] : -1;  // issued first: the only load of the kernel
     for (int e = tid; e < E; e += 1024) cnt[e] = 0;
     if (tid == 0) bad = 0;
     __syncthreads();
@@ -220,6 +222,114 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(const int32_t *__restr
         }
     }
     if (tid == 0) write_header_tail(plan, L, bad, M, topk, E);
+}
+
+__global__ __launch_bounds__(1024) void plan_small_kernel(const int32_t *__restrict__ ids, int M, int topk, int E,
+                                                          int32_t *__restrict__ plan, PlanLayout L)
+{
+    const int raw = (int)threadIdx.x < L.P ? ids[threadIdx.x] : -1;  // issued first: the only load of the kernel
+    plan_small_body(raw, M, topk, E, plan, L);
+}
+
+// ---- router ---------------------------------------------------------------------------------------
+// Top-k routing from FP32 router logits (the "router" that the "[Kernel][SM70] Improve Qwen3.8
+// no-MTP concurrency" page lists among the fused MoE parts, "Scope and related PRs"; the pages give
+// no formula, and this is the plain reading): a token takes the experts of its topk largest
+// logits, largest first; equal logits (+0 and -0 are equal) go in ascending expert order; NaN
+// ranks below every number. The slot weights are the softmax of the selected logits,
+// exp(l_k - l_0) / sum_j exp(l_j - l_0) in FP32, l_0 the largest selected logit.
+//
+// One wave per token. Each logit becomes a unique 64-bit key: an order-preserving 32-bit image of
+// the value (NaN lowest) above the complemented expert id, so equal values put the lower expert
+// higher. Round r takes the wave's largest key below round r-1's winner: nothing is ever removed
+// and every round is one pass over the lane's registers plus a six-step butterfly.
+__device__ __forceinline__ uint64_t route_key(float x, int e)
+{
+    const uint32_t b = __float_as_uint(x == 0.0f ? 0.0f : x);  // -0 and +0 get one image
+    uint32_t k = (b & 0x80000000u) ? ~b : (b | 0x80000000u);   // ascending with the value
+    if (x != x) k = 0;                                          // NaN below -inf
+    return ((uint64_t)k << 32) | (uint64_t)(~(uint32_t)e);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t y = __shfl_xor(v, o, 64);
+        v = y > v ? y : v;
+    }
+    return v;
+}
+
+// Routes token row `lg` (E <= 64*NPL logits, 1 <= topk <= min(E, 32)). Lane k < topk ends with
+// the expert and weight of slot k.
+template <int NPL>
+__device__ __forceinline__ void route_token(const float *__restrict__ lg, int E, int topk, int &id, float &w)
+{
+    const int lane = threadIdx.x & 63;
+    uint64_t c[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int e = lane + 64 * i;
+        c[i] = e < E ? route_key(lg[e], e) : 0;  // 0 is below every real key
+    }
+    uint64_t thr = ~0ull;
+    id = -1;
+    for (int r = 0; r < topk; ++r) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) best = (c[i] < thr && c[i] > best) ? c[i] : best;
+        thr = wave_max_u64(best);
+        if (lane == r) id = (int)~(uint32_t)thr;
+    }
+    const float x = lane < topk ? lg[id] : 0.0f;
+    const float l0 = __shfl(x, 0, 64);
+    const float ev = lane < topk ? expf(x - l0) : 0.0f;
+    float sum = ev;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+    sum = __shfl(sum, 0, 64);  // lane 0's sum for every slot, so all slots divide by one value
+    w = ev / sum;
+}
+
+// Many tokens: one wave per token, four per block.
+template <int NPL>
+__global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ logits, int M, int E, int topk,
+                                                    int32_t *__restrict__ ids, float *__restrict__ weights)
+{
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (t >= M) return;  // wave-uniform
+    int id;
+    float w;
+    route_token<NPL>(logits + (size_t)t * E, E, topk, id, w);
+    if (lane < topk) {
+        ids[(size_t)t * topk + lane] = id;
+        weights[(size_t)t * topk + lane] = w;
+    }
+}
+
+// Decode sizes (M*topk <= 1024, E <= 1024): the sixteen waves route the tokens, the ids meet in
+// LDS, and the same block builds the plan.
+template <int NPL>
+__global__ __launch_bounds__(1024) void route_plan_small_kernel(const float *__restrict__ logits, int M, int E,
+                                                                int topk, int32_t *__restrict__ ids,
+                                                                float *__restrict__ weights,
+                                                                int32_t *__restrict__ plan, PlanLayout L)
+{
+    __shared__ int s_ids[SMALL_PLAN_PAIRS];
+    const int lane = threadIdx.x & 63;
+    for (int t = threadIdx.x >> 6; t < M; t += 16) {  // wave-uniform loop
+        int id;
+        float w;
+        route_token<NPL>(logits + (size_t)t * E, E, topk, id, w);
+        if (lane < topk) {
+            ids[t * topk + lane] = id;
+            weights[t * topk + lane] = w;
+            s_ids[t * topk + lane] = id;
+        }
+    }
+    __syncthreads();
+    plan_small_body((int)threadIdx.x < L.P ? s_ids[threadIdx.x] : -1, M, topk, E, plan, L);
 }
 
 // ---- large path ---------------------------------------------------------------------------------
@@ -305,7 +415,41 @@ __global__ __launch_bounds__(PLAN_CHUNK) void plan_scatter_kernel(const int32_t 
     place_pair(plan, L, p, id, plan[L.offsets + id] + before, before, plan[L.tile_first + id]);
 }
 
+int route_npl(int E)
+{
+    int npl = 1;
+    while (64 * npl < E) npl *= 2;
+    return npl;
+}
+
 }  // namespace
+
+int run_route(const float *logits, int32_t M, int32_t E, int32_t topk, int32_t *ids, float *weights, int32_t *plan,
+              const PlanLayout &L, hipStream_t s)
+{
+    const int npl = route_npl(E);
+    if (L.P <= SMALL_PLAN_PAIRS && npl <= 16) {  // the block's 128 registers per lane hold 16 keys per lane
+#define NVFP4_ROUTE_SMALL(N) \
+    case N: return launch(route_plan_small_kernel<N>, dim3(1), dim3(1024), 0, s, logits, M, E, topk, ids, weights, plan, L);
+        switch (npl) {
+            NVFP4_ROUTE_SMALL(1) NVFP4_ROUTE_SMALL(2) NVFP4_ROUTE_SMALL(4) NVFP4_ROUTE_SMALL(8)
+            NVFP4_ROUTE_SMALL(16)
+        default: return NVFP4_ERR_UNSUPPORTED;
+        }
+#undef NVFP4_ROUTE_SMALL
+    }
+    const dim3 grid((unsigned)(((int64_t)M + 3) / 4)), block(256);
+    int st;
+#define NVFP4_ROUTE(N) \
+    case N: st = launch(route_kernel<N>, grid, block, 0, s, logits, M, E, topk, ids, weights); break;
+    switch (npl) {
+        NVFP4_ROUTE(1) NVFP4_ROUTE(2) NVFP4_ROUTE(4) NVFP4_ROUTE(8) NVFP4_ROUTE(16) NVFP4_ROUTE(32) NVFP4_ROUTE(64)
+    default: return NVFP4_ERR_UNSUPPORTED;
+    }
+#undef NVFP4_ROUTE
+    if (st != NVFP4_OK) return st;
+    return run_plan(ids, M, topk, E, plan, L, s);
+}
 
 int run_plan(const int32_t *ids, int32_t M, int32_t topk, int32_t E, int32_t *plan, const PlanLayout &L, hipStream_t s)
 {

@@ -105,6 +105,24 @@ int nvfp4_moe_plan(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E,
                    void *plan, size_t plan_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Router fused with the plan (the "router" among the fused MoE parts, no-MTP page, "Scope and
+ * related PRs"; the pages print no formula, so this is the plain reading).
+ *   logits        fp32 [M][E]      router logits
+ *   topk_ids      int32 [M][topk]  output: token t's experts, slot k = its k-th largest logit
+ *   topk_weights  fp32 [M][topk]   output: softmax of the selected logits,
+ *                                  w[t][k] = exp(l_k - l_0) / sum_j exp(l_j - l_0), FP32
+ *   plan          as for nvfp4_moe_plan; the result is the plan of the ids written here
+ * Selection order: larger logit first; equal logits (+0 and -0 are equal) in ascending expert id;
+ * a NaN logit ranks below every number. The ids are exact (comparisons only). Non-finite selected
+ * logits make the weights NaN by IEEE rules (for example l_0 = +inf gives inf - inf).
+ * Requirements: 1 <= topk <= min(E, 32), E <= 4096, M*topk <= 2^26; logits, ids, weights 4-byte
+ * aligned, plan 16-byte aligned. With M*topk <= 1024 and E <= 1024 routing and planning are one
+ * launch.
+ * --------------------------------------------------------------------------------------------- */
+int nvfp4_moe_route(const float *logits, int32_t M, int32_t E, int32_t topk, int32_t *topk_ids,
+                    float *topk_weights, void *plan, size_t plan_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Grouped W13 with fused SwiGLU (the "expert-grouped multi-row W13/SiLU", no-MTP page, "Scope and
  * related PRs").
  *   x    fp16 [M][K]          activations (K = w13->k)

@@ -1,0 +1,82 @@
+"""The C ABI on the host (no GPU needed): the built library loads, exports every function that
+include/nvfp4moe.h declares, and its host-side logic (version, status names, buffer sizes and the
+argument checks that fail closed before anything is enqueued) behaves as the header states.
+
+None of these calls reaches the HIP runtime: each returns before a launch.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4moe.h")
+LIB = os.path.join(ROOT, "gemm_nvfp4_amd", "libnvfp4moe.so")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} is not built (python gemm_nvfp4_amd/build.py)")
+    from gemm_nvfp4_amd import _lib
+    return _lib.lib()
+
+
+def declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(nvfp4_\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared() == sorted([
+        "nvfp4_abi_version", "nvfp4_status_str", "nvfp4_moe_plan_bytes", "nvfp4_moe_plan", "nvfp4_moe_route",
+        "nvfp4_moe_w13_swiglu", "nvfp4_moe_w2_workspace_bytes", "nvfp4_moe_w2_reduce", "nvfp4_linear"])
+
+
+def test_library_exports_every_declared_function():
+    raw = C.CDLL(LIB)
+    for name in declared():
+        assert hasattr(raw, name), name
+
+
+def test_version_and_status_names(L):
+    assert L.nvfp4_abi_version() == 1
+    names = [L.nvfp4_status_str(k).decode() for k in range(7)]
+    assert names == ["NVFP4_OK", "NVFP4_ERR_NULL", "NVFP4_ERR_SHAPE", "NVFP4_ERR_ALIGN", "NVFP4_ERR_WORKSPACE",
+                     "NVFP4_ERR_UNSUPPORTED", "NVFP4_ERR_LAUNCH"]
+    assert L.nvfp4_status_str(99) == b"NVFP4_ERR_UNKNOWN"
+
+
+def test_buffer_sizes(L):
+    assert L.nvfp4_moe_plan_bytes(16, 10, 512) % 256 == 0 and L.nvfp4_moe_plan_bytes(16, 10, 512) > 0
+    assert L.nvfp4_moe_plan_bytes(16, 33, 512) == 0  # topk > 32
+    assert L.nvfp4_moe_plan_bytes(-1, 10, 512) == 0
+    assert L.nvfp4_moe_w2_workspace_bytes(16, 10, 2048) == 16 * 10 * 2048 * 4
+    assert L.nvfp4_moe_w2_workspace_bytes(3, 1, 80) == 1024  # 960 bytes, rounded up to 256
+
+
+def test_argument_checks_fail_closed(L):
+    null = None
+    fake = C.c_void_p(0x1000)   # never dereferenced: every call below returns before any launch
+    odd = C.c_void_p(0x1001)
+    # plan
+    assert L.nvfp4_moe_plan(null, -1, 10, 512, null, 0, null) == 2      # ERR_SHAPE
+    assert L.nvfp4_moe_plan(null, 4, 10, 8192, null, 0, null) == 5      # E > 4096: ERR_UNSUPPORTED
+    assert L.nvfp4_moe_plan(null, 0, 10, 512, null, 0, null) == 0       # M = 0 is a no-op
+    assert L.nvfp4_moe_plan(null, 4, 10, 512, fake, 1 << 20, null) == 1  # ERR_NULL
+    assert L.nvfp4_moe_plan(odd, 4, 10, 512, fake, 1 << 20, null) == 3   # ERR_ALIGN
+    assert L.nvfp4_moe_plan(fake, 4, 10, 512, fake, 16, null) == 4       # ERR_WORKSPACE
+    # router
+    assert L.nvfp4_moe_route(fake, 4, 8, 9, fake, fake, fake, 1 << 20, null) == 2   # topk > E
+    assert L.nvfp4_moe_route(fake, 0, 8, 2, null, null, null, 0, null) == 0        # M = 0
+    assert L.nvfp4_moe_route(fake, 4, 8, 2, null, fake, fake, 1 << 20, null) == 1  # ERR_NULL
+    assert L.nvfp4_moe_route(odd, 4, 8, 2, fake, fake, fake, 1 << 20, null) == 3   # ERR_ALIGN
+    assert L.nvfp4_moe_route(fake, 4, 8, 2, fake, fake, fake, 16, null) == 4       # ERR_WORKSPACE
+    # linear: K % 128 != 0 is unsupported, M < 0 a shape error
+    from gemm_nvfp4_amd._lib import nvfp4_weights
+    w = nvfp4_weights(fake, fake, fake, 1, 64, 96)
+    assert L.nvfp4_linear(fake, 4, C.byref(w), fake, null) == 5
+    assert L.nvfp4_linear(fake, -1, C.byref(w), fake, null) == 2
+    w = nvfp4_weights(None, fake, fake, 1, 64, 128)
+    assert L.nvfp4_linear(fake, 4, C.byref(w), fake, null) == 1
