@@ -60,6 +60,7 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--no-route", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--traffic", action="store_true",
@@ -254,6 +255,28 @@ def dense_timing(copies=64, launches=256):
     return res
 
 
+def route_timing(launches=256, patterns=8):
+    """Router fused with the plan (fp32 logits -> ids, weights, plan) against the plan alone from
+    ids, µs per call in graphs of `launches` calls, at 1, 16 and 8192 tokens (512 experts, top-10)."""
+    import torch
+    import gemm_nvfp4_amd as G
+    from synth import inputs as S
+    res = []
+    for M in (1, 16, 8192):
+        xs = [torch.from_numpy(S.router_logits(S.rng_for(S.WORKLOAD_IDS["route"], 20, 100 * M + p), M, E)).cuda()
+              for p in range(patterns)]
+        ids = torch.empty((M, TOPK), dtype=torch.int32, device="cuda")
+        w = torch.empty((M, TOPK), dtype=torch.float32, device="cuda")
+        plan = torch.empty(G.nvfp4_moe_plan_bytes(M, TOPK, E) // 4, dtype=torch.int32, device="cuda")
+        n = launches if M <= 16 else 16
+        route_ms = time_graph(lambda: [G.nvfp4_moe_route(xs[i % patterns], TOPK, ids=ids, weights=w, plan=plan)
+                                       for i in range(n)], n)
+        id_sets = [G.nvfp4_moe_route(x, TOPK)[0] for x in xs]
+        plan_ms = time_graph(lambda: [G.nvfp4_moe_plan(id_sets[i % patterns], E, plan=plan) for i in range(n)], n)
+        res.append({"M": M, "route_plan_us": round(route_ms * 1e3 / n, 3), "plan_us": round(plan_ms * 1e3 / n, 3)})
+    return res
+
+
 def cpu_baseline(W13, W2, seconds):
     """The fp64 oracle (grouped form) on the headline workload's route patterns, on the host's
     cores, for about `seconds` of CPU work; reported in the same unit (weight GB/s)."""
@@ -323,6 +346,10 @@ def main():
     if not args.no_dense:
         dense = dense_timing()
         log(f"dense: {dense}")
+    route = None
+    if not args.no_route:
+        route = route_timing()
+        log(f"route: {route}")
     cpu = None if args.no_cpu else cpu_baseline(W13, W2, args.cpu_seconds)
     if cpu:
         log(f"cpu baseline: {cpu}")
@@ -342,7 +369,7 @@ def main():
                      "kernel": "w13_swiglu_stream_kernel<4, 1>", "us_per_launch": round(k_us, 3),
                      "algorithmic_bytes_per_launch": round(k_bytes)},
         "launch_floor_us": round(floor, 3),
-        "sweep": sweep, "prefill": prefill, "dense": dense, "cpu_baseline": cpu,
+        "sweep": sweep, "prefill": prefill, "dense": dense, "route": route, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

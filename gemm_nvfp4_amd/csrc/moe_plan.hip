@@ -251,14 +251,52 @@ __device__ __forceinline__ uint64_t route_key(float x, int e)
     return ((uint64_t)k << 32) | (uint64_t)(~(uint32_t)e);
 }
 
+// Wave-wide reductions on the DPP crossbar (no LDS round trips): pairs, quads, half rows and rows
+// combine with quad_perm / row mirrors, then row broadcasts 15 and 31 carry rows 0-1 and 0-2 up,
+// so lane 63 ends with the whole wave's result. Lanes a step leaves without a source take the
+// identity. The combining tree is fixed, so a floating-point sum is reproducible.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t identity)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, ROWS, 0xf, false);
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t max_step(uint64_t v)
+{
+    const uint64_t o = ((uint64_t)dpp_u32<CTRL, ROWS>((uint32_t)(v >> 32), 0u) << 32) | dpp_u32<CTRL, ROWS>((uint32_t)v, 0u);
+    return o > v ? o : v;
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float add_step(float v)
+{
+    return v + __uint_as_float(dpp_u32<CTRL, ROWS>(__float_as_uint(v), 0u));
+}
+
+// Largest 64-bit key of the wave, in every lane (0 is the identity: below every real key).
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint64_t y = __shfl_xor(v, o, 64);
-        v = y > v ? y : v;
-    }
-    return v;
+    v = max_step<0xB1, 0xf>(v);   // quad_perm [1,0,3,2]
+    v = max_step<0x4E, 0xf>(v);   // quad_perm [2,3,0,1]
+    v = max_step<0x141, 0xf>(v);  // row_half_mirror
+    v = max_step<0x140, 0xf>(v);  // row_mirror: every lane holds its row's maximum
+    v = max_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v = max_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63), hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Sum over the wave in a fixed order, in every lane.
+__device__ __forceinline__ float wave_sum_f32(float v)
+{
+    v = add_step<0xB1, 0xf>(v);
+    v = add_step<0x4E, 0xf>(v);
+    v = add_step<0x141, 0xf>(v);
+    v = add_step<0x140, 0xf>(v);
+    v = add_step<0x142, 0xa>(v);
+    v = add_step<0x143, 0xc>(v);
+    return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
 }
 
 // Routes token row `lg` (E <= 64*NPL logits, 1 <= topk <= min(E, 32)). Lane k < topk ends with
@@ -273,23 +311,23 @@ __device__ __forceinline__ void route_token(const float *__restrict__ lg, int E,
         const int e = lane + 64 * i;
         c[i] = e < E ? route_key(lg[e], e) : 0;  // 0 is below every real key
     }
-    uint64_t thr = ~0ull;
-    id = -1;
+    uint64_t thr = ~0ull, mine = 0;
     for (int r = 0; r < topk; ++r) {
         uint64_t best = 0;
 #pragma unroll
         for (int i = 0; i < NPL; ++i) best = (c[i] < thr && c[i] > best) ? c[i] : best;
         thr = wave_max_u64(best);
-        if (lane == r) id = (int)~(uint32_t)thr;
+        if (lane == r) mine = thr;
     }
-    const float x = lane < topk ? lg[id] : 0.0f;
-    const float l0 = __shfl(x, 0, 64);
+    // The slot's expert and logit come back from its key: the low word is the complemented
+    // expert; the high word inverts to the value (+0 for either zero, NaN for key 0), which gives
+    // the same exponentials as the logit itself.
+    id = (int)~(uint32_t)mine;
+    const uint32_t k = (uint32_t)(mine >> 32);
+    const float x = k == 0 ? __uint_as_float(0x7fc00000u) : __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+    const float l0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), 0));
     const float ev = lane < topk ? expf(x - l0) : 0.0f;
-    float sum = ev;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
-    sum = __shfl(sum, 0, 64);  // lane 0's sum for every slot, so all slots divide by one value
-    w = ev / sum;
+    w = ev / wave_sum_f32(ev);  // one sum for every slot
 }
 
 // Many tokens: one wave per token, four per block.
