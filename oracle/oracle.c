@@ -144,6 +144,54 @@ void orc_linear(const uint16_t *x, int64_t M, int64_t K, const uint8_t *codes, c
     }
 }
 
+/* ---- dense gated MLP ----------------------------------------------------------------------
+ * The packed gate/up projection with SwiGLU and the down projection of a dense NVFP4 MLP ("[SM70]
+ * [Draft] Extend Qwen3.8 DFlash2 concurrency paths", "TP4-only NVFP4 verifier follow-up": gate/up
+ * and down projections of the packed MLP weights). For token m:
+ *   g_i = sum_k x[m][k] W13[gate_i][k],  u_i likewise on the up row,  h_i = silu(g_i) * u_i,
+ *   y_n = sum_i W2[n][i] h_i.
+ * W13 is [2I][K] (layout 0: gate rows [0, I), up rows [I, 2I); layout 1: row 2i gate i, row 2i+1
+ * up i); W2 is [N][I]. h stays in double (the plain definition). h [M][I] and y [M][N] are double.
+ * The sums run in ascending index order, exactly as the MoE oracle's, so a one-expert top-1 MoE
+ * with weight 1 gives the same values. */
+void orc_gated_mlp(const uint16_t *x, int64_t M, int64_t K, int64_t I,
+                   const uint8_t *c13, const uint8_t *s13, const float *g13, int32_t layout,
+                   const uint8_t *c2, const uint8_t *s2, const float *g2, int64_t N,
+                   double *h, double *y, int nthreads)
+{
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *gr = (double *)malloc(sizeof(double) * (size_t)K);
+        double *ur = (double *)malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < I; ++i) {
+            weight_row(c13, s13, g13, 2 * I, K, 0, layout ? 2 * i : i, gr);
+            weight_row(c13, s13, g13, 2 * I, K, 0, layout ? 2 * i + 1 : I + i, ur);
+            for (int64_t m = 0; m < M; ++m) {
+                double g = dot_half_row(x + m * K, gr, K);
+                double u = dot_half_row(x + m * K, ur, K);
+                h[m * I + i] = silu(g) * u;
+            }
+        }
+        free(gr);
+        free(ur);
+    }
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *row = (double *)malloc(sizeof(double) * (size_t)I);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t n = 0; n < N; ++n) {
+            weight_row(c2, s2, g2, N, I, 0, n, row);
+            for (int64_t m = 0; m < M; ++m) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < I; ++i) acc += row[i] * h[m * I + i];
+                y[m * N + n] = acc;
+            }
+        }
+        free(row);
+    }
+}
+
 /* ---- routing plan ------------------------------------------------------------------------ */
 
 /* Stable counting sort of the (token, slot) pairs by expert id.

@@ -51,6 +51,9 @@ def lib():
         L.orc_moe_grouped.restype = None
         L.orc_moe_grouped.argtypes = ([_vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _i32,
                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int])
+        L.orc_gated_mlp.restype = None
+        L.orc_gated_mlp.argtypes = ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i64,
+                                     _vp, _vp, C.c_int])
         L.orc_route.restype = None
         L.orc_route.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp]
         L.orc_w2_reduce.restype = None
@@ -202,3 +205,21 @@ def route(logits: np.ndarray, topk: int):
     w = np.zeros((M, topk), dtype=np.float64)
     lib().orc_route(_p(x), M, E, topk, _p(ids), _p(w))
     return ids, w
+
+
+def gated_mlp(x16: np.ndarray, w13, w2, layout: int = 0, nthreads=None):
+    """orc_gated_mlp: h = silu(x Wg^T) * (x Wu^T) and y = h W2^T in float64. x16 fp16 [M, K];
+    w13 = (codes, scales, gscale) with 2I rows; w2 = (codes, scales, gscale) [N][I]. Returns (h, y)."""
+    c13, s13, g13 = w13
+    c2, s2, g2 = w2
+    M, K = x16.shape
+    I = c13.shape[1] // 2
+    N = c2.shape[1]
+    h = np.empty((M, I), np.float64)
+    y = np.empty((M, N), np.float64)
+    xb = np.ascontiguousarray(x16).view(np.uint16)
+    lib().orc_gated_mlp(_p(xb), M, K, I, _p(np.ascontiguousarray(c13)), _p(np.ascontiguousarray(s13)),
+                        _p(np.ascontiguousarray(g13, dtype=np.float32)), int(layout), _p(np.ascontiguousarray(c2)),
+                        _p(np.ascontiguousarray(s2)), _p(np.ascontiguousarray(g2, dtype=np.float32)), N, _p(h), _p(y),
+                        _threads(nthreads))
+    return h, y
