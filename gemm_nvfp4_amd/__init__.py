@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     lib,
     nvfp4_abi_version,
     nvfp4_linear,
+    nvfp4_linear_swiglu,
     nvfp4_moe_plan,
     nvfp4_moe_plan_bytes,
     nvfp4_moe_route,

@@ -44,6 +44,7 @@ _SIGS = {
     "nvfp4_moe_w2_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "nvfp4_moe_w2_reduce": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_linear": (C.c_int, [_vp, _i32, C.POINTER(nvfp4_weights), _vp, _vp]),
+    "nvfp4_linear_swiglu": (C.c_int, [_vp, _i32, C.POINTER(nvfp4_weights), _i32, _vp, _vp]),
 }
 
 
@@ -200,6 +201,19 @@ def nvfp4_linear(x: torch.Tensor, w: NVFP4Tensor, y: torch.Tensor | None = None,
     _check("nvfp4_linear", lib().nvfp4_linear(_dev(x, "x", torch.float16), M, C.byref(d),
                                               _dev(y, "y", torch.float16), _stream(stream)))
     return y
+
+
+def nvfp4_linear_swiglu(x: torch.Tensor, w13: NVFP4Tensor, layout: int = 0, h: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """Gated dense projection h = fp16(silu(x Wg^T) * (x Wu^T)) of fp16 x [M, K]; returns h [M, I]."""
+    M = x.shape[0]
+    I = w13.rows // 2
+    if h is None:
+        h = torch.empty((M, I), dtype=torch.float16, device=x.device)
+    d = w13.desc()
+    _check("nvfp4_linear_swiglu", lib().nvfp4_linear_swiglu(_dev(x, "x", torch.float16), M, C.byref(d), layout,
+                                                            _dev(h, "h", torch.float16), _stream(stream)))
+    return h
 
 
 class MoELayer:

@@ -146,3 +146,18 @@ NVFP4_API int nvfp4_linear(const uint16_t *x, int32_t M, const nvfp4_weights *w,
     if (!aligned(x, 16) || !aligned(y, 16)) return NVFP4_ERR_ALIGN;
     return nvfp4::run_linear(x, M, *w, y, static_cast<hipStream_t>(stream));
 }
+
+NVFP4_API int nvfp4_linear_swiglu(const uint16_t *x, int32_t M, const nvfp4_weights *w13, int32_t layout, uint16_t *h,
+                                  void *stream)
+{
+    if (M < 0 || (layout != 0 && layout != 1)) return NVFP4_ERR_SHAPE;
+    int st = check_weights(w13);
+    if (st != NVFP4_OK) return st;
+    if (w13->groups != 1 || w13->rows % 2 != 0) return NVFP4_ERR_SHAPE;
+    if (w13->k % 128 != 0 || w13->k > nvfp4::MAX_LINEAR_SWIGLU_K || (w13->rows / 2) % 16 != 0)
+        return NVFP4_ERR_UNSUPPORTED;
+    if (M == 0) return NVFP4_OK;
+    if (!x || !h) return NVFP4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(h, 16)) return NVFP4_ERR_ALIGN;
+    return nvfp4::run_linear_swiglu(x, M, *w13, layout, h, static_cast<hipStream_t>(stream));
+}

@@ -26,6 +26,7 @@ constexpr int MAX_TOPK = 32;
 // over a block's waves; the dense kernel keeps one LDS partial tile per chunk.
 constexpr int MAX_MOE_RED = 2048;
 constexpr int MAX_LINEAR_K = 32768;
+constexpr int MAX_LINEAR_SWIGLU_K = 16384;  // two partial tiles per chunk: 160 KiB of LDS at most
 
 struct PlanLayout {
     int64_t P, A, T, G;
@@ -99,6 +100,8 @@ int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, 
 int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uint16_t *h, const nvfp4_weights &w,
            const float *topk_weights, uint16_t *out, float *ws, hipStream_t s);
 int run_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, uint16_t *y, hipStream_t s);
+int run_linear_swiglu(const uint16_t *x, int32_t M, const nvfp4_weights &w, int32_t layout, uint16_t *h,
+                      hipStream_t s);
 int run_w13_prefill(const PlanView &pv, int64_t a_max, int32_t M, int32_t topk, const uint16_t *x,
                     const nvfp4_weights &w, int32_t layout, uint16_t *h, hipStream_t s);
 int run_w2_prefill(const PlanView &pv, int64_t a_max, int64_t P, const uint16_t *h, const nvfp4_weights &w, float *ws,

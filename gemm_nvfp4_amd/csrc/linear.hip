@@ -1,14 +1,19 @@
 // linear.hip -- dense NVFP4 projection y = fp16(global * x W^T), the "QPN" projection of the
 // "[SM70][Draft] Extend Qwen3.8 DFlash2 concurrency paths" page ("Purpose": independent row tiles
 // admitted through M <= 32; "TP4-only NVFP4 verifier follow-up": two-row-tile CTAs that reuse the
-// loaded packed weights while keeping the split-K / FP32 reduction order).
+// loaded packed weights while keeping the split-K / FP32 reduction order), and its gated form for
+// the packed gate/up projection of a dense MLP (same page and section: the gate/up and down
+// projections of the packed MLP weights): h = fp16(silu(g) * u) with g and u the projections on
+// the gate and up rows.
 //
-// gfx950 design: one block per 16 output columns (weight rows). Its waves share the reduction
-// axis, one 512-element chunk each (intra-block split-K). A wave decodes its chunk once into MFMA
-// B fragments in registers and applies them to every 16-row tile of x, so at small M the weight
-// bytes are read from HBM exactly once. Chunk partials meet in LDS and are added in chunk order,
-// which is the same reduction order as every other GEMM here. A batch of any size is therefore
-// bitwise equal to single-row calls.
+// gfx950 design: one block per 16 output columns (weight rows; gate and up rows of 16 h columns in
+// the gated form). Its waves share the reduction axis, one 512-element chunk each (intra-block
+// split-K). A wave decodes its chunk once into MFMA B fragments in registers and applies them to
+// every 16-row tile of x, so at small M the weight bytes are read from HBM exactly once. Chunk
+// partials meet in LDS and are added in chunk order, which is the same reduction order as every
+// other GEMM here; the gated epilogue is the MoE W13 epilogue (global scale, then SwiGLU). A batch
+// of any size is therefore bitwise equal to single-row calls, and the gated form equals the
+// grouped W13 of a one-expert MoE bitwise.
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 
@@ -16,25 +21,36 @@ namespace nvfp4 {
 namespace {
 
 constexpr int LDS_ROW = 20;
-constexpr int MAX_WAVES = 10;   // waves per block; chunks beyond are taken in turn
+// Waves per block (chunks beyond are taken in turn): ten for the plain form; eight for the gated
+// form, whose two weight tiles per wave need more than the 168 registers ten waves allow.
+template <int NW>
+constexpr int max_waves() { return NW == 1 ? 10 : 8; }
 constexpr int ROW_GROUP = 2;    // 16-row tiles of x handled per pass over the weights
 
-__global__ __launch_bounds__(MAX_WAVES * 64) void linear_kernel(const f16 *__restrict__ x, int M,
+// NW = 1: plain projection, y[m][nt*16 + col]. NW = 2: gated; tile 0 holds the gate rows and tile 1
+// the up rows of h columns nt*16 .. +15 (layout 0: rows i and I + i; layout 1: rows 2i and 2i + 1).
+template <int NW>
+__global__ __launch_bounds__(max_waves<NW>() * 64) void linear_kernel(const f16 *__restrict__ x, int M,
                                                                  const uint8_t *__restrict__ codes,
                                                                  const uint8_t *__restrict__ scales,
                                                                  const float *__restrict__ gscale, int N, int K,
-                                                                 f16 *__restrict__ y)
+                                                                 int layout, f16 *__restrict__ y)
 {
-    extern __shared__ float part[];  // [S][ROW_GROUP][16][LDS_ROW]
+    extern __shared__ float part[];  // [S][ROW_GROUP][NW][16][LDS_ROW]
     const int nt = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
     const int n = lane & 15, q = lane >> 4;
     const int S = num_chunks(K);
     const int row_tiles = (M + 15) >> 4;
-    const size_t wrow = (size_t)nt * 16 + n;
-    const uint8_t *cr = codes + wrow * ((size_t)K >> 1);
-    const uint8_t *sr = scales + wrow * ((size_t)K >> 4);
+    const int col = nt * 16 + n;  // output column of this lane's weight rows
+    const uint8_t *cr[NW], *sr[NW];
+#pragma unroll
+    for (int t = 0; t < NW; ++t) {
+        const size_t wrow = NW == 1 ? (size_t)col : (size_t)(layout ? 2 * col + t : t * N + col);
+        cr[t] = codes + wrow * ((size_t)K >> 1);
+        sr[t] = scales + wrow * ((size_t)K >> 4);
+    }
     const float gs = gscale[0];
 
     for (int rt0 = 0; rt0 < row_tiles; rt0 += ROW_GROUP) {
@@ -42,7 +58,9 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void linear_kernel(const f16 *__res
             const int kb = c * KCHUNK;
             const int groups = min(KCHUNK, K - kb) >> 7;  // 128-element lane groups with data
             const bool qv = q < groups;
-            const RawChunk w = load_chunk(cr, sr, kb, qv ? q : groups - 1);
+            RawChunk w[NW];
+#pragma unroll
+            for (int t = 0; t < NW; ++t) w[t] = load_chunk(cr[t], sr[t], kb, qv ? q : groups - 1);
 #pragma unroll
             for (int r = 0; r < ROW_GROUP; ++r) {
                 const int rt = rt0 + r;
@@ -65,48 +83,75 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void linear_kernel(const f16 *__res
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
                         if (!rv) af[b][s] = zero8();
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                f32x4 acc[NW];
+#pragma unroll
+                for (int t = 0; t < NW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    const f16x2 sc = chunk_scales(w, b);
+                    f16x2 sc[NW];
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) acc = mfma_step(af[b][s], b_frag(w, sc, b, s, qv), acc);
+                    for (int t = 0; t < NW; ++t) sc[t] = chunk_scales(w[t], b);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+#pragma unroll
+                        for (int t = 0; t < NW; ++t) acc[t] = mfma_step(af[b][s], b_frag(w[t], sc[t], b, s, qv), acc[t]);
                 }
-                float *pc = part + ((size_t)c * ROW_GROUP + r) * 16 * LDS_ROW;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) pc[(4 * q + j) * LDS_ROW + n] = acc[j];
+                for (int t = 0; t < NW; ++t) {
+                    float *pc = part + (((size_t)c * ROW_GROUP + r) * NW + t) * 16 * LDS_ROW;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) pc[(4 * q + j) * LDS_ROW + n] = acc[t][j];
+                }
             }
         }
         __syncthreads();
         for (int o = threadIdx.x; o < ROW_GROUP * 256; o += blockDim.x) {
-            const int r = o >> 8, row = (o >> 4) & 15, col = o & 15;
+            const int r = o >> 8, row = (o >> 4) & 15, cl = o & 15;
             const int m = (rt0 + r) * 16 + row;
             if (rt0 + r < row_tiles && m < M) {
-                float tot = part[((size_t)0 * ROW_GROUP + r) * 16 * LDS_ROW + row * LDS_ROW + col];
-                for (int c = 1; c < S; ++c) tot += part[((size_t)c * ROW_GROUP + r) * 16 * LDS_ROW + row * LDS_ROW + col];
-                y[(size_t)m * N + nt * 16 + col] = (f16)(tot * gs);
+                float tot[NW];
+#pragma unroll
+                for (int t = 0; t < NW; ++t) {
+                    tot[t] = part[(((size_t)0 * ROW_GROUP + r) * NW + t) * 16 * LDS_ROW + row * LDS_ROW + cl];
+                    for (int c = 1; c < S; ++c)
+                        tot[t] += part[(((size_t)c * ROW_GROUP + r) * NW + t) * 16 * LDS_ROW + row * LDS_ROW + cl];
+                }
+                if constexpr (NW == 1) y[(size_t)m * N + nt * 16 + cl] = (f16)(tot[0] * gs);
+                else y[(size_t)m * N + nt * 16 + cl] = (f16)swiglu(tot[0] * gs, tot[1] * gs);
             }
         }
         __syncthreads();
     }
 }
 
+template <int NW>
+int launch_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, int N, int layout, uint16_t *y, hipStream_t s)
+{
+    const int K = w.k;
+    const int S = num_chunks(K);
+    const int waves = S < max_waves<NW>() ? S : max_waves<NW>();
+    const size_t shmem = (size_t)S * ROW_GROUP * NW * 16 * LDS_ROW * sizeof(float);
+    if (shmem > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(linear_kernel<NW>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+        if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
+    }
+    return launch(linear_kernel<NW>, dim3((unsigned)(N / 16)), dim3((unsigned)(waves * 64)), shmem, s,
+                  reinterpret_cast<const f16 *>(x), M, w.codes, w.scales, w.global_scale, N, K, layout,
+                  reinterpret_cast<f16 *>(y));
+}
+
 }  // namespace
 
 int run_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, uint16_t *y, hipStream_t s)
 {
-    const int N = w.rows, K = w.k;
-    const int S = num_chunks(K);
-    const int waves = S < MAX_WAVES ? S : MAX_WAVES;
-    const size_t shmem = (size_t)S * ROW_GROUP * 16 * LDS_ROW * sizeof(float);
-    if (shmem > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(linear_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-        if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
-    }
-    return launch(linear_kernel, dim3((unsigned)(N / 16)), dim3((unsigned)(waves * 64)), shmem, s,
-                  reinterpret_cast<const f16 *>(x), M, w.codes, w.scales, w.global_scale, N, K,
-                  reinterpret_cast<f16 *>(y));
+    return launch_linear<1>(x, M, w, w.rows, 0, y, s);
+}
+
+int run_linear_swiglu(const uint16_t *x, int32_t M, const nvfp4_weights &w, int32_t layout, uint16_t *h,
+                      hipStream_t s)
+{
+    return launch_linear<2>(x, M, w, w.rows / 2, layout, h, s);
 }
 
 }  // namespace nvfp4

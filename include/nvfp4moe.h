@@ -171,6 +171,22 @@ int nvfp4_moe_w2_reduce(const void *plan, int32_t M, int32_t topk, int32_t E,
  * --------------------------------------------------------------------------------------------- */
 int nvfp4_linear(const uint16_t *x, int32_t M, const nvfp4_weights *w, uint16_t *y, void *stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * Gated form of the dense projection: the packed gate/up projection of a dense NVFP4 MLP with
+ * SwiGLU fused (DFlash2 page, "TP4-only NVFP4 verifier follow-up": the gate/up and down
+ * projections of the packed MLP weights; the down projection is nvfp4_linear on h).
+ *   x    fp16 [M][K]
+ *   w13  groups = 1, rows = 2I, k = K; layout 0: gate rows [0, I), up rows [I, 2I);
+ *        layout 1: row 2i is gate i, row 2i+1 is up i
+ *   h    fp16 [M][I]
+ *   g = global * sum_k x[m,k] * e2m1*e4m3 (gate row i),  u = likewise (up row i),
+ *   h[m][i] = fp16_rne( silu(g) * u ),  silu(g) = g / (1 + exp(-g)),  all FP32.
+ * The arithmetic is that of nvfp4_moe_w13_swiglu, so h equals a one-expert MoE's W13 bitwise.
+ * Requirements: K % 128 == 0 and K <= 16384; I % 16 == 0; x, h, codes 16-byte aligned.
+ * --------------------------------------------------------------------------------------------- */
+int nvfp4_linear_swiglu(const uint16_t *x, int32_t M, const nvfp4_weights *w13, int32_t layout, uint16_t *h,
+                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,8 @@ def declared():
 def test_header_declares_the_expected_entry_points():
     assert declared() == sorted([
         "nvfp4_abi_version", "nvfp4_status_str", "nvfp4_moe_plan_bytes", "nvfp4_moe_plan", "nvfp4_moe_route",
-        "nvfp4_moe_w13_swiglu", "nvfp4_moe_w2_workspace_bytes", "nvfp4_moe_w2_reduce", "nvfp4_linear"])
+        "nvfp4_moe_w13_swiglu", "nvfp4_moe_w2_workspace_bytes", "nvfp4_moe_w2_reduce", "nvfp4_linear",
+        "nvfp4_linear_swiglu"])
 
 
 def test_library_exports_every_declared_function():
@@ -80,3 +81,9 @@ def test_argument_checks_fail_closed(L):
     assert L.nvfp4_linear(fake, -1, C.byref(w), fake, null) == 2
     w = nvfp4_weights(None, fake, fake, 1, 64, 128)
     assert L.nvfp4_linear(fake, 4, C.byref(w), fake, null) == 1
+    # gated form: odd rows, I % 16 != 0, K too long, bad layout
+    assert L.nvfp4_linear_swiglu(fake, 4, C.byref(nvfp4_weights(fake, fake, fake, 1, 63, 128)), 0, fake, null) == 2
+    assert L.nvfp4_linear_swiglu(fake, 4, C.byref(nvfp4_weights(fake, fake, fake, 1, 40, 128)), 0, fake, null) == 5
+    assert L.nvfp4_linear_swiglu(fake, 4, C.byref(nvfp4_weights(fake, fake, fake, 1, 64, 32768)), 0, fake, null) == 5
+    assert L.nvfp4_linear_swiglu(fake, 4, C.byref(nvfp4_weights(fake, fake, fake, 1, 64, 128)), 2, fake, null) == 2
+    assert L.nvfp4_linear_swiglu(fake, 0, C.byref(nvfp4_weights(fake, fake, fake, 1, 64, 128)), 0, null, null) == 0
