@@ -61,6 +61,7 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--no-route", action="store_true")
+    p.add_argument("--no-mlp", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--traffic", action="store_true",
@@ -255,6 +256,30 @@ def dense_timing(copies=64, launches=256):
     return res
 
 
+def mlp_timing(copies=48, launches=192):
+    """Dense gated MLP shard (hidden 5120, 2176 intermediate columns): the gated gate/up projection
+    (4352 x 5120 packed weights) and the down projection (5120 x 2176), µs per call in graphs that
+    rotate `copies` weight sets (about 0.9 GB, beyond the 256 MB MALL)."""
+    import torch
+    import gemm_nvfp4_amd as G
+    from synth import inputs as S
+    Kd, Id = S.DENSE_K, S.DENSE_N // 2
+    w13 = [G.NVFP4Tensor(*S.device_nvfp4_weights(9000 + c, 1, 2 * Id, Kd)) for c in range(copies)]
+    w2 = [G.NVFP4Tensor(*S.device_nvfp4_weights(9500 + c, 1, Kd, Id)) for c in range(copies)]
+    b13, b2 = 2 * Id * Kd * 9 // 16, Kd * Id * 9 // 16
+    res = []
+    for M in (1, 16, 32):
+        x = torch.from_numpy(S.activations(S.rng_for(1, 0, 2000 + M), M, Kd)).cuda()
+        h = torch.empty((M, Id), dtype=torch.float16, device="cuda")
+        y = torch.empty((M, Kd), dtype=torch.float16, device="cuda")
+        g_ms = time_graph(lambda: [G.nvfp4_linear_swiglu(x, w13[i % copies], h=h) for i in range(launches)], launches)
+        d_ms = time_graph(lambda: [G.nvfp4_linear(h, w2[i % copies], y=y) for i in range(launches)], launches)
+        g_us, d_us = g_ms * 1e3 / launches, d_ms * 1e3 / launches
+        res.append({"M": M, "gate_up_swiglu_us": round(g_us, 3), "down_us": round(d_us, 3),
+                    "weight_GBps": round((b13 + b2) / ((g_us + d_us) * 1e-6) / 1e9, 1)})
+    return res
+
+
 def route_timing(launches=256, patterns=8):
     """Router fused with the plan (fp32 logits -> ids, weights, plan) against the plan alone from
     ids, µs per call in graphs of `launches` calls, at 1, 16 and 8192 tokens (512 experts, top-10)."""
@@ -346,6 +371,10 @@ def main():
     if not args.no_dense:
         dense = dense_timing()
         log(f"dense: {dense}")
+    mlp = None
+    if not args.no_mlp:
+        mlp = mlp_timing()
+        log(f"dense gated MLP: {mlp}")
     route = None
     if not args.no_route:
         route = route_timing()
@@ -369,7 +398,7 @@ def main():
                      "kernel": "w13_swiglu_stream_kernel<4, 1>", "us_per_launch": round(k_us, 3),
                      "algorithmic_bytes_per_launch": round(k_bytes)},
         "launch_floor_us": round(floor, 3),
-        "sweep": sweep, "prefill": prefill, "dense": dense, "route": route, "cpu_baseline": cpu,
+        "sweep": sweep, "prefill": prefill, "dense": dense, "mlp": mlp, "route": route, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

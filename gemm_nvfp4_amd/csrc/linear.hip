@@ -25,11 +25,13 @@ constexpr int LDS_ROW = 20;
 // form, whose two weight tiles per wave need more than the 168 registers ten waves allow.
 template <int NW>
 constexpr int max_waves() { return NW == 1 ? 10 : 8; }
+
 constexpr int ROW_GROUP = 2;    // 16-row tiles of x handled per pass over the weights
 
-// NW = 1: plain projection, y[m][nt*16 + col]. NW = 2: gated; tile 0 holds the gate rows and tile 1
-// the up rows of h columns nt*16 .. +15 (layout 0: rows i and I + i; layout 1: rows 2i and 2i + 1).
-template <int NW>
+// Each wave holds NW 16-row weight tiles. Plain (GATED false): tile t covers output columns
+// (nt*NW + t)*16 .. +15. Gated: tile 0 holds the gate rows and tile 1 the up rows of h columns
+// nt*16 .. +15 (layout 0: rows i and I + i; layout 1: rows 2i and 2i + 1).
+template <int NW, bool GATED>
 __global__ __launch_bounds__(max_waves<NW>() * 64) void linear_kernel(const f16 *__restrict__ x, int M,
                                                                  const uint8_t *__restrict__ codes,
                                                                  const uint8_t *__restrict__ scales,
@@ -43,11 +45,11 @@ __global__ __launch_bounds__(max_waves<NW>() * 64) void linear_kernel(const f16 
     const int n = lane & 15, q = lane >> 4;
     const int S = num_chunks(K);
     const int row_tiles = (M + 15) >> 4;
-    const int col = nt * 16 + n;  // output column of this lane's weight rows
+    const int col = nt * 16 + n;  // gated: h column of this lane's weight rows
     const uint8_t *cr[NW], *sr[NW];
 #pragma unroll
     for (int t = 0; t < NW; ++t) {
-        const size_t wrow = NW == 1 ? (size_t)col : (size_t)(layout ? 2 * col + t : t * N + col);
+        const size_t wrow = GATED ? (size_t)(layout ? 2 * col + t : t * N + col) : (size_t)((nt * NW + t) * 16 + n);
         cr[t] = codes + wrow * ((size_t)K >> 1);
         sr[t] = scales + wrow * ((size_t)K >> 4);
     }
@@ -116,15 +118,19 @@ __global__ __launch_bounds__(max_waves<NW>() * 64) void linear_kernel(const f16 
                     for (int c = 1; c < S; ++c)
                         tot[t] += part[(((size_t)c * ROW_GROUP + r) * NW + t) * 16 * LDS_ROW + row * LDS_ROW + cl];
                 }
-                if constexpr (NW == 1) y[(size_t)m * N + nt * 16 + cl] = (f16)(tot[0] * gs);
-                else y[(size_t)m * N + nt * 16 + cl] = (f16)swiglu(tot[0] * gs, tot[1] * gs);
+                if constexpr (GATED) {
+                    y[(size_t)m * N + nt * 16 + cl] = (f16)swiglu(tot[0] * gs, tot[1] * gs);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < NW; ++t) y[(size_t)m * N + (nt * NW + t) * 16 + cl] = (f16)(tot[t] * gs);
+                }
             }
         }
         __syncthreads();
     }
 }
 
-template <int NW>
+template <int NW, bool GATED>
 int launch_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, int N, int layout, uint16_t *y, hipStream_t s)
 {
     const int K = w.k;
@@ -132,11 +138,12 @@ int launch_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, int N, i
     const int waves = S < max_waves<NW>() ? S : max_waves<NW>();
     const size_t shmem = (size_t)S * ROW_GROUP * NW * 16 * LDS_ROW * sizeof(float);
     if (shmem > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(linear_kernel<NW>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(linear_kernel<NW, GATED>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
         if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
     }
-    return launch(linear_kernel<NW>, dim3((unsigned)(N / 16)), dim3((unsigned)(waves * 64)), shmem, s,
+    const int blocks = GATED ? N / 16 : N / (16 * NW);
+    return launch(linear_kernel<NW, GATED>, dim3((unsigned)blocks), dim3((unsigned)(waves * 64)), shmem, s,
                   reinterpret_cast<const f16 *>(x), M, w.codes, w.scales, w.global_scale, N, K, layout,
                   reinterpret_cast<f16 *>(y));
 }
@@ -145,13 +152,17 @@ int launch_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, int N, i
 
 int run_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, uint16_t *y, hipStream_t s)
 {
-    return launch_linear<1>(x, M, w, w.rows, 0, y, s);
+#ifndef NVFP4_LINEAR_TILES
+#define NVFP4_LINEAR_TILES 2
+#endif
+    if (NVFP4_LINEAR_TILES == 2 && w.rows % 32 == 0) return launch_linear<2, false>(x, M, w, w.rows, 0, y, s);
+    return launch_linear<1, false>(x, M, w, w.rows, 0, y, s);
 }
 
 int run_linear_swiglu(const uint16_t *x, int32_t M, const nvfp4_weights &w, int32_t layout, uint16_t *h,
                       hipStream_t s)
 {
-    return launch_linear<2>(x, M, w, w.rows / 2, layout, h, s);
+    return launch_linear<2, true>(x, M, w, w.rows / 2, layout, h, s);
 }
 
 }  // namespace nvfp4
