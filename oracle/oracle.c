@@ -144,6 +144,27 @@ void orc_linear(const uint16_t *x, int64_t M, int64_t K, const uint8_t *codes, c
     }
 }
 
+/* ---- channel-FP8 dense projection ---------------------------------------------------------
+ * The channel-FP8 "QPN8" projection ("[SM70][Draft] Extend Qwen3.8 DFlash2 concurrency paths",
+ * "Follow-up: exact channel-FP8 QPN8 concurrency paths and endpoint evidence"): weights are E4M3FN
+ * bytes with one FP32 scale per output channel (weight row). The plain definition:
+ *   y[m][n] = sum_k x[m][k] * (e4m3(W[n][k]) * s[n]),
+ * in double (e4m3 has 4 significant bits and s 24, so each weight is exact). */
+void orc_linear_fp8(const uint16_t *x, int64_t M, int64_t K, const uint8_t *codes, const float *chscale,
+                    int64_t N, double *y, int nthreads)
+{
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *row = (double *)malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t k = 0; k < K; ++k) row[k] = orc_e4m3(codes[n * K + k]) * (double)chscale[n];
+            for (int64_t m = 0; m < M; ++m) y[m * N + n] = dot_half_row(x + m * K, row, K);
+        }
+        free(row);
+    }
+}
+
 /* ---- dense gated MLP ----------------------------------------------------------------------
  * The packed gate/up projection with SwiGLU and the down projection of a dense NVFP4 MLP ("[SM70]
  * [Draft] Extend Qwen3.8 DFlash2 concurrency paths", "TP4-only NVFP4 verifier follow-up": gate/up

@@ -54,6 +54,8 @@ def lib():
         L.orc_gated_mlp.restype = None
         L.orc_gated_mlp.argtypes = ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i64,
                                      _vp, _vp, C.c_int])
+        L.orc_linear_fp8.restype = None
+        L.orc_linear_fp8.argtypes = [_vp, _i64, _i64, _vp, _vp, _i64, _vp, C.c_int]
         L.orc_route.restype = None
         L.orc_route.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp]
         L.orc_w2_reduce.restype = None
@@ -223,3 +225,15 @@ def gated_mlp(x16: np.ndarray, w13, w2, layout: int = 0, nthreads=None):
                         _p(np.ascontiguousarray(s2)), _p(np.ascontiguousarray(g2, dtype=np.float32)), N, _p(h), _p(y),
                         _threads(nthreads))
     return h, y
+
+
+def linear_fp8(x16: np.ndarray, codes: np.ndarray, chscale: np.ndarray, nthreads=None) -> np.ndarray:
+    """orc_linear_fp8: y = x @ (e4m3(W) * s[:, None])^T in float64. x16 fp16 [M,K]; codes uint8 [N,K];
+    chscale float32 [N]."""
+    M, K = x16.shape
+    N = codes.shape[0]
+    y = np.empty((M, N), dtype=np.float64)
+    xb = np.ascontiguousarray(x16).view(np.uint16)
+    lib().orc_linear_fp8(_p(xb), M, K, _p(np.ascontiguousarray(codes, dtype=np.uint8)),
+                         _p(np.ascontiguousarray(chscale, dtype=np.float32)), N, _p(y), _threads(nthreads))
+    return y

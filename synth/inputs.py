@@ -43,6 +43,7 @@ __all__ = [
     "device_nvfp4_weights",
     "active_experts",
     "router_logits",
+    "fp8_channel_weights",
 ]
 
 # E4M3FN bytes of 2^u for integer u in [-8, -4]: 2^-8 and 2^-7 are E4M3 subnormals (0x02, 0x04),
@@ -227,3 +228,14 @@ def router_logits(rng: np.random.Generator, m: int, e: int, kind: str = "normal"
         x[(u >= 0.07) & (u < 0.08)] = np.float32(-0.0)
         return x
     raise ValueError(kind)
+
+
+def fp8_channel_weights(rng: np.random.Generator, rows: int, k: int):
+    """Channel-FP8 weights: uniform random E4M3FN bytes (every exponent, subnormals and both zeros
+    included) with the NaN patterns 0x7F/0xFF replaced by 0x7E/0xFE, and one float32 scale per row
+    2^u, u uniform in [-6, -4]. Returns (codes uint8 [rows, k], scale float32 [rows])."""
+    codes = rng.integers(0, 256, size=(rows, k), dtype=np.uint8)
+    codes[codes == 0x7F] = 0x7E
+    codes[codes == 0xFF] = 0xFE
+    scale = np.exp2(rng.uniform(-6.0, -4.0, size=rows)).astype(np.float32)
+    return codes, scale
