@@ -4,6 +4,7 @@ The compute lives in libnvfp4moe.so (HIP, C ABI in include/nvfp4moe.h); this pac
 Python binding. Entry points carry the C names.
 """
 from ._lib import (  # noqa: F401
+    FP8ChannelTensor,
     MoELayer,
     NVFP4Error,
     NVFP4Tensor,
@@ -11,6 +12,7 @@ from ._lib import (  # noqa: F401
     lib,
     nvfp4_abi_version,
     nvfp4_linear,
+    nvfp4_linear_fp8,
     nvfp4_linear_swiglu,
     nvfp4_moe_plan,
     nvfp4_moe_plan_bytes,

@@ -32,6 +32,10 @@ class nvfp4_weights(C.Structure):
                 ("groups", C.c_int32), ("rows", C.c_int32), ("k", C.c_int32)]
 
 
+class fp8_channel_weights(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("channel_scale", C.c_void_p), ("rows", C.c_int32), ("k", C.c_int32)]
+
+
 _LIB = None
 _vp, _i32, _sz = C.c_void_p, C.c_int32, C.c_size_t
 _SIGS = {
@@ -45,6 +49,7 @@ _SIGS = {
     "nvfp4_moe_w2_reduce": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_linear": (C.c_int, [_vp, _i32, C.POINTER(nvfp4_weights), _vp, _vp]),
     "nvfp4_linear_swiglu": (C.c_int, [_vp, _i32, C.POINTER(nvfp4_weights), _i32, _vp, _vp]),
+    "nvfp4_linear_fp8": (C.c_int, [_vp, _i32, C.POINTER(fp8_channel_weights), _vp, _vp]),
 }
 
 
@@ -200,6 +205,36 @@ def nvfp4_linear(x: torch.Tensor, w: NVFP4Tensor, y: torch.Tensor | None = None,
     d = w.desc()
     _check("nvfp4_linear", lib().nvfp4_linear(_dev(x, "x", torch.float16), M, C.byref(d),
                                               _dev(y, "y", torch.float16), _stream(stream)))
+    return y
+
+
+class FP8ChannelTensor:
+    """Device storage of a channel-FP8 weight: E4M3FN bytes uint8 [N, K] and float32 scales [N]."""
+
+    def __init__(self, codes: torch.Tensor, channel_scale: torch.Tensor):
+        if codes.dim() != 2 or channel_scale.dim() != 1 or channel_scale.shape[0] != codes.shape[0]:
+            raise ValueError("codes must be [N, K] and channel_scale [N]")
+        self.codes, self.channel_scale = codes, channel_scale
+        self.rows, self.k = codes.shape
+
+    @classmethod
+    def from_numpy(cls, w, device="cuda"):
+        codes, scale = w
+        return cls(torch.from_numpy(codes).to(device), torch.from_numpy(scale).to(device))
+
+    def desc(self) -> fp8_channel_weights:
+        return fp8_channel_weights(_dev(self.codes, "codes", torch.uint8),
+                                   _dev(self.channel_scale, "channel_scale", torch.float32), self.rows, self.k)
+
+
+def nvfp4_linear_fp8(x: torch.Tensor, w: FP8ChannelTensor, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Channel-FP8 dense projection y = fp16(s * (x @ e4m3(W)^T)) of fp16 x [M, K]; returns y [M, N]."""
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, w.rows), dtype=torch.float16, device=x.device)
+    d = w.desc()
+    _check("nvfp4_linear_fp8", lib().nvfp4_linear_fp8(_dev(x, "x", torch.float16), M, C.byref(d),
+                                                      _dev(y, "y", torch.float16), _stream(stream)))
     return y
 
 

@@ -161,3 +161,16 @@ NVFP4_API int nvfp4_linear_swiglu(const uint16_t *x, int32_t M, const nvfp4_weig
     if (!aligned(x, 16) || !aligned(h, 16)) return NVFP4_ERR_ALIGN;
     return nvfp4::run_linear_swiglu(x, M, *w13, layout, h, static_cast<hipStream_t>(stream));
 }
+
+NVFP4_API int nvfp4_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights *w, uint16_t *y, void *stream)
+{
+    if (M < 0) return NVFP4_ERR_SHAPE;
+    if (!w || !w->codes || !w->channel_scale) return NVFP4_ERR_NULL;
+    if (w->rows < 1 || w->k < 16) return NVFP4_ERR_SHAPE;
+    if (w->k % 128 != 0 || w->k > nvfp4::MAX_LINEAR_FP8_K || w->rows % 16 != 0) return NVFP4_ERR_UNSUPPORTED;
+    if (!aligned(w->codes, 16) || !aligned(w->channel_scale, 4)) return NVFP4_ERR_ALIGN;
+    if (M == 0) return NVFP4_OK;
+    if (!x || !y) return NVFP4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(y, 16)) return NVFP4_ERR_ALIGN;
+    return nvfp4::run_linear_fp8(x, M, *w, y, static_cast<hipStream_t>(stream));
+}

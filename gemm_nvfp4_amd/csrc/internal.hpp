@@ -27,6 +27,7 @@ constexpr int MAX_TOPK = 32;
 constexpr int MAX_MOE_RED = 2048;
 constexpr int MAX_LINEAR_K = 32768;
 constexpr int MAX_LINEAR_SWIGLU_K = 16384;  // two partial tiles per chunk: 160 KiB of LDS at most
+constexpr int MAX_LINEAR_FP8_K = 16384;     // likewise for the channel-FP8 projection
 
 struct PlanLayout {
     int64_t P, A, T, G;
@@ -100,6 +101,7 @@ int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, 
 int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uint16_t *h, const nvfp4_weights &w,
            const float *topk_weights, uint16_t *out, float *ws, hipStream_t s);
 int run_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, uint16_t *y, hipStream_t s);
+int run_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights &w, uint16_t *y, hipStream_t s);
 int run_linear_swiglu(const uint16_t *x, int32_t M, const nvfp4_weights &w, int32_t layout, uint16_t *h,
                       hipStream_t s);
 int run_w13_prefill(const PlanView &pv, int64_t a_max, int32_t M, int32_t topk, const uint16_t *x,

@@ -130,6 +130,134 @@ __global__ __launch_bounds__(max_waves<NW>() * 64) void linear_kernel(const f16 
     }
 }
 
+// ---- channel-FP8 ("QPN8") weights ----------------------------------------------------------------
+// The channel-FP8 projection of the same page ("Follow-up: exact channel-FP8 QPN8 concurrency
+// paths and endpoint evidence"): E4M3FN weight bytes with one FP32 scale per output channel. An
+// E4M3 byte converts to fp16 exactly (one gfx950 convert per pair, no block scale), the MFMA chain
+// and the chunk order are the library's, and the channel scale multiplies the FP32 sum in the
+// epilogue, where it is exact arithmetic on the definition (the pages apply it before the MMA).
+
+// One lane's bytes of one weight row for one chunk: lane group q's 128 elements, eight 16-byte loads.
+struct Fp8Chunk {
+    u32x4 codes[8];  // codes[j] = elements [kb + 128q + 16j, +16)
+};
+
+__device__ __forceinline__ Fp8Chunk load_chunk8(const uint8_t *row, int kb, int q_ld)
+{
+    Fp8Chunk r;
+    const uint8_t *c = row + kb + 128 * q_ld;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r.codes[j] = *reinterpret_cast<const u32x4 *>(c + 16 * j);
+    return r;
+}
+
+// B fragment of step (b, s): elements [128q + 32b + 8s, +8), i.e. half of load 2b + s/2.
+__device__ __forceinline__ f16x8 b_frag8(const Fp8Chunk &r, int b, int s, bool qv)
+{
+    const u32x4 v = r.codes[2 * b + (s >> 1)];
+    const uint32_t d0 = v[2 * (s & 1)], d1 = v[2 * (s & 1) + 1];
+    const f16x2 p0 = e4m3_pair<false>(d0), p1 = e4m3_pair<true>(d0), p2 = e4m3_pair<false>(d1), p3 = e4m3_pair<true>(d1);
+    const f16x8 w = f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    return qv ? w : zero8();
+}
+
+// Two 16-row weight tiles per wave (output columns (nt*2 + t)*16 .. +15), as the NVFP4 kernel.
+template <int NW>
+__global__ __launch_bounds__(8 * 64) void linear_fp8_kernel(const f16 *__restrict__ x, int M,
+                                                          const uint8_t *__restrict__ codes,
+                                                          const float *__restrict__ chscale, int N, int K,
+                                                          f16 *__restrict__ y)
+{
+    extern __shared__ float part[];  // [S][ROW_GROUP][NW][16][LDS_ROW]
+    const int nt = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const int n = lane & 15, q = lane >> 4;
+    const int S = num_chunks(K);
+    const int row_tiles = (M + 15) >> 4;
+    const uint8_t *cr[NW];
+#pragma unroll
+    for (int t = 0; t < NW; ++t) cr[t] = codes + (size_t)((nt * NW + t) * 16 + n) * K;
+
+    for (int rt0 = 0; rt0 < row_tiles; rt0 += ROW_GROUP) {
+        for (int c = wave; c < S; c += nwaves) {
+            const int kb = c * KCHUNK;
+            const int groups = min(KCHUNK, K - kb) >> 7;
+            const bool qv = q < groups;
+            Fp8Chunk w[NW];
+#pragma unroll
+            for (int t = 0; t < NW; ++t) w[t] = load_chunk8(cr[t], kb, qv ? q : groups - 1);
+#pragma unroll
+            for (int r = 0; r < ROW_GROUP; ++r) {
+                const int rt = rt0 + r;
+                if (rt >= row_tiles) break;
+                const int m = rt * 16 + n;
+                const bool rv = m < M && qv;
+                const f16 *xr = x + (size_t)(m < M ? m : 0) * K;
+                const int qa = qv ? q : 0;
+                f16x8 af[4][4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) af[b][s] = a_frag(xr, kb, qa, b, s);
+                __builtin_amdgcn_sched_barrier(0);  // every load (weights, then A) is issued before the math
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        if (!rv) af[b][s] = zero8();
+                f32x4 acc[NW];
+#pragma unroll
+                for (int t = 0; t < NW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+#pragma unroll
+                        for (int t = 0; t < NW; ++t) acc[t] = mfma_step(af[b][s], b_frag8(w[t], b, s, qv), acc[t]);
+#pragma unroll
+                for (int t = 0; t < NW; ++t) {
+                    float *pc = part + (((size_t)c * ROW_GROUP + r) * NW + t) * 16 * LDS_ROW;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) pc[(4 * q + j) * LDS_ROW + n] = acc[t][j];
+                }
+            }
+        }
+        __syncthreads();
+        for (int o = threadIdx.x; o < ROW_GROUP * 256; o += blockDim.x) {
+            const int r = o >> 8, row = (o >> 4) & 15, cl = o & 15;
+            const int m = (rt0 + r) * 16 + row;
+            if (rt0 + r < row_tiles && m < M) {
+#pragma unroll
+                for (int t = 0; t < NW; ++t) {
+                    float tot = part[(((size_t)0 * ROW_GROUP + r) * NW + t) * 16 * LDS_ROW + row * LDS_ROW + cl];
+                    for (int c = 1; c < S; ++c)
+                        tot += part[(((size_t)c * ROW_GROUP + r) * NW + t) * 16 * LDS_ROW + row * LDS_ROW + cl];
+                    const int colx = (nt * NW + t) * 16 + cl;
+                    y[(size_t)m * N + colx] = (f16)(tot * chscale[colx]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int NW>
+int launch_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights &w, uint16_t *y, hipStream_t s)
+{
+    const int N = w.rows, K = w.k;
+    const int S = num_chunks(K);
+    const int waves = S < 8 ? S : 8;
+    const size_t shmem = (size_t)S * ROW_GROUP * NW * 16 * LDS_ROW * sizeof(float);
+    if (shmem > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(linear_fp8_kernel<NW>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+        if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
+    }
+    return launch(linear_fp8_kernel<NW>, dim3((unsigned)(N / (16 * NW))), dim3((unsigned)(waves * 64)), shmem, s,
+                  reinterpret_cast<const f16 *>(x), M, w.codes, w.channel_scale, N, K, reinterpret_cast<f16 *>(y));
+}
+
 template <int NW, bool GATED>
 int launch_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, int N, int layout, uint16_t *y, hipStream_t s)
 {
@@ -157,6 +285,12 @@ int run_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, uint16_t *y
 #endif
     if (NVFP4_LINEAR_TILES == 2 && w.rows % 32 == 0) return launch_linear<2, false>(x, M, w, w.rows, 0, y, s);
     return launch_linear<1, false>(x, M, w, w.rows, 0, y, s);
+}
+
+int run_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights &w, uint16_t *y, hipStream_t s)
+{
+    if (w.rows % 32 == 0) return launch_linear_fp8<2>(x, M, w, y, s);
+    return launch_linear_fp8<1>(x, M, w, y, s);
 }
 
 int run_linear_swiglu(const uint16_t *x, int32_t M, const nvfp4_weights &w, int32_t layout, uint16_t *h,

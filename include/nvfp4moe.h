@@ -67,6 +67,14 @@ typedef struct nvfp4_weights {
     int32_t groups, rows, k;
 } nvfp4_weights;
 
+/* A channel-FP8 weight tensor (the "QPN8" format): `rows` x `k` E4M3FN bytes and one FP32 scale
+ * per row (output channel). */
+typedef struct fp8_channel_weights {
+    const uint8_t *codes;          /* device, [rows][k] E4M3FN bytes, 16-byte aligned            */
+    const float *channel_scale;    /* device, [rows]                                             */
+    int32_t rows, k;
+} fp8_channel_weights;
+
 /* ABI version of the loaded library (NVFP4_ABI_VERSION). A caller checks it before use
  * ("native ABI capability check", DFlash2 page, "Purpose"). */
 int nvfp4_abi_version(void);
@@ -170,6 +178,18 @@ int nvfp4_moe_w2_reduce(const void *plan, int32_t M, int32_t topk, int32_t E,
  * Requirements: K % 128 == 0; N % 16 == 0; x, y, codes 16-byte aligned.
  * --------------------------------------------------------------------------------------------- */
 int nvfp4_linear(const uint16_t *x, int32_t M, const nvfp4_weights *w, uint16_t *y, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Channel-FP8 dense projection (the "QPN8" path, DFlash2 page, "Follow-up: exact channel-FP8 QPN8
+ * concurrency paths and endpoint evidence"):
+ *   y[m][n] = fp16_rne( s[n] * sum_k x[m][k] * e4m3(W[n][k]) ),  FP32 accumulation,
+ *   x fp16 [M][K], w rows = N, k = K, y fp16 [M][N].
+ * The E4M3 bytes convert to fp16 exactly; the channel scale multiplies the FP32 sum (the pages
+ * apply it before the MMA). The reduction order is the library's, so a batch is bitwise equal to
+ * single-row calls.
+ * Requirements: K % 128 == 0 and K <= 16384; N % 16 == 0; x, y, codes 16-byte aligned.
+ * --------------------------------------------------------------------------------------------- */
+int nvfp4_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights *w, uint16_t *y, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Gated form of the dense projection: the packed gate/up projection of a dense NVFP4 MLP with

@@ -32,7 +32,7 @@ def test_header_declares_the_expected_entry_points():
     assert declared() == sorted([
         "nvfp4_abi_version", "nvfp4_status_str", "nvfp4_moe_plan_bytes", "nvfp4_moe_plan", "nvfp4_moe_route",
         "nvfp4_moe_w13_swiglu", "nvfp4_moe_w2_workspace_bytes", "nvfp4_moe_w2_reduce", "nvfp4_linear",
-        "nvfp4_linear_swiglu"])
+        "nvfp4_linear_swiglu", "nvfp4_linear_fp8"])
 
 
 def test_library_exports_every_declared_function():
@@ -87,3 +87,11 @@ def test_argument_checks_fail_closed(L):
     assert L.nvfp4_linear_swiglu(fake, 4, C.byref(nvfp4_weights(fake, fake, fake, 1, 64, 32768)), 0, fake, null) == 5
     assert L.nvfp4_linear_swiglu(fake, 4, C.byref(nvfp4_weights(fake, fake, fake, 1, 64, 128)), 2, fake, null) == 2
     assert L.nvfp4_linear_swiglu(fake, 0, C.byref(nvfp4_weights(fake, fake, fake, 1, 64, 128)), 0, null, null) == 0
+    # channel-FP8 projection
+    from gemm_nvfp4_amd._lib import fp8_channel_weights as f8
+    assert L.nvfp4_linear_fp8(fake, 4, C.byref(f8(fake, fake, 64, 96)), fake, null) == 5     # K % 128
+    assert L.nvfp4_linear_fp8(fake, 4, C.byref(f8(fake, fake, 40, 128)), fake, null) == 5    # N % 16
+    assert L.nvfp4_linear_fp8(fake, 4, C.byref(f8(None, fake, 64, 128)), fake, null) == 1
+    assert L.nvfp4_linear_fp8(fake, 4, C.byref(f8(odd, fake, 64, 128)), fake, null) == 3
+    assert L.nvfp4_linear_fp8(fake, -1, C.byref(f8(fake, fake, 64, 128)), fake, null) == 2
+    assert L.nvfp4_linear_fp8(null, 0, C.byref(f8(fake, fake, 64, 128)), null, null) == 0
