@@ -256,6 +256,29 @@ def dense_timing(copies=64, launches=256):
     return res
 
 
+def fp8_timing(copies=40, launches=192):
+    """Channel-FP8 dense projection 4352 x 5120 (22.3 MB of E4M3 bytes + scales), µs per call in
+    graphs that rotate `copies` weight copies (about 0.9 GB)."""
+    import torch
+    import gemm_nvfp4_amd as G
+    from synth import inputs as S
+    N, Kd = S.DENSE_N, S.DENSE_K
+    ws = []
+    for c in range(copies):
+        codes, scale = S.fp8_channel_weights(S.rng_for(S.WORKLOAD_IDS["dense"], 700 + c, 0), N, Kd)
+        ws.append(G.FP8ChannelTensor.from_numpy((codes, scale)))
+    wbytes = N * Kd + N * 4
+    res = []
+    for M in (1, 16, 32):
+        x = torch.from_numpy(S.activations(S.rng_for(1, 0, 3000 + M), M, Kd)).cuda()
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        ms = time_graph(lambda: [G.nvfp4_linear_fp8(x, ws[i % copies], y=y) for i in range(launches)], launches)
+        us = ms * 1e3 / launches
+        res.append({"M": M, "us": round(us, 3), "weight_GBps": round(wbytes / (us * 1e-6) / 1e9, 1),
+                    "hbm_frac": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+    return res
+
+
 def mlp_timing(copies=48, launches=192):
     """Dense gated MLP shard (hidden 5120, 2176 intermediate columns): the gated gate/up projection
     (4352 x 5120 packed weights) and the down projection (5120 x 2176), µs per call in graphs that
@@ -371,6 +394,10 @@ def main():
     if not args.no_dense:
         dense = dense_timing()
         log(f"dense: {dense}")
+    fp8 = None
+    if not args.no_dense:
+        fp8 = fp8_timing()
+        log(f"dense channel-FP8: {fp8}")
     mlp = None
     if not args.no_mlp:
         mlp = mlp_timing()
@@ -398,7 +425,7 @@ def main():
                      "kernel": "w13_swiglu_stream_kernel<4, 1>", "us_per_launch": round(k_us, 3),
                      "algorithmic_bytes_per_launch": round(k_bytes)},
         "launch_floor_us": round(floor, 3),
-        "sweep": sweep, "prefill": prefill, "dense": dense, "mlp": mlp, "route": route, "cpu_baseline": cpu,
+        "sweep": sweep, "prefill": prefill, "dense": dense, "dense_fp8": fp8, "mlp": mlp, "route": route, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
