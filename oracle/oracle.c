@@ -144,6 +144,19 @@ void orc_linear(const uint16_t *x, int64_t M, int64_t K, const uint8_t *codes, c
     }
 }
 
+/* ---- shared expert gate --------------------------------------------------------------------
+ * The "shared gate" of the no-MTP page ("Scope and related PRs"; no formula is printed): the
+ * shared expert's output enters the MoE output scaled by sigmoid(x . g), g an fp16 vector [K].
+ *   sigma[m] = 1 / (1 + exp(-sum_k x[m][k] g[k])),  in double. */
+void orc_shared_gate(const uint16_t *x, int64_t M, int64_t K, const uint16_t *g, double *sigma)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        double z = 0.0;
+        for (int64_t k = 0; k < K; ++k) z += orc_half(x[m * K + k]) * orc_half(g[k]);
+        sigma[m] = 1.0 / (1.0 + exp(-z));
+    }
+}
+
 /* ---- channel-FP8 dense projection ---------------------------------------------------------
  * The channel-FP8 "QPN8" projection ("[SM70][Draft] Extend Qwen3.8 DFlash2 concurrency paths",
  * "Follow-up: exact channel-FP8 QPN8 concurrency paths and endpoint evidence"): weights are E4M3FN

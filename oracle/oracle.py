@@ -56,6 +56,8 @@ def lib():
                                      _vp, _vp, C.c_int])
         L.orc_linear_fp8.restype = None
         L.orc_linear_fp8.argtypes = [_vp, _i64, _i64, _vp, _vp, _i64, _vp, C.c_int]
+        L.orc_shared_gate.restype = None
+        L.orc_shared_gate.argtypes = [_vp, _i64, _i64, _vp, _vp]
         L.orc_route.restype = None
         L.orc_route.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp]
         L.orc_w2_reduce.restype = None
@@ -237,3 +239,24 @@ def linear_fp8(x16: np.ndarray, codes: np.ndarray, chscale: np.ndarray, nthreads
     lib().orc_linear_fp8(_p(xb), M, K, _p(np.ascontiguousarray(codes, dtype=np.uint8)),
                          _p(np.ascontiguousarray(chscale, dtype=np.float32)), N, _p(y), _threads(nthreads))
     return y
+
+
+def shared_gate(x16: np.ndarray, g16: np.ndarray) -> np.ndarray:
+    """orc_shared_gate: sigmoid(x @ g) per token, float64 [M]. x16 fp16 [M, K], g16 fp16 [K]."""
+    M, K = x16.shape
+    s = np.empty(M, np.float64)
+    lib().orc_shared_gate(_p(np.ascontiguousarray(x16).view(np.uint16)), M, K,
+                          _p(np.ascontiguousarray(g16, dtype=np.float16).view(np.uint16)), _p(s))
+    return s
+
+
+def moe_with_shared(case: dict, shared: dict, layout: int = 0, tokens=None, nthreads=None):
+    """The MoE output with the shared expert added: out[t] = sum_k w[t,k] y_k[t] + sigma[t] * y_s[t]
+    (routed part: orc_moe_token; shared expert: orc_gated_mlp on x with its own weights; gate:
+    orc_shared_gate). ``shared`` holds w13, w2 (NVFP4 tuples), layout and g (fp16 [K]). Returns
+    (out, y_s, sigma) for the selected tokens, float64."""
+    x = case["x"] if tokens is None else case["x"][np.asarray(tokens)]
+    out = moe_token(case, tokens=tokens, layout=layout, nthreads=nthreads)
+    _, ys = gated_mlp(x, shared["w13"], shared["w2"], shared.get("layout", 0), nthreads)
+    sg = shared_gate(x, shared["g"])
+    return out + sg[:, None] * ys, ys, sg

@@ -44,6 +44,7 @@ __all__ = [
     "active_experts",
     "router_logits",
     "fp8_channel_weights",
+    "shared_expert",
 ]
 
 # E4M3FN bytes of 2^u for integer u in [-8, -4]: 2^-8 and 2^-7 are E4M3 subnormals (0x02, 0x04),
@@ -239,3 +240,12 @@ def fp8_channel_weights(rng: np.random.Generator, rows: int, k: int):
     codes[codes == 0xFF] = 0xFE
     scale = np.exp2(rng.uniform(-6.0, -4.0, size=rows)).astype(np.float32)
     return codes, scale
+
+
+def shared_expert(rng: np.random.Generator, k: int, i: int, gscale: float = 1.0):
+    """A shared expert for a MoE layer of hidden size k: NVFP4 gate/up weights [2i, k], down weights
+    [k, i], and the fp16 shared-gate vector g [k] drawn N(0, 1/k) (so x . g is about N(0, 1))."""
+    w13 = nvfp4_weights(rng, 1, 2 * i, k, gscale=gscale)
+    w2 = nvfp4_weights(rng, 1, k, i, gscale=gscale)
+    g = (rng.standard_normal(k) / np.sqrt(k)).astype(np.float16)
+    return {"w13": w13, "w2": w2, "g": g, "layout": 0}
