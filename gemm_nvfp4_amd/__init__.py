@@ -17,8 +17,10 @@ from ._lib import (  # noqa: F401
     nvfp4_moe_plan,
     nvfp4_moe_plan_bytes,
     nvfp4_moe_route,
+    nvfp4_moe_shared_expert,
     nvfp4_moe_w13_swiglu,
     nvfp4_moe_w2_reduce,
+    nvfp4_moe_w2_reduce_shared,
     nvfp4_moe_w2_workspace_bytes,
     nvfp4_status_str,
     plan_fields,

@@ -48,6 +48,10 @@ _SIGS = {
     "nvfp4_moe_w2_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "nvfp4_moe_w2_reduce": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_linear": (C.c_int, [_vp, _i32, C.POINTER(nvfp4_weights), _vp, _vp]),
+    "nvfp4_moe_shared_expert": (C.c_int, [_vp, _i32, C.POINTER(nvfp4_weights), _i32, C.POINTER(nvfp4_weights), _vp,
+                                          _vp, _vp, _vp, _vp]),
+    "nvfp4_moe_w2_reduce_shared": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _vp, _vp, _vp,
+                                             _vp, _vp, _sz, _vp]),
     "nvfp4_linear_swiglu": (C.c_int, [_vp, _i32, C.POINTER(nvfp4_weights), _i32, _vp, _vp]),
     "nvfp4_linear_fp8": (C.c_int, [_vp, _i32, C.POINTER(fp8_channel_weights), _vp, _vp]),
 }
@@ -194,6 +198,43 @@ def nvfp4_moe_w2_reduce(plan: torch.Tensor, M: int, topk: int, E: int, h: torch.
         _dev(plan, "plan", torch.int32), M, topk, E, _dev(h, "h", torch.float16), C.byref(d),
         _dev(topk_weights, "topk_weights", torch.float32), _dev(out, "out", torch.float16),
         _dev(ws, "ws", ws.dtype), ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def nvfp4_moe_shared_expert(x: torch.Tensor, w13: NVFP4Tensor, w2: NVFP4Tensor, gate: torch.Tensor, layout: int = 0,
+                            h: torch.Tensor | None = None, shared_y: torch.Tensor | None = None,
+                            shared_sigma: torch.Tensor | None = None, stream=None):
+    """Shared expert on fp16 x [M, K]: returns (shared_y FP32 [M, K], shared_sigma FP32 [M], h fp16 [M, I])."""
+    M, K = x.shape
+    I = w13.rows // 2
+    dev = x.device
+    h = torch.empty((M, I), dtype=torch.float16, device=dev) if h is None else h
+    shared_y = torch.empty((M, K), dtype=torch.float32, device=dev) if shared_y is None else shared_y
+    shared_sigma = torch.empty((M,), dtype=torch.float32, device=dev) if shared_sigma is None else shared_sigma
+    d13, d2 = w13.desc(), w2.desc()
+    _check("nvfp4_moe_shared_expert", lib().nvfp4_moe_shared_expert(
+        _dev(x, "x", torch.float16), M, C.byref(d13), layout, C.byref(d2), _dev(gate, "gate", torch.float16),
+        _dev(h, "h", torch.float16), _dev(shared_y, "shared_y", torch.float32),
+        _dev(shared_sigma, "shared_sigma", torch.float32), _stream(stream)))
+    return shared_y, shared_sigma, h
+
+
+def nvfp4_moe_w2_reduce_shared(plan: torch.Tensor, M: int, topk: int, E: int, h: torch.Tensor, w2: NVFP4Tensor,
+                               topk_weights: torch.Tensor, shared_y: torch.Tensor, shared_sigma: torch.Tensor,
+                               out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                               stream=None) -> torch.Tensor:
+    """Grouped W2 + slot-order reduction with the shared expert added last. Returns out fp16 [M, K]."""
+    K = w2.rows
+    dev = h.device
+    out = torch.empty((M, K), dtype=torch.float16, device=dev) if out is None else out
+    if ws is None:
+        ws = torch.empty(max(nvfp4_moe_w2_workspace_bytes(M, topk, K), 256), dtype=torch.uint8, device=dev)
+    d = w2.desc()
+    _check("nvfp4_moe_w2_reduce_shared", lib().nvfp4_moe_w2_reduce_shared(
+        _dev(plan, "plan", torch.int32), M, topk, E, _dev(h, "h", torch.float16), C.byref(d),
+        _dev(topk_weights, "topk_weights", torch.float32), _dev(shared_y, "shared_y", torch.float32),
+        _dev(shared_sigma, "shared_sigma", torch.float32), _dev(out, "out", torch.float16), ws.data_ptr(), ws.numel(),
+        _stream(stream)))
     return out
 
 

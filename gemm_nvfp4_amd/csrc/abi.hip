@@ -107,9 +107,10 @@ NVFP4_API size_t nvfp4_moe_w2_workspace_bytes(int32_t M, int32_t topk, int32_t K
     return (b + 255) & ~(size_t)255;
 }
 
-NVFP4_API int nvfp4_moe_w2_reduce(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16_t *h,
-                                  const nvfp4_weights *w2, const float *topk_weights, uint16_t *out, void *ws,
-                                  size_t ws_bytes, void *stream)
+namespace {
+
+int w2_reduce(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16_t *h, const nvfp4_weights *w2,
+              const float *topk_weights, uint16_t *out, void *ws, size_t ws_bytes, void *stream, nvfp4::SharedTerm sh)
 {
     if (!plan_shape_ok(M, topk, E)) return NVFP4_ERR_SHAPE;
     if (E > nvfp4::MAX_EXPERTS) return NVFP4_ERR_UNSUPPORTED;
@@ -122,6 +123,7 @@ NVFP4_API int nvfp4_moe_w2_reduce(const void *plan, int32_t M, int32_t topk, int
     if (!plan || !h || !topk_weights || !out || !ws) return NVFP4_ERR_NULL;
     if (!aligned(plan, 16) || !aligned(h, 16) || !aligned(out, 16) || !aligned(ws, 16) || !aligned(topk_weights, 4))
         return NVFP4_ERR_ALIGN;
+    if (sh.y && (!aligned(sh.y, 16) || !aligned(sh.sigma, 4))) return NVFP4_ERR_ALIGN;
     if (ws_bytes < nvfp4_moe_w2_workspace_bytes(M, topk, K)) return NVFP4_ERR_WORKSPACE;
     const PlanLayout L = nvfp4::plan_layout(M, topk, E);
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -129,9 +131,54 @@ NVFP4_API int nvfp4_moe_w2_reduce(const void *plan, int32_t M, int32_t topk, int
     if (nvfp4::use_prefill(M, L.P, E, K, I)) {
         const int st = nvfp4::run_w2_prefill(pv, L.A, L.P, h, *w2, static_cast<float *>(ws), s);
         if (st != NVFP4_OK) return st;
-        return nvfp4::run_reduce(pv, M, topk, w2->rows, topk_weights, static_cast<const float *>(ws), out, s);
+        return nvfp4::run_reduce(pv, M, topk, w2->rows, topk_weights, static_cast<const float *>(ws), out, s, sh);
     }
-    return nvfp4::run_w2(pv, L.T, M, topk, h, *w2, topk_weights, out, static_cast<float *>(ws), s);
+    return nvfp4::run_w2(pv, L.T, M, topk, h, *w2, topk_weights, out, static_cast<float *>(ws), s, sh);
+}
+
+}  // namespace
+
+NVFP4_API int nvfp4_moe_w2_reduce(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16_t *h,
+                                  const nvfp4_weights *w2, const float *topk_weights, uint16_t *out, void *ws,
+                                  size_t ws_bytes, void *stream)
+{
+    return w2_reduce(plan, M, topk, E, h, w2, topk_weights, out, ws, ws_bytes, stream, {});
+}
+
+NVFP4_API int nvfp4_moe_w2_reduce_shared(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16_t *h,
+                                         const nvfp4_weights *w2, const float *topk_weights, const float *shared_y,
+                                         const float *shared_sigma, uint16_t *out, void *ws, size_t ws_bytes,
+                                         void *stream)
+{
+    if (M > 0 && (!shared_y || !shared_sigma)) return NVFP4_ERR_NULL;
+    nvfp4::SharedTerm sh;
+    sh.y = shared_y;
+    sh.sigma = shared_sigma;
+    return w2_reduce(plan, M, topk, E, h, w2, topk_weights, out, ws, ws_bytes, stream, sh);
+}
+
+NVFP4_API int nvfp4_moe_shared_expert(const uint16_t *x, int32_t M, const nvfp4_weights *w13, int32_t layout,
+                                      const nvfp4_weights *w2, const uint16_t *gate, uint16_t *h, float *shared_y,
+                                      float *shared_sigma, void *stream)
+{
+    if (M < 0 || (layout != 0 && layout != 1)) return NVFP4_ERR_SHAPE;
+    int st = check_weights(w13);
+    if (st == NVFP4_OK) st = check_weights(w2);
+    if (st != NVFP4_OK) return st;
+    const int K = w13->k, I = w13->rows / 2;
+    if (w13->groups != 1 || w2->groups != 1 || w13->rows % 2 != 0 || w2->rows != K || w2->k != I)
+        return NVFP4_ERR_SHAPE;
+    if (K % 128 != 0 || K > nvfp4::MAX_LINEAR_SWIGLU_K || I % 128 != 0 || I > nvfp4::MAX_LINEAR_K)
+        return NVFP4_ERR_UNSUPPORTED;
+    if (M == 0) return NVFP4_OK;
+    if (!x || !gate || !h || !shared_y || !shared_sigma) return NVFP4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(h, 16) || !aligned(shared_y, 16) || !aligned(gate, 2) || !aligned(shared_sigma, 4))
+        return NVFP4_ERR_ALIGN;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = nvfp4::run_linear_swiglu(x, M, *w13, layout, h, s);
+    if (st == NVFP4_OK) st = nvfp4::run_linear_f32(h, M, *w2, shared_y, s);
+    if (st == NVFP4_OK) st = nvfp4::run_shared_gate(x, M, K, gate, shared_sigma, s);
+    return st;
 }
 
 NVFP4_API int nvfp4_linear(const uint16_t *x, int32_t M, const nvfp4_weights *w, uint16_t *y, void *stream)

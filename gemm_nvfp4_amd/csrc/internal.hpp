@@ -98,8 +98,15 @@ int run_route(const float *logits, int32_t M, int32_t E, int32_t topk, int32_t *
               const PlanLayout &L, hipStream_t s);
 int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, const nvfp4_weights &w,
             int32_t layout, uint16_t *h, hipStream_t s);
+// The shared expert's contribution to the MoE output (both pointers NULL: none): FP32 y [M][K] and
+// the per-token gate sigma [M], added after the routed slots as one more fmaf.
+struct SharedTerm {
+    const float *y = nullptr;
+    const float *sigma = nullptr;
+};
+
 int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uint16_t *h, const nvfp4_weights &w,
-           const float *topk_weights, uint16_t *out, float *ws, hipStream_t s);
+           const float *topk_weights, uint16_t *out, float *ws, hipStream_t s, SharedTerm sh = {});
 int run_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, uint16_t *y, hipStream_t s);
 int run_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights &w, uint16_t *y, hipStream_t s);
 int run_linear_swiglu(const uint16_t *x, int32_t M, const nvfp4_weights &w, int32_t layout, uint16_t *h,
@@ -111,7 +118,9 @@ int run_w2_prefill(const PlanView &pv, int64_t a_max, int64_t P, const uint16_t 
 // The prefill kernels address x, h and one expert's weights with 32-bit byte offsets.
 bool prefill_offsets_fit(int64_t M, int64_t P, int32_t K, int32_t I);
 int run_reduce(const PlanView &pv, int32_t M, int32_t topk, int32_t K, const float *topk_weights, const float *ws,
-               uint16_t *out, hipStream_t s);
+               uint16_t *out, hipStream_t s, SharedTerm sh = {});
+int run_linear_f32(const uint16_t *x, int32_t M, const nvfp4_weights &w, float *y, hipStream_t s);
+int run_shared_gate(const uint16_t *x, int32_t M, int32_t K, const uint16_t *g, float *sigma, hipStream_t s);
 
 // Regime switch (performance only: every kernel uses the same reduction order, so results are
 // bitwise identical either way). The MFMA-tiled prefill kernels pay off once experts average at

@@ -31,12 +31,14 @@ constexpr int ROW_GROUP = 2;    // 16-row tiles of x handled per pass over the w
 // Each wave holds NW 16-row weight tiles. Plain (GATED false): tile t covers output columns
 // (nt*NW + t)*16 .. +15. Gated: tile 0 holds the gate rows and tile 1 the up rows of h columns
 // nt*16 .. +15 (layout 0: rows i and I + i; layout 1: rows 2i and 2i + 1).
-template <int NW, bool GATED>
+// OUT is the output type: fp16 (rounded once), or FP32 for a result that is summed further (the
+// shared expert's down projection, added into the MoE output before its one rounding).
+template <int NW, bool GATED, typename OUT = f16>
 __global__ __launch_bounds__(max_waves<NW>() * 64) void linear_kernel(const f16 *__restrict__ x, int M,
                                                                  const uint8_t *__restrict__ codes,
                                                                  const uint8_t *__restrict__ scales,
                                                                  const float *__restrict__ gscale, int N, int K,
-                                                                 int layout, f16 *__restrict__ y)
+                                                                 int layout, OUT *__restrict__ y)
 {
     extern __shared__ float part[];  // [S][ROW_GROUP][NW][16][LDS_ROW]
     const int nt = blockIdx.x;
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(max_waves<NW>() * 64) void linear_kernel(const f16 
                     y[(size_t)m * N + nt * 16 + cl] = (f16)swiglu(tot[0] * gs, tot[1] * gs);
                 } else {
 #pragma unroll
-                    for (int t = 0; t < NW; ++t) y[(size_t)m * N + (nt * NW + t) * 16 + cl] = (f16)(tot[t] * gs);
+                    for (int t = 0; t < NW; ++t) y[(size_t)m * N + (nt * NW + t) * 16 + cl] = (OUT)(tot[t] * gs);
                 }
             }
         }
@@ -258,22 +260,22 @@ int launch_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights &w
                   reinterpret_cast<const f16 *>(x), M, w.codes, w.channel_scale, N, K, reinterpret_cast<f16 *>(y));
 }
 
-template <int NW, bool GATED>
-int launch_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, int N, int layout, uint16_t *y, hipStream_t s)
+template <int NW, bool GATED, typename OUT = f16>
+int launch_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, int N, int layout, void *y, hipStream_t s)
 {
     const int K = w.k;
     const int S = num_chunks(K);
     const int waves = S < max_waves<NW>() ? S : max_waves<NW>();
     const size_t shmem = (size_t)S * ROW_GROUP * NW * 16 * LDS_ROW * sizeof(float);
     if (shmem > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(linear_kernel<NW, GATED>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(linear_kernel<NW, GATED, OUT>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
         if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
     }
     const int blocks = GATED ? N / 16 : N / (16 * NW);
-    return launch(linear_kernel<NW, GATED>, dim3((unsigned)blocks), dim3((unsigned)(waves * 64)), shmem, s,
+    return launch(linear_kernel<NW, GATED, OUT>, dim3((unsigned)blocks), dim3((unsigned)(waves * 64)), shmem, s,
                   reinterpret_cast<const f16 *>(x), M, w.codes, w.scales, w.global_scale, N, K, layout,
-                  reinterpret_cast<f16 *>(y));
+                  static_cast<OUT *>(y));
 }
 
 }  // namespace
@@ -285,6 +287,37 @@ int run_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, uint16_t *y
 #endif
     if (NVFP4_LINEAR_TILES == 2 && w.rows % 32 == 0) return launch_linear<2, false>(x, M, w, w.rows, 0, y, s);
     return launch_linear<1, false>(x, M, w, w.rows, 0, y, s);
+}
+
+int run_linear_f32(const uint16_t *x, int32_t M, const nvfp4_weights &w, float *y, hipStream_t s)
+{
+    if (w.rows % 32 == 0) return launch_linear<2, false, float>(x, M, w, w.rows, 0, y, s);
+    return launch_linear<1, false, float>(x, M, w, w.rows, 0, y, s);
+}
+
+// ---- shared-expert gate ---------------------------------------------------------------------------
+// sigma[m] = 1 / (1 + e^-z), z = sum_k x[m][k] g[k] (the "shared gate" of the "[Kernel][SM70] Improve
+// Qwen3.8 no-MTP concurrency" page, "Scope and related PRs"). One wave per token: each lane sums
+// its strided elements in FP32 in ascending order, then a fixed butterfly over the lanes, read
+// from lane 0, so the value never depends on the batch.
+__global__ __launch_bounds__(256) void shared_gate_kernel(const f16 *__restrict__ x, int M, int K,
+                                                          const f16 *__restrict__ g, float *__restrict__ sigma)
+{
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (m >= M) return;  // wave-uniform
+    const f16 *xr = x + (size_t)m * K;
+    float z = 0.0f;
+    for (int k = lane; k < K; k += 64) z = fmaf((float)xr[k], (float)g[k], z);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
+    z = __shfl(z, 0, 64);
+    if (lane == 0) sigma[m] = 1.0f / (1.0f + expf(-z));
+}
+
+int run_shared_gate(const uint16_t *x, int32_t M, int32_t K, const uint16_t *g, float *sigma, hipStream_t s)
+{
+    return launch(shared_gate_kernel, dim3((unsigned)(((int64_t)M + 3) / 4)), dim3(256), 0, s,
+                  reinterpret_cast<const f16 *>(x), M, K, reinterpret_cast<const f16 *>(g), sigma);
 }
 
 int run_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights &w, uint16_t *y, hipStream_t s)

@@ -350,7 +350,7 @@ __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, con
 // written and never used. Each thread owns 4 consecutive columns of one token.
 __global__ __launch_bounds__(256) void reduce_kernel(const int32_t *__restrict__ pos_of_pair, const float *__restrict__ tw,
                                                      const float *__restrict__ ws, int topk, int K, int blocks_per_token,
-                                                     f16 *__restrict__ out)
+                                                     SharedTerm sh, f16 *__restrict__ out)
 {
     const int t = blockIdx.x / blocks_per_token;
     const int nb = blockIdx.x - t * blocks_per_token;
@@ -383,6 +383,14 @@ __global__ __launch_bounds__(256) void reduce_kernel(const int32_t *__restrict__
             }
         }
     }
+    if (sh.y) {  // the shared expert, after the routed slots
+        const float g = sh.sigma[t];
+        const float4 v = *reinterpret_cast<const float4 *>(sh.y + (size_t)t * K + n);
+        s0 = fmaf(g, v.x, s0);
+        s1 = fmaf(g, v.y, s1);
+        s2 = fmaf(g, v.z, s2);
+        s3 = fmaf(g, v.w, s3);
+    }
     typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
     *reinterpret_cast<f16x4 *>(out + (size_t)t * K + n) = f16x4{(f16)s0, (f16)s1, (f16)s2, (f16)s3};
 }
@@ -400,7 +408,8 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
                                                           const uint8_t *__restrict__ codes,
                                                           const uint8_t *__restrict__ scales,
                                                           const float *__restrict__ gscale, int K, int I,
-                                                          const float *__restrict__ tw, f16 *__restrict__ out)
+                                                          const float *__restrict__ tw, SharedTerm sh,
+                                                          f16 *__restrict__ out)
 {
     __shared__ float yk[MAX_TOPK][16];
     __shared__ int s_row[MAX_TOPK], s_e[MAX_TOPK];
@@ -491,6 +500,7 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
         float acc = 0.f;
         for (int k = 0; k < topk; ++k)
             if (s_e[k] >= 0) acc = fmaf(s_w[k], yk[k][threadIdx.x], acc);
+        if (sh.y) acc = fmaf(sh.sigma[t], sh.y[(size_t)t * K + nt * 16 + threadIdx.x], acc);  // shared expert last
         out[(size_t)t * K + nt * 16 + threadIdx.x] = (f16)acc;
     }
 }
@@ -535,13 +545,13 @@ int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, 
 }
 
 int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uint16_t *h, const nvfp4_weights &w,
-           const float *topk_weights, uint16_t *out, float *ws, hipStream_t s)
+           const float *topk_weights, uint16_t *out, float *ws, hipStream_t s, SharedTerm sh)
 {
     const int K = w.rows, I = w.k;
     if (use_token_w2((int64_t)M * topk, w.groups)) {
         const int64_t G = (int64_t)M * (K / 16);
         return launch(w2_token_kernel, dim3((unsigned)((G + 7) / 8 * 8)), dim3(256), 0, s, pv, M, topk,
-                      reinterpret_cast<const f16 *>(h), w.codes, w.scales, w.global_scale, K, I, topk_weights,
+                      reinterpret_cast<const f16 *>(h), w.codes, w.scales, w.global_scale, K, I, topk_weights, sh,
                       reinterpret_cast<f16 *>(out));
     }
     const int split = split_for(I);
@@ -556,15 +566,15 @@ int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uin
     default: st = launch(w2_stream_kernel<4, W2_TP>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws); break;
     }
     if (st != NVFP4_OK) return st;
-    return run_reduce(pv, M, topk, K, topk_weights, ws, out, s);
+    return run_reduce(pv, M, topk, K, topk_weights, ws, out, s, sh);
 }
 
 int run_reduce(const PlanView &pv, int32_t M, int32_t topk, int32_t K, const float *topk_weights, const float *ws,
-               uint16_t *out, hipStream_t s)
+               uint16_t *out, hipStream_t s, SharedTerm sh)
 {
     const int bpt = (K / 4 + 255) / 256;
     return launch(reduce_kernel, dim3((unsigned)((int64_t)M * bpt)), dim3(256), 0, s, pv.pos_of_pair, topk_weights,
-                  ws, topk, K, bpt, reinterpret_cast<f16 *>(out));
+                  ws, topk, K, bpt, sh, reinterpret_cast<f16 *>(out));
 }
 
 }  // namespace nvfp4

@@ -170,6 +170,26 @@ int nvfp4_moe_w2_reduce(const void *plan, int32_t M, int32_t topk, int32_t E,
                         uint16_t *out, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Shared expert and shared gate (the "shared gate" among the fused MoE parts, no-MTP page, "Scope
+ * and related PRs"; no formula is printed, so this is the plain reading): a dense NVFP4 gated MLP
+ * on every token, scaled by sigmoid(x . g) and added to the routed output.
+ *   nvfp4_moe_shared_expert: x fp16 [M][K]; w13 groups = 1, rows = 2I, k = K (layouts as for
+ *     nvfp4_linear_swiglu); w2 groups = 1, rows = K, k = I; gate fp16 [K];
+ *     h fp16 [M][I] (scratch, the gated MLP's h), shared_y FP32 [M][K] = W2 h (unrounded, global
+ *     scale applied), shared_sigma FP32 [M] = 1 / (1 + exp(-sum_k x[m][k] gate[k])).
+ *     Requirements: K % 128 == 0, K <= 16384, I % 128 == 0; x, h, shared_y 16-byte aligned.
+ *   nvfp4_moe_w2_reduce_shared: nvfp4_moe_w2_reduce with the shared expert as one more slot after
+ *     the routed ones: s = (routed fmaf chain); s = fmaf(shared_sigma[t], shared_y[t][n], s);
+ *     out = fp16_rne(s). shared_y 16-byte aligned.
+ * --------------------------------------------------------------------------------------------- */
+int nvfp4_moe_shared_expert(const uint16_t *x, int32_t M, const nvfp4_weights *w13, int32_t layout,
+                            const nvfp4_weights *w2, const uint16_t *gate, uint16_t *h, float *shared_y,
+                            float *shared_sigma, void *stream);
+int nvfp4_moe_w2_reduce_shared(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16_t *h,
+                               const nvfp4_weights *w2, const float *topk_weights, const float *shared_y,
+                               const float *shared_sigma, uint16_t *out, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Dense NVFP4 projection (the "QPN" projection, DFlash2 page, "Purpose" and "TP4-only NVFP4
  * verifier follow-up"):
  *   y[m][n] = fp16_rne( global * sum_k x[m][k] * e2m1*e4m3 ),  FP32 accumulation.

@@ -32,7 +32,7 @@ def test_header_declares_the_expected_entry_points():
     assert declared() == sorted([
         "nvfp4_abi_version", "nvfp4_status_str", "nvfp4_moe_plan_bytes", "nvfp4_moe_plan", "nvfp4_moe_route",
         "nvfp4_moe_w13_swiglu", "nvfp4_moe_w2_workspace_bytes", "nvfp4_moe_w2_reduce", "nvfp4_linear",
-        "nvfp4_linear_swiglu", "nvfp4_linear_fp8"])
+        "nvfp4_linear_swiglu", "nvfp4_linear_fp8", "nvfp4_moe_shared_expert", "nvfp4_moe_w2_reduce_shared"])
 
 
 def test_library_exports_every_declared_function():
@@ -87,6 +87,17 @@ def test_argument_checks_fail_closed(L):
     assert L.nvfp4_linear_swiglu(fake, 4, C.byref(nvfp4_weights(fake, fake, fake, 1, 64, 32768)), 0, fake, null) == 5
     assert L.nvfp4_linear_swiglu(fake, 4, C.byref(nvfp4_weights(fake, fake, fake, 1, 64, 128)), 2, fake, null) == 2
     assert L.nvfp4_linear_swiglu(fake, 0, C.byref(nvfp4_weights(fake, fake, fake, 1, 64, 128)), 0, null, null) == 0
+    # shared expert: w2 must be [K][I] for w13 [2I][K]; I % 128
+    w13 = nvfp4_weights(fake, fake, fake, 1, 256, 256)
+    assert L.nvfp4_moe_shared_expert(fake, 4, C.byref(w13), 0, C.byref(nvfp4_weights(fake, fake, fake, 1, 256, 64)),
+                                     fake, fake, fake, fake, null) == 2
+    assert L.nvfp4_moe_shared_expert(fake, 4, C.byref(w13), 0, C.byref(nvfp4_weights(fake, fake, fake, 1, 256, 128)),
+                                     null, fake, fake, fake, null) == 1
+    w13b = nvfp4_weights(fake, fake, fake, 1, 128, 256)  # I = 64: not a multiple of 128
+    assert L.nvfp4_moe_shared_expert(fake, 4, C.byref(w13b), 0, C.byref(nvfp4_weights(fake, fake, fake, 1, 256, 64)),
+                                     fake, fake, fake, fake, null) == 5
+    assert L.nvfp4_moe_w2_reduce_shared(fake, 4, 2, 8, fake, C.byref(nvfp4_weights(fake, fake, fake, 8, 256, 128)),
+                                        fake, null, fake, fake, fake, 1 << 20, null) == 1
     # channel-FP8 projection
     from gemm_nvfp4_amd._lib import fp8_channel_weights as f8
     assert L.nvfp4_linear_fp8(fake, 4, C.byref(f8(fake, fake, 64, 96)), fake, null) == 5     # K % 128

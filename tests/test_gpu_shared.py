@@ -1,0 +1,86 @@
+"""GPU parity of the shared expert and shared gate against the fp64 oracle ("shared gate" among
+the fused MoE parts of the "[Kernel][SM70] Improve Qwen3.8 no-MTP concurrency" page, "Scope and
+related PRs"; reading: out = routed + sigmoid(x . g) * shared MLP(x), the shared term added after
+the routed slots, one fp16 rounding).
+
+Covers the shared expert's FP32 output and gate, the MoE output with the shared term in all three
+W2 regimes (token-major, expert-major streaming, MFMA-tiled prefill), batch invariance, and that a
+zero shared term leaves the routed output bitwise unchanged.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gemm_nvfp4_amd as G
+from synth import inputs as S
+from tests.parity import assert_rows_close, dev_moe, run_moe, to_np64
+
+pytestmark = pytest.mark.gpu
+
+
+def _shared_dev(shared):
+    return (G.NVFP4Tensor.from_numpy(shared["w13"]), G.NVFP4Tensor.from_numpy(shared["w2"]),
+            torch.from_numpy(shared["g"]).cuda())
+
+
+def _run(case, shared, d=None):
+    sh = case["shape"]
+    res = run_moe(case, dev=d)  # plan, h (W13) and the routed-only output
+    d = res["dev"]
+    w13s, w2s, g = _shared_dev(shared)
+    ys, sg, _ = G.nvfp4_moe_shared_expert(d["x"], w13s, w2s, g)
+    out = G.nvfp4_moe_w2_reduce_shared(res["plan"], sh.m, sh.topk, sh.e, res["h"], d["w2"], d["tw"], ys, sg)
+    torch.cuda.synchronize()
+    return out, ys, sg, res
+
+
+def test_shared_expert_outputs(orc):
+    rng = S.rng_for(S.WORKLOAD_IDS["decode"], 50, 0)
+    shared = S.shared_expert(rng, 2048, 512)
+    x = S.activations(rng, 16, 2048)
+    w13s, w2s, g = _shared_dev(shared)
+    ys, sg, _ = G.nvfp4_moe_shared_expert(torch.from_numpy(x).cuda(), w13s, w2s, g)
+    torch.cuda.synchronize()
+    _, ys_ref = orc.gated_mlp(x, shared["w13"], shared["w2"])
+    sg_ref = orc.shared_gate(x, shared["g"])
+    assert_rows_close(ys.cpu().numpy().astype(np.float64), ys_ref, "shared y")
+    assert np.all(np.abs(sg.cpu().numpy() - sg_ref) <= 1e-6 + 1e-5 * sg_ref)
+
+
+@pytest.mark.parametrize("shape,routing", [
+    (S.MoEShape(m=5, e=512, topk=10, k=2048, i=512), "uniform"),      # token-major W2 (P <= E/4)
+    (S.DECODE, "uniform"),                                             # expert-major streaming W2
+    (S.MoEShape(m=600, e=8, topk=2, k=512, i=128), "repeat_invalid"),  # MFMA-tiled prefill W2
+])
+def test_moe_with_shared_matches_oracle(orc, shape, routing):
+    case = S.moe_case(shape, routing=routing, route_pattern=31)
+    shared = S.shared_expert(S.rng_for(S.WORKLOAD_IDS["decode"], 51, shape.m), shape.k, 256)
+    out, _, _, _ = _run(case, shared)
+    tokens = None if shape.m <= 16 else np.arange(0, shape.m, 37, dtype=np.int32)
+    ref, _, _ = orc.moe_with_shared(case, shared, tokens=tokens)
+    got = to_np64(out) if tokens is None else to_np64(out)[tokens]
+    assert_rows_close(got, ref, f"moe+shared m={shape.m}")
+
+
+def test_moe_with_shared_batch_invariance():
+    case = S.moe_case(S.DECODE, route_pattern=32)
+    shared = S.shared_expert(S.rng_for(S.WORKLOAD_IDS["decode"], 52, 0), S.DECODE.k, 256)
+    out, _, _, res = _run(case, shared)
+    for t in (0, 7, 15):
+        one = dict(case)
+        one["shape"] = S.MoEShape(m=1, e=S.DECODE.e, topk=S.DECODE.topk, k=S.DECODE.k, i=S.DECODE.i)
+        one["x"], one["ids"], one["topk_weights"] = case["x"][t:t + 1], case["ids"][t:t + 1], case["topk_weights"][t:t + 1]
+        o1, _, _, _ = _run(one, shared)
+        assert torch.equal(o1[0].view(torch.int16), out[t].view(torch.int16)), t
+
+
+def test_zero_shared_term_is_the_routed_output():
+    case = S.moe_case(S.DECODE, route_pattern=33)
+    res = run_moe(case)
+    sh = S.DECODE
+    zeros_y = torch.zeros((sh.m, sh.k), dtype=torch.float32, device="cuda")
+    zeros_s = torch.zeros((sh.m,), dtype=torch.float32, device="cuda")
+    d = res["dev"]
+    out = G.nvfp4_moe_w2_reduce_shared(res["plan"], sh.m, sh.topk, sh.e, res["h"], d["w2"], d["tw"], zeros_y, zeros_s)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), res["out"].view(torch.int16))
