@@ -256,6 +256,50 @@ def dense_timing(copies=64, launches=256):
     return res
 
 
+def shared_layer_timing(steps, W13, W2, routes, i_shared=512):
+    """The 16-token decode layer with a shared expert (K=2048, 512 intermediate columns) and its gate:
+    plan, W13, shared expert, W2 with the shared term. Weight sets rotate as in the headline; the
+    shared expert rotates over as many copies."""
+    import torch
+    import gemm_nvfp4_amd as G
+    from synth import inputs as S
+    R, P, M = len(W13), len(routes.x), 16
+    sw13 = [G.NVFP4Tensor(*S.device_nvfp4_weights(8000 + r, 1, 2 * i_shared, K)) for r in range(R)]
+    sw2 = [G.NVFP4Tensor(*S.device_nvfp4_weights(8500 + r, 1, K, i_shared)) for r in range(R)]
+    g = torch.from_numpy((np.random.default_rng(3).standard_normal(K) / np.sqrt(K)).astype(np.float16)).cuda()
+    layer = G.MoELayer(M, TOPK, W13[0], W2[0])
+    hs = torch.empty((M, i_shared), dtype=torch.float16, device="cuda")
+    ys = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    sg = torch.empty((M,), dtype=torch.float32, device="cuda")
+
+    side = torch.cuda.Stream()  # default priority
+
+    def step(i, overlap):
+        p, r = i % P, i % R
+        cur = torch.cuda.current_stream()
+        if overlap:  # the shared expert depends on x only: run it beside plan + W13
+            side.wait_stream(cur)
+            with torch.cuda.stream(side):
+                G.nvfp4_moe_shared_expert(routes.x[p], sw13[r], sw2[r], g, h=hs, shared_y=ys, shared_sigma=sg,
+                                          stream=side)
+        else:
+            G.nvfp4_moe_shared_expert(routes.x[p], sw13[r], sw2[r], g, h=hs, shared_y=ys, shared_sigma=sg)
+        G.nvfp4_moe_plan(routes.ids[p], E, plan=layer.plan)
+        G.nvfp4_moe_w13_swiglu(layer.plan, M, TOPK, E, routes.x[p], W13[r], 0, h=layer.h)
+        if overlap:
+            cur.wait_stream(side)
+        G.nvfp4_moe_w2_reduce_shared(layer.plan, M, TOPK, E, layer.h, W2[r], routes.tw[p], ys, sg, out=layer.out,
+                                     ws=layer.ws)
+
+    wbytes = sum(routes.active[i % P] * EXPERT_BYTES + 3 * i_shared * K * 9 // 16 for i in range(steps))
+    res = {"M": M, "shared_intermediate": i_shared}
+    for name, ov in (("serial", False), ("overlapped", True)):
+        ms = time_graph(lambda: [step(i, ov) for i in range(steps)], steps, lambda: [step(i, ov) for i in range(8)])
+        res[f"us_per_layer_{name}"] = round(ms * 1e3 / steps, 3)
+        res[f"weight_GBps_{name}"] = round(wbytes / (ms * 1e-3) / 1e9, 1)
+    return res
+
+
 def fp8_timing(copies=40, launches=192):
     """Channel-FP8 dense projection 4352 x 5120 (22.3 MB of E4M3 bytes + scales), µs per call in
     graphs that rotate `copies` weight copies (about 0.9 GB)."""
@@ -380,6 +424,9 @@ def main():
     floor = launch_floor()
     log(f"graph launch floor: {floor:.3f} us")
 
+    shared = shared_layer_timing(args.steps, W13, W2, routes16)
+    log(f"layer with shared expert: {shared}")
+
     sweep = []
     if not args.no_sweep:
         for M in (1, 2, 4, 8, 16):
@@ -425,7 +472,7 @@ def main():
                      "kernel": "w13_swiglu_stream_kernel<4, 1>", "us_per_launch": round(k_us, 3),
                      "algorithmic_bytes_per_launch": round(k_bytes)},
         "launch_floor_us": round(floor, 3),
-        "sweep": sweep, "prefill": prefill, "dense": dense, "dense_fp8": fp8, "mlp": mlp, "route": route, "cpu_baseline": cpu,
+        "sweep": sweep, "prefill": prefill, "dense": dense, "dense_fp8": fp8, "mlp": mlp, "with_shared_expert": shared, "route": route, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
