@@ -38,9 +38,8 @@ constexpr int PF_T = 4;                 // weight tiles per wave
 constexpr int AQ = 32;                  // elements of one lane group per quarter chunk (one step group)
 constexpr int A_ROW = 4 * AQ + 8;       // staged quarter per row: 4 lane groups + 16 bytes of bank padding
 constexpr int NBUF = 3;                 // ring of quarter buffers
-constexpr int PPT = PF_ROWS * 16 / 256; // 16-byte pieces of a staged quarter per thread
 #ifndef NVFP4_W2S1_R
-#define NVFP4_W2S1_R 6
+#define NVFP4_W2S1_R 5
 #endif
 constexpr int W2S1_R = NVFP4_W2S1_R;   // row tiles per pass of the one-chunk W2 kernel
 
@@ -79,8 +78,28 @@ __device__ __forceinline__ int xcd_logical_block(int G)
     return logical < G ? logical : -1;
 }
 
+// Eight E2M1 codes (one dword, element order) -> four unscaled fp16 pairs.
+__device__ __forceinline__ void e2m1_pairs(f16x2 (&o)[4], uint32_t codes)
+{
+    o[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
+    o[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
+    o[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
+    o[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3);
+}
+
+// Four unscaled pairs times one block scale -> eight exact fp16 weights: the same products as
+// decode8, formed from converts issued earlier.
+__device__ __forceinline__ f16x8 scale8(const f16x2 (&p)[4], f16 scale)
+{
+    const f16x2 s2 = {scale, scale};
+    const f16x2 p0 = p[0] * s2, p1 = p[1] * s2, p2 = p[2] * s2, p3 = p[3] * s2;
+    return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// One thread's 16-byte pieces of a staged quarter: one per row tile of the pass.
+template <int NR>
 struct StageRegs {
-    u32x4 v[PPT];
+    u32x4 v[NR];
 };
 
 // Scheduling hints for one MFMA step (row tile outer, weight tile inner): each MFMA is followed by
@@ -112,8 +131,10 @@ struct PassSrc {
 // j = 4b + s from +0, every accumulator seeing its steps in ascending order.
 //
 // Software pipeline, per wave:
-//   * MFMA steps: while step j's NR x 4 MFMAs run, the B fragments of step j + 1 are decoded
-//     from packed registers, and as soon as a row tile's four MFMAs have issued, its A fragment
+//   * MFMA steps: while step j's NR x 4 MFMAs run, the B fragments of step j + 1 are scaled and
+//     the codes of step j + 2 converted (two independent halves of the decode: a convert followed
+//     at once by the multiply that reads it stalls the in-order issue, measured at about 1.8 us
+//     per 80-row chunk on MI355X), and as soon as a row tile's four MFMAs have issued, its A fragment
 //     for step j + 1 is read from LDS. Each B fragment feeds NR MFMAs and each A fragment feeds 4.
 //   * Activations move through LDS a quarter chunk at a time (quarter g = 4c + b: lane group q's
 //     32 elements of step group b, for every row), in a ring of three buffers. Quarter g + 2 is
@@ -139,25 +160,25 @@ __device__ __forceinline__ void pass_chunks(PrefillShared &sh, const PassSrc &sr
 {
     const int red = src.red, S = num_chunks(red), G = 4 * S;
     const int qs = (threadIdx.x >> 2) & 3, ps = threadIdx.x & 3, srow = threadIdx.x >> 4;  // staged piece
-    uint32_t vo[PPT];
+    uint32_t vo[NR];
 #pragma unroll
-    for (int i = 0; i < PPT; ++i) {
+    for (int i = 0; i < NR; ++i) {
         const int r = srow + 16 * i;
         vo[i] = (uint32_t)sh.arow[r < rows ? r : 0] * src.row_bytes + 256 * qs + 16 * ps;
     }
     auto groups_of = [&](int c) { return min(KCHUNK, red - c * KCHUNK) >> 7; };
-    auto stage_load = [&](StageRegs &st, int g) {
+    // Lane groups past a short chunk's end stage zeros: their loads get an offset of at least 2^31,
+    // out of range of every buffer here (all are smaller than 2^31 bytes), and read as zero.
+    auto stage_load = [&](StageRegs<NR> &st, int g) {
         g = g < G ? g : G - 1;  // quarters past the end re-read the last one; they are never used
         const uint32_t so = (uint32_t)((g >> 2) * KCHUNK + AQ * (g & 3)) * 2;
+        const uint32_t oob = qs < groups_of(g >> 2) ? 0u : 0x80000000u;
 #pragma unroll
-        for (int i = 0; i < PPT; ++i) st.v[i] = bload16(src.act, vo[i], so);
+        for (int i = 0; i < NR; ++i) st.v[i] = bload16(src.act, vo[i] | oob, so);
     };
-    auto stage_store = [&](const StageRegs &st, int buf, int g) {
-        g = g < G ? g : G - 1;
-        const bool ok = qs < groups_of(g >> 2);
+    auto stage_store = [&](const StageRegs<NR> &st, int buf) {
 #pragma unroll
-        for (int i = 0; i < PPT; ++i)
-            *reinterpret_cast<u32x4 *>(&sh.a[buf][srow + 16 * i][AQ * qs + 8 * ps]) = ok ? st.v[i] : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < NR; ++i) *reinterpret_cast<u32x4 *>(&sh.a[buf][srow + 16 * i][AQ * qs + 8 * ps]) = st.v[i];
     };
     RawChunk w[PF_T];
     auto load_quarter = [&](int c, int b) {
@@ -170,34 +191,50 @@ __device__ __forceinline__ void pass_chunks(PrefillShared &sh, const PassSrc &sr
     };
     auto buf_next = [](int x) { return x == NBUF - 1 ? 0 : x + 1; };
 
-    StageRegs st;
+    StageRegs<NR> st;
     // Prologue: quarters 0 and 1 in LDS, chunk 0's weights in registers.
     stage_load(st, 0);
-    stage_store(st, 0, 0);
+    stage_store(st, 0);
     stage_load(st, 1);
 #pragma unroll
     for (int b = 0; b < 4; ++b) load_quarter(0, b);
-    stage_store(st, 1, 1);
+    stage_store(st, 1);
     lds_barrier();
 
     f32x4 tot[PF_R][PF_T], ca[PF_R][PF_T];
     f16x8 bf[2][PF_T], av[NR];
+    f16x2 raw[PF_T][4];
     f16x2 sc[PF_T];
     int cur = 0;  // LDS buffer of the current quarter
-    // B fragments of step (b, s) of chunk c into pipeline slot `slot`.
-    auto decode = [&](int slot, int c, int b, int s) {
+    // B decode in two stages, so that no VALU op waits on the one just before it:
+    //   cvt_step: E2M1 codes of step (b, s) -> unscaled fp16 pairs in raw (two steps ahead);
+    //   mul_step: raw times the block scale -> B fragments of step (b, s) of chunk c in bf[slot]
+    //             (one step ahead). Each step runs mul_step before cvt_step overwrites raw.
+    auto cvt_step = [&](int b, int s) {
+#pragma unroll
+        for (int t = 0; t < PF_T; ++t) e2m1_pairs(raw[t], w[t].codes[b][s]);
+    };
+    auto mul_step = [&](int slot, int c, int b, int s) {
         if (s == 0) {
             const bool qv = q < groups_of(c < S ? c : S - 1);
 #pragma unroll
             for (int t = 0; t < PF_T; ++t) sc[t] = qv ? chunk_scales(w[t], b) : f16x2{0, 0};
         }
 #pragma unroll
-        for (int t = 0; t < PF_T; ++t) bf[slot][t] = decode8(w[t].codes[b][s], sc[t][s >> 1]);
+        for (int t = 0; t < PF_T; ++t) bf[slot][t] = scale8(raw[t], sc[t][s >> 1]);
     };
     auto a_read = [&](int r, int s, int buf) {
         return *reinterpret_cast<const f16x8 *>(&sh.a[buf][16 * r + n][AQ * q + 8 * s]);
     };
-    decode(0, 0, 0, 0);
+    // The chunk sum starts from +0: +0 + c0 is c0 bitwise, because a chain that starts from +0
+    // never ends in -0 (x + y is -0 only when both are -0).
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int t = 0; t < PF_T; ++t) tot[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    cvt_step(0, 0);
+    mul_step(0, 0, 0, 0);
+    cvt_step(0, 1);
 #pragma unroll
     for (int r = 0; r < NR; ++r) av[r] = a_read(r, 0, 0);
     for (int c = 0; c < S; ++c) {
@@ -205,11 +242,12 @@ __device__ __forceinline__ void pass_chunks(PrefillShared &sh, const PassSrc &sr
         for (int j = 0; j < 16; ++j) {
             const int b = j >> 2, s = j & 3, g = 4 * c + b, slot = j & 1;
             if (s == 0) stage_load(st, g + 2);
-            // Operands of step j + 1. The last step's successor is the next chunk's first step:
-            // quarter g + 1, already in LDS (after the last chunk this reads a stale buffer and the
-            // refilled registers; never used).
+            // Operands of steps j + 1 (scaled) and j + 2 (converted). Steps past 15 belong to the
+            // next chunk: quarter 0 of its codes is already refilled and quarter g + 1 is already
+            // in LDS (after the last chunk they are stale or refilled; never used).
             const int sn = (j + 1) & 3, bn = ((j + 1) >> 2) & 3, bufn = s == 3 ? buf_next(cur) : cur;
-            decode(slot ^ 1, j < 15 ? c : c + 1, bn, sn);
+            mul_step(slot ^ 1, j < 15 ? c : c + 1, bn, sn);
+            cvt_step(((j + 2) >> 2) & 3, (j + 2) & 3);
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
 #pragma unroll
@@ -222,7 +260,7 @@ __device__ __forceinline__ void pass_chunks(PrefillShared &sh, const PassSrc &sr
             if (s == 3) {
                 // Quarter b of this chunk is fully decoded: refill it with the next chunk's bytes.
                 load_quarter(c + 1, b);
-                stage_store(st, buf_next(buf_next(cur)), g + 2);
+                stage_store(st, buf_next(buf_next(cur)));
                 lds_barrier();
                 cur = buf_next(cur);
                 __builtin_amdgcn_sched_barrier(0);
@@ -231,7 +269,7 @@ __device__ __forceinline__ void pass_chunks(PrefillShared &sh, const PassSrc &sr
 #pragma unroll
         for (int r = 0; r < NR; ++r)
 #pragma unroll
-            for (int t = 0; t < PF_T; ++t) tot[r][t] = c == 0 ? ca[r][t] : tot[r][t] + ca[r][t];
+            for (int t = 0; t < PF_T; ++t) tot[r][t] += ca[r][t];
     }
     if (working) epi(tot, NR);
 }
@@ -427,7 +465,9 @@ __global__ __launch_bounds__(256, 1) void w2_prefill_s1_kernel(PlanView pv, cons
     }
 
     const int qs = (threadIdx.x >> 2) & 3, ps = threadIdx.x & 3, srow = threadIdx.x >> 4;
-    const bool qs_ok = qs < groups;
+    // Lane groups past the end of a short chunk (I < 512) stage zeros: an offset of at least 2^31
+    // is out of range of every buffer here (all are smaller than 2^31 bytes) and reads as zero.
+    const uint32_t oob = qs < groups ? 0u : 0x80000000u;
     struct Stage {
         u32x4 v[PIECES];
     };
@@ -437,13 +477,12 @@ __global__ __launch_bounds__(256, 1) void w2_prefill_s1_kernel(PlanView pv, cons
 #pragma unroll
         for (int i = 0; i < PIECES; ++i) {
             const int row = base + min(r0 + srow + 16 * i, cnt - 1);
-            st.v[i] = bload16(act, (uint32_t)row * (uint32_t)(I * 2) + 256 * (qs_ok ? qs : 0) + 16 * ps, AQ * 2 * (g & 3));
+            st.v[i] = bload16(act, ((uint32_t)row * (uint32_t)(I * 2) + 256 * qs + 16 * ps) | oob, AQ * 2 * (g & 3));
         }
     };
     auto stage_store = [&](const Stage &st, int buf) {
 #pragma unroll
-        for (int i = 0; i < PIECES; ++i)
-            *reinterpret_cast<u32x4 *>(&sh.a[buf][srow + 16 * i][AQ * qs + 8 * ps]) = qs_ok ? st.v[i] : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < PIECES; ++i) *reinterpret_cast<u32x4 *>(&sh.a[buf][srow + 16 * i][AQ * qs + 8 * ps]) = st.v[i];
     };
     auto pairs_load = [&](int p) {  // pair indices of pass p's rows, one per thread
         const int r = p * ROWS + (int)threadIdx.x;
@@ -469,15 +508,23 @@ __global__ __launch_bounds__(256, 1) void w2_prefill_s1_kernel(PlanView pv, cons
         for (int b = 0; b < 4; ++b) sc[t][b] = qv ? chunk_scales(w[t], b) : f16x2{0, 0};
     f32x4 ca[NR][PF_T];
     f16x8 bf[2][PF_T], av[NR];
-    auto decode = [&](int slot, int b, int s) {
+    f16x2 raw[PF_T][4];
+    // B decode in two stages, as in pass_chunks: converts two steps ahead, scaling one step ahead.
+    auto cvt_step = [&](int b, int s) {
 #pragma unroll
-        for (int t = 0; t < PF_T; ++t) bf[slot][t] = decode8(w[t].codes[b][s], sc[t][b][s >> 1]);
+        for (int t = 0; t < PF_T; ++t) e2m1_pairs(raw[t], w[t].codes[b][s]);
+    };
+    auto mul_step = [&](int slot, int b, int s) {
+#pragma unroll
+        for (int t = 0; t < PF_T; ++t) bf[slot][t] = scale8(raw[t], sc[t][b][s >> 1]);
     };
     auto a_read = [&](int r, int s, int buf) {
         return *reinterpret_cast<const f16x8 *>(&sh.a[buf][16 * r + n][AQ * q + 8 * s]);
     };
     int cur = 0;
-    decode(0, 0, 0);
+    cvt_step(0, 0);
+    mul_step(0, 0, 0);
+    cvt_step(0, 1);
 #pragma unroll
     for (int r = 0; r < NR; ++r) av[r] = a_read(r, 0, 0);
     for (int p = 0; p < npass; ++p) {
@@ -488,7 +535,8 @@ __global__ __launch_bounds__(256, 1) void w2_prefill_s1_kernel(PlanView pv, cons
             if (s == 0) stage_load(st[(b + 1) & 1], g + 3);
             if (j == 4) pr_next = pairs_load(p + 1);
             const int sn = (j + 1) & 3, bn = ((j + 1) >> 2) & 3, bufn = s == 3 ? buf_next(cur) : cur;
-            decode(slot ^ 1, bn, sn);
+            mul_step(slot ^ 1, bn, sn);  // steps past 15: the next pass, same weights
+            cvt_step(((j + 2) >> 2) & 3, (j + 2) & 3);
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
 #pragma unroll
