@@ -9,10 +9,10 @@
 // MI355X that works best with many resident waves each holding one unit's loads (measured: deeper
 // per-wave prefetch lowers the achieved read rate). gfx950 design:
 //   * Work unit: (row tile of the plan, a group of 16-row weight tiles). A row tile has at most
-//     16 bucket rows (pairs) of one expert. Units are numbered tile-major and cut into equal
-//     contiguous ranges, one per persistent block (three 256-thread blocks per CU, at most 168
-//     VGPRs per lane, so 12 waves per CU). Blocks past the device-side unit count leave at once,
-//     so no device-to-host read is ever needed.
+//     16 bucket rows (pairs) of one expert. Units are numbered tile-major and cut into contiguous
+//     ranges, one per persistent block (W13: two 256-thread blocks per CU; W2: one), weighted so
+//     that blocks that start late get fewer units (unit_range). Blocks past the device-side unit
+//     count leave at once, so no device-to-host read is ever needed.
 //   * Block start: the block stages its range's tile descriptors from the plan (expert, rows, first
 //     bucket row, activation row of each row) in LDS: one load after the tile count.
 //   * Inside a block the four waves split the reduction axis into its 512-element chunks
@@ -48,10 +48,34 @@ struct TileStage {
 };
 
 // Contiguous unit range of this block out of U units; returns false if empty.
-__device__ __forceinline__ bool unit_range(int64_t U, int64_t &u0, int64_t &u1)
+//
+// The first `first` blocks are the first resident block of each CU. With two blocks per CU, the
+// second block's first loads queue behind the first block's first unit and its prefetch, so it
+// runs about 1.7 units behind for the whole kernel (measured on MI355X at 16 tokens: first units
+// done at 7.5 vs 12.2 us, ends at 27.7 vs 34.0 us). First blocks therefore take weight FIRST_W and
+// second ones SECOND_W (13 : 7 was the fastest of 11 : 9 to 14 : 6 for W13 at 16 tokens: 36.8 vs
+// 38.1 us with an equal split). Only while there are at most two blocks per CU and more units than
+// blocks; otherwise the split is equal (with U <= G every block has at most one unit anyway).
+//
+// The hardware deals block ids to the 8 XCDs round-robin. Within each group of blocks the ranges
+// are laid out XCD-major (the blocks of one XCD get consecutive ranges), so that the rounding of
+// U / G to whole units does not fall on the same XCDs every time (an equal split at U/G = 8.5 gave
+// every odd XCD 9 units per block and every even one 8).
+constexpr int FIRST_W = 13, SECOND_W = 7;
+
+__device__ __forceinline__ bool unit_range(int64_t U, int first, int64_t &u0, int64_t &u1)
 {
-    u0 = U * blockIdx.x / gridDim.x;
-    u1 = U * (blockIdx.x + 1) / gridDim.x;
+    const int G = (int)gridDim.x, b = (int)blockIdx.x;
+    const int nA = min(first, G), nB = G - nA;
+    const bool weighted = nB > 0 && nB <= nA && U > G;
+    const int wa = weighted ? FIRST_W : 1, wb = weighted ? SECOND_W : 1;
+    const bool in_a = b < nA;
+    const int n = in_a ? nA : nB, i = in_a ? b : b - nA, w = in_a ? wa : wb;
+    const int L = (n & 7) == 0 ? (i & 7) * (n >> 3) + (i >> 3) : i;
+    const int64_t W0 = (in_a ? 0 : (int64_t)nA * wa) + (int64_t)L * w;
+    const int64_t Wt = (int64_t)nA * wa + (int64_t)nB * wb;
+    u0 = U * W0 / Wt;
+    u1 = U * (W0 + w) / Wt;
     return u0 < u1;
 }
 
@@ -159,7 +183,7 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
                                                                              const uint8_t *__restrict__ codes,
                                                                              const uint8_t *__restrict__ scales,
                                                                              const float *__restrict__ gscale, int K, int I,
-                                                                             int layout, f16 *__restrict__ h)
+                                                                             int layout, f16 *__restrict__ h, int first)
 {
     using G = Geo<SPLIT>;
     constexpr int SL = G::GROUPS * TP;  // i slices per unit
@@ -168,7 +192,7 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
     const int itiles = I >> 4;
     const int upt = (itiles + SL - 1) / SL;  // units per row tile
     int64_t u0, u1;
-    if (!unit_range((int64_t)pv.hdr[3] * upt, u0, u1)) return;  // block-uniform
+    if (!unit_range((int64_t)pv.hdr[3] * upt, first, u0, u1)) return;  // block-uniform
     const int t_lo = (int)(u0 / upt);
     const G g(K);
     const size_t crow = (size_t)K >> 1, srow = (size_t)K >> 4;
@@ -252,7 +276,7 @@ __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, con
                                                                  const uint8_t *__restrict__ codes,
                                                                  const uint8_t *__restrict__ scales,
                                                                  const float *__restrict__ gscale, int K, int I,
-                                                                 float *__restrict__ ws)
+                                                                 float *__restrict__ ws, int first)
 {
     using G = Geo<SPLIT>;
     constexpr int NT = 2 * TP;            // output tiles per wave
@@ -262,7 +286,7 @@ __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, con
     const int ntiles = K >> 4;
     const int upt = (ntiles + UT - 1) / UT;
     int64_t u0, u1;
-    if (!unit_range((int64_t)pv.hdr[3] * upt, u0, u1)) return;
+    if (!unit_range((int64_t)pv.hdr[3] * upt, first, u0, u1)) return;
     const int t_lo = (int)(u0 / upt);
     const G g(I);
     const size_t crow = (size_t)I >> 1, srow = (size_t)I >> 4;
@@ -512,14 +536,19 @@ int split_for(int k)
 }
 
 // Persistent grid: `occ` 256-thread blocks per CU, never more blocks than units, and enough
-// blocks that no block's unit range spans more than MAX_RANGE_TILES row tiles
-// (range <= t_max/G + 2).
-unsigned stream_grid(int occ, int64_t units_max, int64_t t_max)
+// blocks that no block's unit range spans more than MAX_RANGE_TILES row tiles. With the weighted
+// split of unit_range (only while G <= 2 * first) a block gets at most 2*13/20 U/G + 1 units, i.e.
+// at most 1.3 t_max/G + 3 row tiles, so G >= t_max / 10 keeps that within 16 (checked by brute
+// force over t_max up to 60000, 1..32 units per tile and 1..304 CUs: at most 14 tiles).
+// *cus_out: the device's CU count.
+unsigned stream_grid(int occ, int64_t units_max, int64_t t_max, int *cus_out)
 {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    *cus_out = cus;
+    static_assert(MAX_RANGE_TILES == 16, "the bound below assumes 16 staged row tiles");
     int64_t g = occ * (int64_t)cus;
-    const int64_t g_min = (t_max + MAX_RANGE_TILES - 3) / (MAX_RANGE_TILES - 2);
+    const int64_t g_min = (t_max + 9) / 10;
     if (g < g_min) g = g_min;
     if (g > units_max) g = units_max;
     return (unsigned)(g > 0 ? g : 1);
@@ -534,13 +563,15 @@ int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, 
     const int split = split_for(K);
     const int sl = (4 / split) * W13_TP;
     const int upt = (I / 16 + sl - 1) / sl;
-    const dim3 grid(stream_grid(W13_OCC, t_max * upt, t_max)), block(256);
+    int cus = 0;
+    const dim3 grid(stream_grid(W13_OCC, t_max * upt, t_max, &cus)), block(256);
+    const int first = W13_OCC > 1 ? cus : (int)grid.x;  // one block per CU resident first
     const f16 *xp = reinterpret_cast<const f16 *>(x);
     f16 *hp = reinterpret_cast<f16 *>(h);
     switch (split) {
-    case 1: return launch(w13_swiglu_stream_kernel<1, W13_TP>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp);
-    case 2: return launch(w13_swiglu_stream_kernel<2, W13_TP>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp);
-    default: return launch(w13_swiglu_stream_kernel<4, W13_TP>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp);
+    case 1: return launch(w13_swiglu_stream_kernel<1, W13_TP>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first);
+    case 2: return launch(w13_swiglu_stream_kernel<2, W13_TP>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first);
+    default: return launch(w13_swiglu_stream_kernel<4, W13_TP>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first);
     }
 }
 
@@ -557,13 +588,15 @@ int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uin
     const int split = split_for(I);
     const int ut = (4 / split) * 2 * W2_TP;
     const int upt = (K / 16 + ut - 1) / ut;
-    const dim3 grid(stream_grid(W2_OCC, t_max * upt, t_max)), block(256);
+    int cus = 0;
+    const dim3 grid(stream_grid(W2_OCC, t_max * upt, t_max, &cus)), block(256);
+    const int first = W2_OCC > 1 ? cus : (int)grid.x;
     const f16 *hp = reinterpret_cast<const f16 *>(h);
     int st;
     switch (split) {
-    case 1: st = launch(w2_stream_kernel<1, W2_TP>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws); break;
-    case 2: st = launch(w2_stream_kernel<2, W2_TP>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws); break;
-    default: st = launch(w2_stream_kernel<4, W2_TP>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws); break;
+    case 1: st = launch(w2_stream_kernel<1, W2_TP>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws, first); break;
+    case 2: st = launch(w2_stream_kernel<2, W2_TP>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws, first); break;
+    default: st = launch(w2_stream_kernel<4, W2_TP>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws, first); break;
     }
     if (st != NVFP4_OK) return st;
     return run_reduce(pv, M, topk, K, topk_weights, ws, out, s, sh);
