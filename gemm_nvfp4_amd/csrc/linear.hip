@@ -300,6 +300,10 @@ int run_linear_f32(const uint16_t *x, int32_t M, const nvfp4_weights &w, float *
 // Qwen3.8 no-MTP concurrency" page, "Scope and related PRs"). One wave per token: each lane sums
 // its strided elements in FP32 in ascending order, then a fixed butterfly over the lanes, read
 // from lane 0, so the value never depends on the batch.
+// VEC (g 16-byte aligned; x rows always are, K % 128 == 0): lane l takes the 8-element pieces
+// l, l + 64, ... with 16-byte loads, four pieces' loads in flight at once. Otherwise one element per
+// lane and step. Either way a token's sum has one fixed order, whatever M.
+template <bool VEC>
 __global__ __launch_bounds__(256) void shared_gate_kernel(const f16 *__restrict__ x, int M, int K,
                                                           const f16 *__restrict__ g, float *__restrict__ sigma)
 {
@@ -307,7 +311,18 @@ __global__ __launch_bounds__(256) void shared_gate_kernel(const f16 *__restrict_
     if (m >= M) return;  // wave-uniform
     const f16 *xr = x + (size_t)m * K;
     float z = 0.0f;
-    for (int k = lane; k < K; k += 64) z = fmaf((float)xr[k], (float)g[k], z);
+    if (VEC) {
+        const int pieces = K >> 3;
+#pragma unroll 4
+        for (int pc = lane; pc < pieces; pc += 64) {
+            const f16x8 a = *reinterpret_cast<const f16x8 *>(xr + 8 * pc);
+            const f16x8 b = *reinterpret_cast<const f16x8 *>(g + 8 * pc);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z = fmaf((float)a[e], (float)b[e], z);
+        }
+    } else {
+        for (int k = lane; k < K; k += 64) z = fmaf((float)xr[k], (float)g[k], z);
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
     z = __shfl(z, 0, 64);
@@ -316,8 +331,11 @@ __global__ __launch_bounds__(256) void shared_gate_kernel(const f16 *__restrict_
 
 int run_shared_gate(const uint16_t *x, int32_t M, int32_t K, const uint16_t *g, float *sigma, hipStream_t s)
 {
-    return launch(shared_gate_kernel, dim3((unsigned)(((int64_t)M + 3) / 4)), dim3(256), 0, s,
-                  reinterpret_cast<const f16 *>(x), M, K, reinterpret_cast<const f16 *>(g), sigma);
+    const dim3 grid((unsigned)(((int64_t)M + 3) / 4));
+    const f16 *xp = reinterpret_cast<const f16 *>(x), *gp = reinterpret_cast<const f16 *>(g);
+    if ((reinterpret_cast<uintptr_t>(g) & 15) == 0 && K % 8 == 0)
+        return launch(shared_gate_kernel<true>, grid, dim3(256), 0, s, xp, M, K, gp, sigma);
+    return launch(shared_gate_kernel<false>, grid, dim3(256), 0, s, xp, M, K, gp, sigma);
 }
 
 int run_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights &w, uint16_t *y, hipStream_t s)

@@ -226,12 +226,12 @@ __device__ __forceinline__ void pass_chunks(PrefillShared &sh, const PassSrc &sr
     auto a_read = [&](int r, int s, int buf) {
         return *reinterpret_cast<const f16x8 *>(&sh.a[buf][16 * r + n][AQ * q + 8 * s]);
     };
-    // The chunk sum starts from +0: +0 + c0 is c0 bitwise, because a chain that starts from +0
-    // never ends in -0 (x + y is -0 only when both are -0).
+    // The chunk sum starts from -0, the exact identity of addition (-0 + x is x for every x,
+    // zeros of both signs included), so no chunk needs a special case.
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int t = 0; t < PF_T; ++t) tot[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < PF_T; ++t) tot[r][t] = f32x4{-0.f, -0.f, -0.f, -0.f};
     cvt_step(0, 0);
     mul_step(0, 0, 0, 0);
     cvt_step(0, 1);

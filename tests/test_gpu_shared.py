@@ -47,6 +47,26 @@ def test_shared_expert_outputs(orc):
     assert np.all(np.abs(sg.cpu().numpy() - sg_ref) <= 1e-6 + 1e-5 * sg_ref)
 
 
+def test_shared_gate_unaligned_gate_vector(orc):
+    """A gate vector that is only 2-byte aligned takes the element-wise gate kernel (16-byte
+    aligned ones take the vector loads); both match the oracle."""
+    rng = S.rng_for(S.WORKLOAD_IDS["decode"], 52, 0)
+    shared = S.shared_expert(rng, 2048, 256)
+    x = S.activations(rng, 7, 2048)
+    w13s, w2s, g = _shared_dev(shared)
+    buf = torch.zeros(2048 + 8, dtype=torch.float16, device="cuda")
+    g_odd = buf[1:2049]
+    g_odd.copy_(g)
+    assert g_odd.data_ptr() % 16 == 2
+    xd = torch.from_numpy(x).cuda()
+    _, sg_vec, _ = G.nvfp4_moe_shared_expert(xd, w13s, w2s, g)
+    _, sg_el, _ = G.nvfp4_moe_shared_expert(xd, w13s, w2s, g_odd)
+    torch.cuda.synchronize()
+    sg_ref = orc.shared_gate(x, shared["g"])
+    for sg in (sg_vec, sg_el):
+        assert np.all(np.abs(sg.cpu().numpy() - sg_ref) <= 1e-6 + 1e-5 * sg_ref)
+
+
 @pytest.mark.parametrize("shape,routing", [
     (S.MoEShape(m=5, e=512, topk=10, k=2048, i=512), "uniform"),      # token-major W2 (P <= E/4)
     (S.DECODE, "uniform"),                                             # expert-major streaming W2
