@@ -144,3 +144,24 @@ def test_moe_token_major_and_expert_major_w2_agree(orc, i):
               "tw": d["tw"][t:t + 1].contiguous(), "w13": d["w13"], "w2": d["w2"]}
         single = run_moe(one, 0, dev=dd)["out"][0]
         assert torch.equal(single.view(torch.int16), res["out"][t].view(torch.int16)), f"token {t}"
+
+
+@pytest.mark.parametrize("m", [2, 9])
+def test_moe_maximum_reduction_lengths(orc, m):
+    """K = I = 2048, the largest reduction lengths the grouped GEMMs accept: W13 and W2 both split
+    into four 512-element chunks. m = 2 (P = 8 <= E/4) runs W2 token-major, m = 9 (P = 36)
+    expert-major with the four-way intra-block split; both must match the oracle and each token
+    alone, bitwise."""
+    sh = S.MoEShape(m=m, e=32, topk=4, k=2048, i=2048)
+    case = S.moe_case(sh, routing="uniform", workload="stress", route_pattern=70 + m)
+    res = run_moe(case, 0)
+    _check_against_oracle(orc, case, 0, res, f"max K/I m={m}")
+    d = res["dev"]
+    for t in (0, m - 1):
+        one = dict(case)
+        one["shape"] = S.MoEShape(m=1, e=sh.e, topk=sh.topk, k=sh.k, i=sh.i)
+        one["x"], one["ids"], one["topk_weights"] = case["x"][t:t + 1], case["ids"][t:t + 1], case["topk_weights"][t:t + 1]
+        dd = {"x": d["x"][t:t + 1].contiguous(), "ids": d["ids"][t:t + 1].contiguous(),
+              "tw": d["tw"][t:t + 1].contiguous(), "w13": d["w13"], "w2": d["w2"]}
+        single = run_moe(one, 0, dev=dd)["out"][0]
+        assert torch.equal(single.view(torch.int16), res["out"][t].view(torch.int16)), f"token {t}"

@@ -78,3 +78,20 @@ def test_prefill_8192_tokens_sampled(orc):
     for t in tokens[:6]:
         single = _single_token_out(case, res["dev"], int(t), 0)
         assert torch.equal(single.view(torch.int16), res["out"][int(t)].view(torch.int16)), f"token {t}"
+
+
+@pytest.mark.parametrize("i", [640, 1024])
+def test_prefill_multi_chunk_w2(orc, i):
+    """I > 512: W2 reduces over several chunks and runs the multi-chunk prefill kernel (passes of up
+    to 80 rows, chunk sums in order); I = 640 ends in a 128-element chunk. About 150 rows per
+    expert: two passes each."""
+    sh = S.MoEShape(m=300, e=4, topk=2, k=256, i=i)
+    case = S.moe_case(sh, routing="uniform", workload="prefill", route_pattern=40 + i)
+    res = run_moe(case, 0)
+    pl = orc.plan(case["ids"], sh.e, 16)
+    h_ref, out_ref = orc.moe_grouped(case, pl)
+    assert_rows_close(to_np64(res["h"][: pl["n_valid"]]), h_ref, f"prefill I={i} h")
+    assert_rows_close(to_np64(res["out"]), out_ref, f"prefill I={i} out")
+    for t in (0, 149, 299):
+        single = _single_token_out(case, res["dev"], t, 0)
+        assert torch.equal(single.view(torch.int16), res["out"][t].view(torch.int16)), f"token {t}"
