@@ -259,7 +259,8 @@ def dense_timing(copies=64, launches=256):
 def shared_layer_timing(steps, W13, W2, routes, i_shared=512):
     """The 16-token decode layer with a shared expert (K=2048, 512 intermediate columns) and its gate:
     plan, W13, shared expert, W2 with the shared term. Weight sets rotate as in the headline; the
-    shared expert rotates over as many copies."""
+    shared expert rotates over as many copies. Three forms: the shared expert's own launches in the
+    same stream (serial), on a second stream (overlapped), and inside the routed launches (fused)."""
     import torch
     import gemm_nvfp4_amd as G
     from synth import inputs as S
@@ -274,7 +275,17 @@ def shared_layer_timing(steps, W13, W2, routes, i_shared=512):
 
     side = torch.cuda.Stream()  # default priority
 
+    def step_fused(i):  # the shared expert as extra tiles of the routed W13 and W2 launches
+        p, r = i % P, i % R
+        G.nvfp4_moe_plan(routes.ids[p], E, plan=layer.plan)
+        G.nvfp4_moe_w13_swiglu_with_shared(layer.plan, M, TOPK, E, routes.x[p], W13[r], sw13[r], g, h=layer.h,
+                                           shared_h=hs, shared_sigma=sg)
+        G.nvfp4_moe_w2_reduce_with_shared(layer.plan, M, TOPK, E, layer.h, W2[r], routes.tw[p], hs, sw2[r], sg,
+                                          shared_y=ys, out=layer.out, ws=layer.ws)
+
     def step(i, overlap):
+        if overlap is None:
+            return step_fused(i)
         p, r = i % P, i % R
         cur = torch.cuda.current_stream()
         if overlap:  # the shared expert depends on x only: run it beside plan + W13
@@ -293,7 +304,7 @@ def shared_layer_timing(steps, W13, W2, routes, i_shared=512):
 
     wbytes = sum(routes.active[i % P] * EXPERT_BYTES + 3 * i_shared * K * 9 // 16 for i in range(steps))
     res = {"M": M, "shared_intermediate": i_shared}
-    for name, ov in (("serial", False), ("overlapped", True)):
+    for name, ov in (("serial", False), ("overlapped", True), ("fused", None)):
         ms = time_graph(lambda: [step(i, ov) for i in range(steps)], steps, lambda: [step(i, ov) for i in range(8)])
         res[f"us_per_layer_{name}"] = round(ms * 1e3 / steps, 3)
         res[f"weight_GBps_{name}"] = round(wbytes / (ms * 1e-3) / 1e9, 1)

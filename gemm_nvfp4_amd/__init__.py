@@ -21,6 +21,8 @@ from ._lib import (  # noqa: F401
     nvfp4_moe_w13_swiglu,
     nvfp4_moe_w2_reduce,
     nvfp4_moe_w2_reduce_shared,
+    nvfp4_moe_w13_swiglu_with_shared,
+    nvfp4_moe_w2_reduce_with_shared,
     nvfp4_moe_w2_workspace_bytes,
     nvfp4_status_str,
     plan_fields,

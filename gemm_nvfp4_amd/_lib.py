@@ -52,6 +52,10 @@ _SIGS = {
                                           _vp, _vp, _vp, _vp]),
     "nvfp4_moe_w2_reduce_shared": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _vp, _vp, _vp,
                                              _vp, _vp, _sz, _vp]),
+    "nvfp4_moe_w13_swiglu_with_shared": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _i32, _vp,
+                                                   C.POINTER(nvfp4_weights), _vp, _vp, _vp, _vp]),
+    "nvfp4_moe_w2_reduce_with_shared": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _vp, _vp,
+                                                  C.POINTER(nvfp4_weights), _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_linear_swiglu": (C.c_int, [_vp, _i32, C.POINTER(nvfp4_weights), _i32, _vp, _vp]),
     "nvfp4_linear_fp8": (C.c_int, [_vp, _i32, C.POINTER(fp8_channel_weights), _vp, _vp]),
 }
@@ -339,3 +343,45 @@ def plan_fields(plan: torch.Tensor, M: int, topk: int, E: int) -> dict:
     f["tile_rows"] = f["tile_rows"][:nt]
     f["tile_pair"] = f["tile_pair"][:nt]
     return f
+
+
+def nvfp4_moe_w13_swiglu_with_shared(plan: torch.Tensor, M: int, topk: int, E: int, x: torch.Tensor,
+                                     w13: NVFP4Tensor, shared_w13: NVFP4Tensor, gate: torch.Tensor, layout: int = 0,
+                                     h: torch.Tensor | None = None, shared_h: torch.Tensor | None = None,
+                                     shared_sigma: torch.Tensor | None = None, stream=None):
+    """Grouped W13 + SwiGLU with the shared expert's gate/up and its gate in the same launch.
+    Returns (h fp16 [M*topk, I] in bucket order, shared_h fp16 [M, Is], shared_sigma FP32 [M])."""
+    I, Is = w13.rows // 2, shared_w13.rows // 2
+    dev = x.device
+    h = torch.empty((M * topk, I), dtype=torch.float16, device=dev) if h is None else h
+    shared_h = torch.empty((M, Is), dtype=torch.float16, device=dev) if shared_h is None else shared_h
+    shared_sigma = torch.empty((M,), dtype=torch.float32, device=dev) if shared_sigma is None else shared_sigma
+    d, ds = w13.desc(), shared_w13.desc()
+    _check("nvfp4_moe_w13_swiglu_with_shared", lib().nvfp4_moe_w13_swiglu_with_shared(
+        _dev(plan, "plan", torch.int32), M, topk, E, _dev(x, "x", torch.float16), C.byref(d), layout,
+        _dev(h, "h", torch.float16), C.byref(ds), _dev(gate, "gate", torch.float16),
+        _dev(shared_h, "shared_h", torch.float16), _dev(shared_sigma, "shared_sigma", torch.float32),
+        _stream(stream)))
+    return h, shared_h, shared_sigma
+
+
+def nvfp4_moe_w2_reduce_with_shared(plan: torch.Tensor, M: int, topk: int, E: int, h: torch.Tensor, w2: NVFP4Tensor,
+                                    topk_weights: torch.Tensor, shared_h: torch.Tensor, shared_w2: NVFP4Tensor,
+                                    shared_sigma: torch.Tensor, shared_y: torch.Tensor | None = None,
+                                    out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                                    stream=None) -> torch.Tensor:
+    """Grouped W2 + slot-order reduction with the shared expert's down projection in the same launch
+    and its term added last. Returns out fp16 [M, K]."""
+    K = w2.rows
+    dev = h.device
+    out = torch.empty((M, K), dtype=torch.float16, device=dev) if out is None else out
+    shared_y = torch.empty((M, K), dtype=torch.float32, device=dev) if shared_y is None else shared_y
+    if ws is None:
+        ws = torch.empty(max(nvfp4_moe_w2_workspace_bytes(M, topk, K), 256), dtype=torch.uint8, device=dev)
+    d, ds = w2.desc(), shared_w2.desc()
+    _check("nvfp4_moe_w2_reduce_with_shared", lib().nvfp4_moe_w2_reduce_with_shared(
+        _dev(plan, "plan", torch.int32), M, topk, E, _dev(h, "h", torch.float16), C.byref(d),
+        _dev(topk_weights, "topk_weights", torch.float32), _dev(shared_h, "shared_h", torch.float16), C.byref(ds),
+        _dev(shared_sigma, "shared_sigma", torch.float32), _dev(shared_y, "shared_y", torch.float32),
+        _dev(out, "out", torch.float16), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return out

@@ -181,6 +181,92 @@ NVFP4_API int nvfp4_moe_shared_expert(const uint16_t *x, int32_t M, const nvfp4_
     return st;
 }
 
+NVFP4_API int nvfp4_moe_w13_swiglu_with_shared(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16_t *x,
+                                               const nvfp4_weights *w13, int32_t layout, uint16_t *h,
+                                               const nvfp4_weights *shared_w13, const uint16_t *gate, uint16_t *shared_h,
+                                               float *shared_sigma, void *stream)
+{
+    if (!plan_shape_ok(M, topk, E) || (layout != 0 && layout != 1)) return NVFP4_ERR_SHAPE;
+    if (E > nvfp4::MAX_EXPERTS) return NVFP4_ERR_UNSUPPORTED;
+    int st = check_weights(w13);
+    if (st == NVFP4_OK) st = check_weights(shared_w13);
+    if (st != NVFP4_OK) return st;
+    if (w13->groups != E || w13->rows % 2 != 0 || shared_w13->groups != 1 || shared_w13->rows % 2 != 0 ||
+        shared_w13->k != w13->k)
+        return NVFP4_ERR_SHAPE;
+    const int K = w13->k, I = w13->rows / 2, Is = shared_w13->rows / 2;
+    if (K % 128 != 0 || K > nvfp4::MAX_MOE_RED || I % 16 != 0 || Is % 16 != 0) return NVFP4_ERR_UNSUPPORTED;
+    if (M == 0) return NVFP4_OK;
+    if (!plan || !x || !h || !gate || !shared_h || !shared_sigma) return NVFP4_ERR_NULL;
+    if (!aligned(plan, 16) || !aligned(x, 16) || !aligned(h, 16) || !aligned(shared_h, 16) || !aligned(gate, 2) ||
+        !aligned(shared_sigma, 4))
+        return NVFP4_ERR_ALIGN;
+    const PlanLayout L = nvfp4::plan_layout(M, topk, E);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const nvfp4::PlanView pv = nvfp4::plan_view(plan, L);
+    if (!nvfp4::use_prefill(M, L.P, E, K, I) && Is == I && aligned(gate, 16)) {
+        nvfp4::SharedW13 shx;
+        shx.codes = shared_w13->codes;
+        shx.scales = shared_w13->scales;
+        shx.gscale = shared_w13->global_scale;
+        shx.h = shared_h;
+        shx.gate = gate;
+        shx.sigma = shared_sigma;
+        shx.M = M;
+        return nvfp4::run_w13(pv, L.T, topk, x, *w13, layout, h, s, shx);
+    }
+    // Separate launches: the routed regime's W13, then the shared expert's gate/up and its gate.
+    st = nvfp4::use_prefill(M, L.P, E, K, I) ? nvfp4::run_w13_prefill(pv, L.A, M, topk, x, *w13, layout, h, s)
+                                              : nvfp4::run_w13(pv, L.T, topk, x, *w13, layout, h, s);
+    if (st == NVFP4_OK) st = nvfp4::run_linear_swiglu(x, M, *shared_w13, layout, shared_h, s);
+    if (st == NVFP4_OK) st = nvfp4::run_shared_gate(x, M, K, gate, shared_sigma, s);
+    return st;
+}
+
+NVFP4_API int nvfp4_moe_w2_reduce_with_shared(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16_t *h,
+                                              const nvfp4_weights *w2, const float *topk_weights,
+                                              const uint16_t *shared_h, const nvfp4_weights *shared_w2,
+                                              const float *shared_sigma, float *shared_y, uint16_t *out, void *ws,
+                                              size_t ws_bytes, void *stream)
+{
+    if (!plan_shape_ok(M, topk, E)) return NVFP4_ERR_SHAPE;
+    if (E > nvfp4::MAX_EXPERTS) return NVFP4_ERR_UNSUPPORTED;
+    int st = check_weights(w2);
+    if (st == NVFP4_OK) st = check_weights(shared_w2);
+    if (st != NVFP4_OK) return st;
+    if (w2->groups != E || shared_w2->groups != 1 || shared_w2->rows != w2->rows) return NVFP4_ERR_SHAPE;
+    const int K = w2->rows, I = w2->k, Is = shared_w2->k;
+    if (I % 128 != 0 || I > nvfp4::MAX_MOE_RED || K % 64 != 0 || Is % 128 != 0 || Is > nvfp4::MAX_LINEAR_K)
+        return NVFP4_ERR_UNSUPPORTED;
+    if (M == 0) return NVFP4_OK;
+    if (!plan || !h || !topk_weights || !out || !ws || !shared_h || !shared_sigma || !shared_y) return NVFP4_ERR_NULL;
+    if (!aligned(plan, 16) || !aligned(h, 16) || !aligned(out, 16) || !aligned(ws, 16) || !aligned(topk_weights, 4) ||
+        !aligned(shared_h, 16) || !aligned(shared_sigma, 4) || !aligned(shared_y, 16))
+        return NVFP4_ERR_ALIGN;
+    if (ws_bytes < nvfp4_moe_w2_workspace_bytes(M, topk, K)) return NVFP4_ERR_WORKSPACE;
+    const PlanLayout L = nvfp4::plan_layout(M, topk, E);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const nvfp4::PlanView pv = nvfp4::plan_view(plan, L);
+    if (!nvfp4::use_prefill(M, L.P, E, K, I) && Is == I) {
+        nvfp4::SharedW2 shw;
+        shw.codes = shared_w2->codes;
+        shw.scales = shared_w2->scales;
+        shw.gscale = shared_w2->global_scale;
+        shw.h = shared_h;
+        shw.y = shared_y;
+        shw.sigma = shared_sigma;
+        shw.M = M;
+        return nvfp4::run_w2(pv, L.T, M, topk, h, *w2, topk_weights, out, static_cast<float *>(ws), s, {}, shw);
+    }
+    // Separate launches: the shared expert's down projection, then W2 + reduction with its term.
+    st = nvfp4::run_linear_f32(shared_h, M, *shared_w2, shared_y, s);
+    if (st != NVFP4_OK) return st;
+    nvfp4::SharedTerm sh;
+    sh.y = shared_y;
+    sh.sigma = shared_sigma;
+    return w2_reduce(plan, M, topk, E, h, w2, topk_weights, out, ws, ws_bytes, stream, sh);
+}
+
 NVFP4_API int nvfp4_linear(const uint16_t *x, int32_t M, const nvfp4_weights *w, uint16_t *y, void *stream)
 {
     if (M < 0) return NVFP4_ERR_SHAPE;

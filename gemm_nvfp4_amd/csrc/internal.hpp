@@ -96,17 +96,40 @@ int run_plan(const int32_t *ids, int32_t M, int32_t topk, int32_t E, int32_t *pl
              hipStream_t s);
 int run_route(const float *logits, int32_t M, int32_t E, int32_t topk, int32_t *ids, float *weights, int32_t *plan,
               const PlanLayout &L, hipStream_t s);
+// The shared expert as extra tiles of the routed W13 stream launch (M = 0: none). Its tiles come
+// before the plan's: tile t covers tokens 16t .. 16t+15. Its weights have the routed I and layout.
+// Besides its h, the launch computes each token's gate sigma = 1 / (1 + e^-(x . gate)).
+struct SharedW13 {
+    const uint8_t *codes = nullptr, *scales = nullptr;  // one group: [2I][K/2], [2I][K/16]
+    const float *gscale = nullptr;
+    uint16_t *h = nullptr;           // [M][I] fp16
+    const uint16_t *gate = nullptr;  // [K], 16-byte aligned
+    float *sigma = nullptr;          // [M]
+    int32_t M = 0;
+};
 int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, const nvfp4_weights &w,
-            int32_t layout, uint16_t *h, hipStream_t s);
+            int32_t layout, uint16_t *h, hipStream_t s, SharedW13 shx = {});
 // The shared expert's contribution to the MoE output (both pointers NULL: none): FP32 y [M][K] and
 // the per-token gate sigma [M], added after the routed slots as one more fmaf.
 struct SharedTerm {
     const float *y = nullptr;
     const float *sigma = nullptr;
 };
+// The shared expert as extra tiles of the routed W2 launch (M = 0: none): in the expert-major
+// regime its tiles (first, as in SharedW13) write y, which the reduction adds with sigma; in the
+// token-major regime it is one more slot, after the routed ones, with weight sigma.
+struct SharedW2 {
+    const uint8_t *codes = nullptr, *scales = nullptr;  // one group: [K][I/2], [K][I/16]
+    const float *gscale = nullptr;
+    const uint16_t *h = nullptr;  // [M][I] fp16
+    float *y = nullptr;           // [M][K] FP32
+    const float *sigma = nullptr; // [M]
+    int32_t M = 0;
+};
 
 int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uint16_t *h, const nvfp4_weights &w,
-           const float *topk_weights, uint16_t *out, float *ws, hipStream_t s, SharedTerm sh = {});
+           const float *topk_weights, uint16_t *out, float *ws, hipStream_t s, SharedTerm sh = {},
+           SharedW2 shw = {});
 int run_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, uint16_t *y, hipStream_t s);
 int run_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights &w, uint16_t *y, hipStream_t s);
 int run_linear_swiglu(const uint16_t *x, int32_t M, const nvfp4_weights &w, int32_t layout, uint16_t *h,

@@ -121,10 +121,10 @@ __global__ __launch_bounds__(max_waves<NW>() * 64) void linear_kernel(const f16 
                         tot[t] += part[(((size_t)c * ROW_GROUP + r) * NW + t) * 16 * LDS_ROW + row * LDS_ROW + cl];
                 }
                 if constexpr (GATED) {
-                    y[(size_t)m * N + nt * 16 + cl] = (f16)swiglu(tot[0] * gs, tot[1] * gs);
+                    y[(size_t)m * N + nt * 16 + cl] = f16_of_f32(swiglu(tot[0] * gs, tot[1] * gs));
                 } else {
 #pragma unroll
-                    for (int t = 0; t < NW; ++t) y[(size_t)m * N + (nt * NW + t) * 16 + cl] = (OUT)(tot[t] * gs);
+                    for (int t = 0; t < NW; ++t) y[(size_t)m * N + (nt * NW + t) * 16 + cl] = to_out<OUT>(tot[t] * gs);
                 }
             }
         }
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(8 * 64) void linear_fp8_kernel(const f16 *__restric
                     for (int c = 1; c < S; ++c)
                         tot += part[(((size_t)c * ROW_GROUP + r) * NW + t) * 16 * LDS_ROW + row * LDS_ROW + cl];
                     const int colx = (nt * NW + t) * 16 + cl;
-                    y[(size_t)m * N + colx] = (f16)(tot * chscale[colx]);
+                    y[(size_t)m * N + colx] = f16_of_f32(tot * chscale[colx]);
                 }
             }
         }
@@ -300,9 +300,9 @@ int run_linear_f32(const uint16_t *x, int32_t M, const nvfp4_weights &w, float *
 // Qwen3.8 no-MTP concurrency" page, "Scope and related PRs"). One wave per token: each lane sums
 // its strided elements in FP32 in ascending order, then a fixed butterfly over the lanes, read
 // from lane 0, so the value never depends on the batch.
-// VEC (g 16-byte aligned; x rows always are, K % 128 == 0): lane l takes the 8-element pieces
-// l, l + 64, ... with 16-byte loads, four pieces' loads in flight at once. Otherwise one element per
-// lane and step. Either way a token's sum has one fixed order, whatever M.
+// VEC (g 16-byte aligned; x rows always are, K % 128 == 0): wave_dot_f16, 16-byte loads with four
+// pieces in flight at once (the order the fused shared-expert launch uses too). Otherwise one element
+// per lane and step. Either way a token's sum has one fixed order, whatever M.
 template <bool VEC>
 __global__ __launch_bounds__(256) void shared_gate_kernel(const f16 *__restrict__ x, int M, int K,
                                                           const f16 *__restrict__ g, float *__restrict__ sigma)
@@ -310,22 +310,16 @@ __global__ __launch_bounds__(256) void shared_gate_kernel(const f16 *__restrict_
     const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (m >= M) return;  // wave-uniform
     const f16 *xr = x + (size_t)m * K;
-    float z = 0.0f;
+    float z;
     if (VEC) {
-        const int pieces = K >> 3;
-#pragma unroll 4
-        for (int pc = lane; pc < pieces; pc += 64) {
-            const f16x8 a = *reinterpret_cast<const f16x8 *>(xr + 8 * pc);
-            const f16x8 b = *reinterpret_cast<const f16x8 *>(g + 8 * pc);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) z = fmaf((float)a[e], (float)b[e], z);
-        }
+        z = wave_dot_f16(xr, g, K);
     } else {
+        z = 0.0f;
         for (int k = lane; k < K; k += 64) z = fmaf((float)xr[k], (float)g[k], z);
-    }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
-    z = __shfl(z, 0, 64);
+        for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
+        z = __shfl(z, 0, 64);
+    }
     if (lane == 0) sigma[m] = 1.0f / (1.0f + expf(-z));
 }
 

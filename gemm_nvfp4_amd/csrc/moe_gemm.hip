@@ -47,6 +47,8 @@ struct TileStage {
     int pair[MAX_RANGE_TILES][16];
 };
 
+__device__ __forceinline__ int t_lo_of(int64_t u0, int upt) { return (int)(u0 / upt); }
+
 // Contiguous unit range of this block out of U units; returns false if empty.
 //
 // The first `first` blocks are the first resident block of each CU. With two blocks per CU, the
@@ -82,20 +84,32 @@ __device__ __forceinline__ bool unit_range(int64_t U, int first, int64_t &u0, in
 // Stage tiles [t_lo, t_lo + ntl) from the plan's tile descriptors: expert id, row count, first
 // bucket row, each row's pair, and its activation row: the pair's token when topk > 0 (W13), else
 // the bucket row itself (W2). All of it is one dependent load away from the tile index.
-__device__ __forceinline__ void stage_tiles(const PlanView &pv, TileStage &st, int t_lo, int ntl, int topk)
+// The first Ts tiles are the shared expert's (Ts = 0: none): expert id -1, tokens 16t .. 16t+15 of
+// Ms as rows (first row 16t of its own h or y; activation row: the token, or its shared h row).
+template <bool SH = false>
+__device__ __forceinline__ void stage_tiles(const PlanView &pv, TileStage &st, int t_lo, int ntl, int topk, int Ts = 0,
+                                            int Ms = 0)
 {
+    if constexpr (!SH) Ts = 0;
     if ((int)threadIdx.x < ntl) {
-        const int t = t_lo + threadIdx.x;
-        st.e[threadIdx.x] = pv.tile_expert[t];
-        st.cnt[threadIdx.x] = pv.tile_rows[t];
-        st.base[threadIdx.x] = pv.tile_base[t];
+        const int tg = t_lo + threadIdx.x, t = tg - Ts;
+        const bool shr = SH && tg < Ts;
+        st.e[threadIdx.x] = shr ? -1 : pv.tile_expert[t];
+        st.cnt[threadIdx.x] = shr ? min(16, Ms - 16 * tg) : pv.tile_rows[t];
+        st.base[threadIdx.x] = shr ? 16 * tg : pv.tile_base[t];
     }
     if ((int)threadIdx.x < ntl * 16) {
-        const int i = threadIdx.x >> 4, r = threadIdx.x & 15, t = t_lo + i;
-        const int n = pv.tile_rows[t];
-        const int p = r < n ? pv.tile_pair[(int64_t)t * 16 + r] : 0;  // padding rows: pair 0, never stored
-        st.pair[i][r] = p;
-        st.arow[i][r] = topk > 0 ? p / topk : pv.tile_base[t] + (r < n ? r : 0);
+        const int i = threadIdx.x >> 4, r = threadIdx.x & 15, tg = t_lo + i, t = tg - Ts;
+        if (SH && tg < Ts) {
+            const int n = min(16, Ms - 16 * tg);
+            st.pair[i][r] = 0;
+            st.arow[i][r] = 16 * tg + (r < n ? r : 0);
+        } else {
+            const int n = pv.tile_rows[t];
+            const int p = r < n ? pv.tile_pair[(int64_t)t * 16 + r] : 0;  // padding rows: pair 0, never stored
+            st.pair[i][r] = p;
+            st.arow[i][r] = topk > 0 ? p / topk : pv.tile_base[t] + (r < n ? r : 0);
+        }
     }
     __syncthreads();
 }
@@ -178,12 +192,15 @@ __device__ __forceinline__ void mma_chunk(const RawChunk (&w)[NW], const f16x8 a
 // Unit = (row tile, GROUPS*TP consecutive 16-wide i slices); wave (sub, c) owns the gate and up rows
 // of slices (GROUPS*unit_index + sub)*TP .. +TP-1 for chunk c. A wave loads unit u+1's weights
 // while unit u computes; barriers order LDS only, so they do not wait for those loads.
-template <int SPLIT, int TP>
+//
+// SH: the shared expert's tiles come first (SharedW13); without it the kernel has none of their code.
+template <int SPLIT, int TP, bool SH>
 __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanView pv, int topk, const f16 *__restrict__ x,
                                                                              const uint8_t *__restrict__ codes,
                                                                              const uint8_t *__restrict__ scales,
                                                                              const float *__restrict__ gscale, int K, int I,
-                                                                             int layout, f16 *__restrict__ h, int first)
+                                                                             int layout, f16 *__restrict__ h, int first,
+                                                                             SharedW13 shx)
 {
     using G = Geo<SPLIT>;
     constexpr int SL = G::GROUPS * TP;  // i slices per unit
@@ -191,12 +208,32 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
     __shared__ TileStage st;
     const int itiles = I >> 4;
     const int upt = (itiles + SL - 1) / SL;  // units per row tile
+    const int Ts = SH ? (shx.M + 15) >> 4 : 0;  // shared expert tiles, before the plan's
     int64_t u0, u1;
-    if (!unit_range((int64_t)pv.hdr[3] * upt, first, u0, u1)) return;  // block-uniform
+    // Shared expert: block b computes the gates of tokens b, b + G, ... (wave 0). The first one's
+    // loads are issued before the tile staging, which hides their latency.
+    const bool has_units = unit_range((int64_t)(Ts + pv.hdr[3]) * upt, first, u0, u1);
+    if constexpr (SH) {
+        const f16 *gv = reinterpret_cast<const f16 *>(shx.gate);
+        const bool gate0 = (int)blockIdx.x < shx.M && threadIdx.x < 64;
+        WaveDotRegs gr;
+        if (gate0) wave_dot_load(gr, x + (size_t)blockIdx.x * K, gv, K);
+        if (has_units) stage_tiles<SH>(pv, st, t_lo_of(u0, upt), (int)((u1 - 1) / upt) - t_lo_of(u0, upt) + 1, topk, Ts,
+                                       shx.M);
+        if (gate0) {
+            const float z = wave_dot_sum(gr, K);
+            if (threadIdx.x == 0) shx.sigma[blockIdx.x] = 1.0f / (1.0f + expf(-z));
+            for (int r = blockIdx.x + gridDim.x; r < shx.M; r += gridDim.x) {
+                const float zr = wave_dot_f16(x + (size_t)r * K, gv, K);
+                if (threadIdx.x == 0) shx.sigma[r] = 1.0f / (1.0f + expf(-zr));
+            }
+        }
+    }
+    if (!has_units) return;  // block-uniform
     const int t_lo = (int)(u0 / upt);
     const G g(K);
     const size_t crow = (size_t)K >> 1, srow = (size_t)K >> 4;
-    stage_tiles(pv, st, t_lo, (int)((u1 - 1) / upt) - t_lo + 1, topk);
+    if constexpr (!SH) stage_tiles<SH>(pv, st, t_lo, (int)((u1 - 1) / upt) - t_lo + 1, topk);
 
     int cur = -1;
     f16x8 af[4][4];
@@ -205,14 +242,16 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
     auto load_unit = [&](int64_t u, RawChunk (&w)[2 * TP]) {
         const int ti = (int)(u / upt) - t_lo;
         const int it0 = (int)(u % upt) * SL + g.sub * TP;
-        const size_t eb = (size_t)st.e[ti] * 2 * I;
+        const int e = st.e[ti];
+        const uint8_t *cb = !SH || e >= 0 ? codes : shx.codes, *sb = !SH || e >= 0 ? scales : shx.scales;
+        const size_t eb = !SH || e >= 0 ? (size_t)e * 2 * I : 0;
 #pragma unroll
         for (int p = 0; p < TP; ++p) {
             const int i_row = min(it0 + p, itiles - 1) * 16 + g.n;
             const int rg = layout ? 2 * i_row : i_row;
             const int ru = layout ? 2 * i_row + 1 : I + i_row;
-            w[2 * p] = load_chunk(codes + (eb + rg) * crow, scales + (eb + rg) * srow, g.kb_ld, g.q_ld);
-            w[2 * p + 1] = load_chunk(codes + (eb + ru) * crow, scales + (eb + ru) * srow, g.kb_ld, g.q_ld);
+            w[2 * p] = load_chunk(cb + (eb + rg) * crow, sb + (eb + rg) * srow, g.kb_ld, g.q_ld);
+            w[2 * p + 1] = load_chunk(cb + (eb + ru) * crow, sb + (eb + ru) * srow, g.kb_ld, g.q_ld);
         }
     };
     // One unit: math on `w` (already loading), next unit's weights into `wn`. Called with the two
@@ -220,7 +259,11 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
     auto step = [&](int64_t u, RawChunk (&w)[2 * TP], RawChunk (&wn)[2 * TP]) {
         const int ti = (int)(u / upt) - t_lo;
         const int it0 = (int)(u % upt) * SL + g.sub * TP;
-        const int e = st.e[ti], cnt = st.cnt[ti], base = st.base[ti];
+        const int e = SH ? __builtin_amdgcn_readfirstlane(st.e[ti]) : st.e[ti], cnt = st.cnt[ti], base = st.base[ti];
+        // With the shared expert the global scale is a select of two loads: read it before the
+        // prefetch below, so that waiting for it never waits for that.
+        float gs = 0.f;
+        if constexpr (SH) gs = e >= 0 ? gscale[e] : shx.gscale[0];
         if (ti != cur) {  // A of this tile's rows, reused by every unit of the tile
             cur = ti;
             load_a_chunk(af, x + (size_t)st.arow[ti][g.n] * K, g.qv && g.n < cnt, g.kb, g.q);
@@ -240,7 +283,8 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
 #pragma unroll
             for (int j = 0; j < 4; ++j) part[g.wave][t][4 * g.q + j][g.n] = acc[t][j];
         lds_barrier();
-        const float gs = gscale[e];
+        if constexpr (!SH) gs = gscale[e];
+        f16 *hb = !SH || e >= 0 ? h : reinterpret_cast<f16 *>(shx.h);
         const int row = threadIdx.x >> 4, col = threadIdx.x & 15;
 #pragma unroll
         for (int gp = 0; gp < G::GROUPS; ++gp)
@@ -254,7 +298,7 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
                         Gs += part[gp * SPLIT + cc][2 * p][row][col];
                         Us += part[gp * SPLIT + cc][2 * p + 1][row][col];
                     }
-                    h[(size_t)(base + row) * I + itx * 16 + col] = (f16)swiglu(Gs * gs, Us * gs);
+                    hb[(size_t)(base + row) * I + itx * 16 + col] = f16_of_f32(swiglu(Gs * gs, Us * gs));
                 }
             }
         lds_barrier();
@@ -271,12 +315,14 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
 // Unit = (row tile, 2*GROUPS*TP consecutive 16-row output tiles); wave (sub, c) owns output tiles
 // 2*TP*(GROUPS*unit_index + sub) .. +2*TP-1 for chunk c. With one chunk (I <= 512) the waves never
 // meet. As in W13, unit u+1's weights load while unit u computes.
-template <int SPLIT, int TP>
+//
+// SH: the shared expert's tiles come first (SharedW2); without it the kernel has none of their code.
+template <int SPLIT, int TP, bool SH>
 __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, const f16 *__restrict__ hin,
                                                                  const uint8_t *__restrict__ codes,
                                                                  const uint8_t *__restrict__ scales,
                                                                  const float *__restrict__ gscale, int K, int I,
-                                                                 float *__restrict__ ws, int first)
+                                                                 float *__restrict__ ws, int first, SharedW2 shw)
 {
     using G = Geo<SPLIT>;
     constexpr int NT = 2 * TP;            // output tiles per wave
@@ -285,12 +331,13 @@ __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, con
     __shared__ TileStage st;
     const int ntiles = K >> 4;
     const int upt = (ntiles + UT - 1) / UT;
+    const int Ts = SH ? (shw.M + 15) >> 4 : 0;  // shared expert tiles, before the plan's
     int64_t u0, u1;
-    if (!unit_range((int64_t)pv.hdr[3] * upt, first, u0, u1)) return;
+    if (!unit_range((int64_t)(Ts + pv.hdr[3]) * upt, first, u0, u1)) return;
     const int t_lo = (int)(u0 / upt);
     const G g(I);
     const size_t crow = (size_t)I >> 1, srow = (size_t)I >> 4;
-    stage_tiles(pv, st, t_lo, (int)((u1 - 1) / upt) - t_lo + 1, 0);
+    stage_tiles<SH>(pv, st, t_lo, (int)((u1 - 1) / upt) - t_lo + 1, 0, Ts, SH ? shw.M : 0);
 
     int cur = -1;
     f16x8 af[4][4];
@@ -298,37 +345,48 @@ __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, con
     auto load_unit = [&](int64_t u, RawChunk (&w)[NT]) {
         const int ti = (int)(u / upt) - t_lo;
         const int nt0 = (int)(u % upt) * UT + g.sub * NT;
-        const size_t eb = (size_t)st.e[ti] * K;
+        const int e = st.e[ti];
+        const uint8_t *cb = !SH || e >= 0 ? codes : shw.codes, *sb = !SH || e >= 0 ? scales : shw.scales;
+        const size_t eb = !SH || e >= 0 ? (size_t)e * K : 0;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const size_t r = eb + min(nt0 + t, ntiles - 1) * 16 + g.n;
-            w[t] = load_chunk(codes + r * crow, scales + r * srow, g.kb_ld, g.q_ld);
+            w[t] = load_chunk(cb + r * crow, sb + r * srow, g.kb_ld, g.q_ld);
         }
     };
     // One unit: math on `w`, next unit's weights into `wn` (the buffers alternate).
     auto step = [&](int64_t u, RawChunk (&w)[NT], RawChunk (&wn)[NT]) {
         const int ti = (int)(u / upt) - t_lo;
         const int nt0 = (int)(u % upt) * UT + g.sub * NT;
-        const int e = st.e[ti], cnt = st.cnt[ti];
+        const int e = SH ? __builtin_amdgcn_readfirstlane(st.e[ti]) : st.e[ti], cnt = st.cnt[ti], base = st.base[ti];
         const bool working = g.chunk && nt0 < ntiles;
+        // With the shared expert the global scale is a select of two loads: read it before the
+        // prefetch below, so that waiting for it never waits for that.
+        float gs = 0.f;
+        if constexpr (SH) gs = e >= 0 ? gscale[e] : shw.gscale[0];
         if (ti != cur) {
             cur = ti;
-            load_a_chunk(af, hin + (size_t)st.arow[ti][g.n] * I, g.qv && g.n < cnt, g.kb, g.q);
+            const f16 *ha = !SH || e >= 0 ? hin : reinterpret_cast<const f16 *>(shw.h);
+            load_a_chunk(af, ha + (size_t)st.arow[ti][g.n] * I, g.qv && g.n < cnt, g.kb, g.q);
         }
+        // Row `row`'s output: its pair's row of ws, or for the shared expert the token's row of y.
+        auto out_row = [&](int row) {
+            return !SH || e >= 0 ? ws + (size_t)st.pair[ti][row] * K : shw.y + (size_t)(base + row) * K;
+        };
         load_unit(u + 1 < u1 ? u + 1 : u, wn);  // the last unit re-reads itself
         __builtin_amdgcn_sched_barrier(0);      // keep those loads ahead of this unit's math
         f32x4 acc[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         mma_chunk<NT>(w, af, g.qv, acc);
-        const float gs = gscale[e];
+        if constexpr (!SH) gs = gscale[e];
         if constexpr (SPLIT == 1) {
             if (working) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int row = 4 * g.q + j;
                     if (row < cnt) {
-                        float *y = ws + (size_t)st.pair[ti][row] * K + nt0 * 16 + g.n;
+                        float *y = out_row(row) + nt0 * 16 + g.n;
 #pragma unroll
                         for (int t = 0; t < NT; ++t)
                             if (nt0 + t < ntiles) y[16 * t] = acc[t][j] * gs;
@@ -354,7 +412,7 @@ __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, con
                     if (ntx < ntiles && row < cnt) {
                         float Y = part[gp * SPLIT][t][row][col];
                         for (int cc = 1; cc < g.S; ++cc) Y += part[gp * SPLIT + cc][t][row][col];
-                        ws[(size_t)st.pair[ti][row] * K + ntx * 16 + col] = Y * gs;
+                        out_row(row)[ntx * 16 + col] = Y * gs;
                     }
                 }
             lds_barrier();
@@ -416,7 +474,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(const int32_t *__restrict__
         s3 = fmaf(g, v.w, s3);
     }
     typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-    *reinterpret_cast<f16x4 *>(out + (size_t)t * K + n) = f16x4{(f16)s0, (f16)s1, (f16)s2, (f16)s3};
+    *reinterpret_cast<f16x4 *>(out + (size_t)t * K + n) = f16x4{f16_of_f32(s0), f16_of_f32(s1), f16_of_f32(s2), f16_of_f32(s3)};
 }
 
 // ---- W2 + reduction, token-major (small batches) -----------------------------------------------------
@@ -525,7 +583,125 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
         for (int k = 0; k < topk; ++k)
             if (s_e[k] >= 0) acc = fmaf(s_w[k], yk[k][threadIdx.x], acc);
         if (sh.y) acc = fmaf(sh.sigma[t], sh.y[(size_t)t * K + nt * 16 + threadIdx.x], acc);  // shared expert last
-        out[(size_t)t * K + nt * 16 + threadIdx.x] = (f16)acc;
+        out[(size_t)t * K + nt * 16 + threadIdx.x] = f16_of_f32(acc);
+    }
+}
+
+//
+// w2_token_shared_kernel: w2_token_kernel with slot topk the shared expert (SharedW2): row t of its
+// h, its own weights, weight sigma, added after the routed slots. The routed-only kernel is kept
+// separate so that it carries none of this.
+__global__ __launch_bounds__(256, W2T_OCC) void w2_token_shared_kernel(PlanView pv, int M, int topk, const f16 *__restrict__ hin,
+                                                          const uint8_t *__restrict__ codes,
+                                                          const uint8_t *__restrict__ scales,
+                                                          const float *__restrict__ gscale, int K, int I,
+                                                          const float *__restrict__ tw, SharedW2 shw,
+                                                          f16 *__restrict__ out)
+{
+    constexpr int NS = MAX_TOPK + 1;
+    __shared__ float yk[NS][16];
+    __shared__ int s_row[NS], s_e[NS];
+    __shared__ float s_w[NS];
+    __shared__ __attribute__((aligned(16))) f16 s_h[NS][KCHUNK];  // the slots' h rows (one-chunk case)
+    const int ntiles = K >> 4;
+    const int G = M * ntiles;
+    const int per = (G + 7) >> 3;
+    const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);  // XCD-aware numbering
+    if (item >= G) return;
+    const int nt = item / M, t = item - nt * M;
+    const int nslot = topk + 1;  // slot topk: the shared expert
+    if ((int)threadIdx.x < topk) {
+        const int p = t * topk + threadIdx.x;
+        const int j = pv.pos_of_pair[p];
+        s_row[threadIdx.x] = j;
+        s_e[threadIdx.x] = j >= 0 ? pv.pair_expert[p] : -1;
+        s_w[threadIdx.x] = tw[p];
+    } else if ((int)threadIdx.x == topk) {
+        s_row[topk] = t;
+        s_e[topk] = 0;
+        s_w[topk] = shw.sigma[t];
+    }
+    __syncthreads();
+    auto slot_h = [&](int k) { return k < topk ? hin : reinterpret_cast<const f16 *>(shw.h); };
+    auto slot_codes = [&](int k) { return k < topk ? codes : shw.codes; };
+    auto slot_scales = [&](int k) { return k < topk ? scales : shw.scales; };
+    auto slot_gs = [&](int k) { return k < topk ? gscale[s_e[k]] : shw.gscale[0]; };
+    auto slot_row0 = [&](int k, int e) { return (k < topk ? (size_t)e * K : 0) + nt * 16; };
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, q = lane >> 4;
+    const int S = num_chunks(I);
+    const size_t crow = (size_t)I >> 1, srow = (size_t)I >> 4;
+    if (S == 1) {
+        // One chunk (I <= 512). Stage the valid slots' h rows in LDS (16-byte pieces), and load
+        // each wave's packed rows for up to three slots at once, so the latencies overlap.
+        const int pieces = I >> 3;
+        for (int idx = threadIdx.x; idx < nslot * pieces; idx += 256) {
+            const int k = idx / pieces, pc = idx - k * pieces;
+            if (s_e[k] >= 0)
+                *reinterpret_cast<u32x4 *>(&s_h[k][8 * pc]) =
+                    *reinterpret_cast<const u32x4 *>(slot_h(k) + (size_t)s_row[k] * I + 8 * pc);
+        }
+        const int groups = I >> 7;
+        const bool qv = q < groups;
+        const int q_ld = qv ? q : groups - 1;
+        const int ngroups = (nslot + 11) / 12;  // block-uniform trip count (the loop holds a barrier)
+        for (int gi = 0; gi < ngroups; ++gi) {
+            const int k0 = wave + 12 * gi;
+            RawChunk w[3];
+#pragma unroll
+            for (int g = 0; g < 3; ++g) {
+                const int k = k0 + 4 * g;
+                const int e = (k < nslot && s_e[k] >= 0) ? s_e[k] : 0;  // idle slots read expert 0, unused
+                const int ks = k < nslot ? k : 0;
+                const size_t wr = slot_row0(ks, e) + n;
+                w[g] = load_chunk(slot_codes(ks) + wr * crow, slot_scales(ks) + wr * srow, 0, q_ld);
+            }
+            if (gi == 0) __syncthreads();  // s_h staged; it is not written again
+#pragma unroll
+            for (int g = 0; g < 3; ++g) {
+                const int k = k0 + 4 * g;
+                if (k >= nslot || s_e[k] < 0) continue;  // wave-uniform
+                f16x8 af[4][4];
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+                    for (int ss = 0; ss < 4; ++ss) {
+                        const f16x8 v = *reinterpret_cast<const f16x8 *>(&s_h[k][128 * q_ld + 32 * bb + 8 * ss]);
+                        af[bb][ss] = (n == 0 && qv) ? v : zero8();  // row 0 of the tile is the pair
+                    }
+                f32x4 ca[1] = {{0.f, 0.f, 0.f, 0.f}};
+                mma_chunk<1>(reinterpret_cast<const RawChunk(&)[1]>(w[g]), af, qv, ca);
+                if (q == 0) yk[k][n] = ca[0][0] * slot_gs(k);
+            }
+        }
+    } else {
+        for (int k = wave; k < nslot; k += 4) {
+            const int e = s_e[k];
+            if (e < 0) continue;  // wave-uniform
+            const size_t wr = slot_row0(k, e) + n;
+            const uint8_t *cb = slot_codes(k), *sb = slot_scales(k);
+            const f16 *hr = slot_h(k) + (size_t)s_row[k] * I;
+            f32x4 tot = {-0.f, -0.f, -0.f, -0.f};  // -0 + x == x: chunk 0 needs no special case
+            for (int c = 0; c < S; ++c) {
+                const int kb = c * KCHUNK;
+                const int groups = min(KCHUNK, I - kb) >> 7;
+                const bool qv = q < groups;
+                const RawChunk w = load_chunk(cb + wr * crow, sb + wr * srow, kb, qv ? q : groups - 1);
+                f16x8 af[4][4];
+                load_a_chunk(af, hr, n == 0 && qv, kb, q);  // the pair's h row in row 0 of the tile
+                f32x4 ca[1] = {{0.f, 0.f, 0.f, 0.f}};
+                mma_chunk<1>(reinterpret_cast<const RawChunk(&)[1]>(w), af, qv, ca);
+                tot += ca[0];
+            }
+            if (q == 0) yk[k][n] = tot[0] * slot_gs(k);  // row 0 of the tile: lanes 0..15, register 0
+        }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < 16) {
+        float acc = 0.f;
+        for (int k = 0; k < topk; ++k)
+            if (s_e[k] >= 0) acc = fmaf(s_w[k], yk[k][threadIdx.x], acc);
+        acc = fmaf(s_w[topk], yk[topk][threadIdx.x], acc);  // the shared expert last
+        out[(size_t)t * K + nt * 16 + threadIdx.x] = f16_of_f32(acc);
     }
 }
 
@@ -557,46 +733,56 @@ unsigned stream_grid(int occ, int64_t units_max, int64_t t_max, int *cus_out)
 }  // namespace
 
 int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, const nvfp4_weights &w, int32_t layout,
-            uint16_t *h, hipStream_t s)
+            uint16_t *h, hipStream_t s, SharedW13 shx)
 {
     const int K = w.k, I = w.rows / 2;
     const int split = split_for(K);
     const int sl = (4 / split) * W13_TP;
     const int upt = (I / 16 + sl - 1) / sl;
+    t_max += (shx.M + 15) / 16;  // the shared expert's tiles
     int cus = 0;
     const dim3 grid(stream_grid(W13_OCC, t_max * upt, t_max, &cus)), block(256);
     const int first = W13_OCC > 1 ? cus : (int)grid.x;  // one block per CU resident first
     const f16 *xp = reinterpret_cast<const f16 *>(x);
     f16 *hp = reinterpret_cast<f16 *>(h);
     switch (split) {
-    case 1: return launch(w13_swiglu_stream_kernel<1, W13_TP>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first);
-    case 2: return launch(w13_swiglu_stream_kernel<2, W13_TP>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first);
-    default: return launch(w13_swiglu_stream_kernel<4, W13_TP>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first);
+    case 1: return launch(shx.M > 0 ? w13_swiglu_stream_kernel<1, W13_TP, true> : w13_swiglu_stream_kernel<1, W13_TP, false>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx);
+    case 2: return launch(shx.M > 0 ? w13_swiglu_stream_kernel<2, W13_TP, true> : w13_swiglu_stream_kernel<2, W13_TP, false>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx);
+    default: return launch(shx.M > 0 ? w13_swiglu_stream_kernel<4, W13_TP, true> : w13_swiglu_stream_kernel<4, W13_TP, false>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx);
     }
 }
 
 int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uint16_t *h, const nvfp4_weights &w,
-           const float *topk_weights, uint16_t *out, float *ws, hipStream_t s, SharedTerm sh)
+           const float *topk_weights, uint16_t *out, float *ws, hipStream_t s, SharedTerm sh, SharedW2 shw)
 {
     const int K = w.rows, I = w.k;
     if (use_token_w2((int64_t)M * topk, w.groups)) {
         const int64_t G = (int64_t)M * (K / 16);
+        if (shw.M > 0)
+            return launch(w2_token_shared_kernel, dim3((unsigned)((G + 7) / 8 * 8)), dim3(256), 0, s, pv, M, topk,
+                          reinterpret_cast<const f16 *>(h), w.codes, w.scales, w.global_scale, K, I, topk_weights,
+                          shw, reinterpret_cast<f16 *>(out));
         return launch(w2_token_kernel, dim3((unsigned)((G + 7) / 8 * 8)), dim3(256), 0, s, pv, M, topk,
                       reinterpret_cast<const f16 *>(h), w.codes, w.scales, w.global_scale, K, I, topk_weights, sh,
                       reinterpret_cast<f16 *>(out));
     }
+    if (shw.M > 0) {  // the shared tiles write y; the reduction adds sigma * y after the routed slots
+        sh.y = shw.y;
+        sh.sigma = shw.sigma;
+    }
     const int split = split_for(I);
     const int ut = (4 / split) * 2 * W2_TP;
     const int upt = (K / 16 + ut - 1) / ut;
+    t_max += (shw.M + 15) / 16;
     int cus = 0;
     const dim3 grid(stream_grid(W2_OCC, t_max * upt, t_max, &cus)), block(256);
     const int first = W2_OCC > 1 ? cus : (int)grid.x;
     const f16 *hp = reinterpret_cast<const f16 *>(h);
     int st;
     switch (split) {
-    case 1: st = launch(w2_stream_kernel<1, W2_TP>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws, first); break;
-    case 2: st = launch(w2_stream_kernel<2, W2_TP>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws, first); break;
-    default: st = launch(w2_stream_kernel<4, W2_TP>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws, first); break;
+    case 1: st = launch(shw.M > 0 ? w2_stream_kernel<1, W2_TP, true> : w2_stream_kernel<1, W2_TP, false>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws, first, shw); break;
+    case 2: st = launch(shw.M > 0 ? w2_stream_kernel<2, W2_TP, true> : w2_stream_kernel<2, W2_TP, false>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws, first, shw); break;
+    default: st = launch(shw.M > 0 ? w2_stream_kernel<4, W2_TP, true> : w2_stream_kernel<4, W2_TP, false>, grid, block, 0, s, pv, hp, w.codes, w.scales, w.global_scale, K, I, ws, first, shw); break;
     }
     if (st != NVFP4_OK) return st;
     return run_reduce(pv, M, topk, K, topk_weights, ws, out, s, sh);

@@ -341,8 +341,8 @@ __global__ __launch_bounds__(256, 1) void w13_swiglu_prefill_kernel(PlanView pv,
                     const int row = 16 * r + 4 * q + j;
                     if (row < rows) {
                         f16 *hr = h + (size_t)(base + rp + row) * I + it0 * 16 + n;
-                        hr[0] = (f16)swiglu(tot[r][0][j] * gs, tot[r][1][j] * gs);
-                        if (it0 + 1 < itiles) hr[16] = (f16)swiglu(tot[r][2][j] * gs, tot[r][3][j] * gs);
+                        hr[0] = f16_of_f32(swiglu(tot[r][0][j] * gs, tot[r][1][j] * gs));
+                        if (it0 + 1 < itiles) hr[16] = f16_of_f32(swiglu(tot[r][2][j] * gs, tot[r][3][j] * gs));
                     }
                 }
             }

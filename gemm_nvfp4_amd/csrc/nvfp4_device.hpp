@@ -140,4 +140,75 @@ __device__ __forceinline__ float swiglu(float g, float u)
     return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
+// fp16_rne of an FP32 value that is already rounded to FP32: every fp16 output of the library (h,
+// the MoE output, the dense projections) is one conversion of an FP32 result. The empty asm keeps
+// the compiler from merging the conversion into the multiply or fmaf that produced x (a
+// mixed-precision FMA would round the exact result to fp16 once, which differs at ties), so every
+// kernel that writes the same output rounds it the same way.
+__device__ __forceinline__ f16 f16_of_f32(float x)
+{
+    asm volatile("" : "+v"(x));
+    return (f16)x;
+}
+
+// An FP32 result to the output type: fp16 through f16_of_f32, FP32 as is.
+template <typename OUT>
+__device__ __forceinline__ OUT to_out(float x)
+{
+    if constexpr (sizeof(OUT) == 2) return f16_of_f32(x);
+    else return x;
+}
+
+// One wave's dot product x . g over K elements (K % 8 == 0, both 16-byte aligned), in one fixed
+// order: lane l sums the 8-element pieces l, l + 64, ... with fmaf, then a butterfly over the 64
+// lanes. Every kernel that computes a gate calls this, so they agree bitwise. All lanes get the sum.
+__device__ __forceinline__ float wave_dot_f16(const f16 *x, const f16 *g, int K)
+{
+    const int lane = threadIdx.x & 63, pieces = K >> 3;
+    float z = 0.0f;
+#pragma unroll 4
+    for (int pc = lane; pc < pieces; pc += 64) {
+        const f16x8 a = *reinterpret_cast<const f16x8 *>(x + 8 * pc);
+        const f16x8 b = *reinterpret_cast<const f16x8 *>(g + 8 * pc);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z = fmaf((float)a[e], (float)b[e], z);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
+    return __shfl(z, 0, 64);
+}
+
+// wave_dot_f16 for K <= 2048 in two halves, the same sum bitwise: wave_dot_load issues the lane's
+// (at most four) pieces, wave_dot_sum adds them once they are needed, so other work can hide the
+// loads' latency.
+struct WaveDotRegs {
+    f16x8 a[4], b[4];
+};
+__device__ __forceinline__ void wave_dot_load(WaveDotRegs &r, const f16 *x, const f16 *g, int K)
+{
+    const int lane = threadIdx.x & 63, pieces = K >> 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int pc = lane + 64 * i;
+        if (pc < pieces) {
+            r.a[i] = *reinterpret_cast<const f16x8 *>(x + 8 * pc);
+            r.b[i] = *reinterpret_cast<const f16x8 *>(g + 8 * pc);
+        }
+    }
+}
+__device__ __forceinline__ float wave_dot_sum(const WaveDotRegs &r, int K)
+{
+    const int lane = threadIdx.x & 63, pieces = K >> 3;
+    float z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i < pieces) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z = fmaf((float)r.a[i][e], (float)r.b[i][e], z);
+        }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
+    return __shfl(z, 0, 64);
+}
+
 }  // namespace nvfp4

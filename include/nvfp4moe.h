@@ -190,6 +190,32 @@ int nvfp4_moe_w2_reduce_shared(const void *plan, int32_t M, int32_t topk, int32_
                                const float *shared_sigma, uint16_t *out, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * The same shared expert and gate run inside the routed launches (the "shared gate" among the
+ * fused MoE parts, no-MTP page, "Scope and related PRs"): its rows join the routed W13 and W2
+ * launches as extra tiles, so it adds no launches of its own. Results are bitwise those of
+ * nvfp4_moe_w13_swiglu + nvfp4_moe_shared_expert, and of nvfp4_moe_w2_reduce_shared.
+ *   nvfp4_moe_w13_swiglu_with_shared: nvfp4_moe_w13_swiglu's arguments, plus shared_w13
+ *     (groups = 1, rows = 2Is, k = K, same layout), gate fp16 [K], and the outputs shared_h fp16
+ *     [M][Is] and shared_sigma FP32 [M] (as in nvfp4_moe_shared_expert).
+ *   nvfp4_moe_w2_reduce_with_shared: nvfp4_moe_w2_reduce's arguments, plus shared_h (from the call
+ *     above), shared_w2 (groups = 1, rows = K, k = Is), shared_sigma, and shared_y FP32 [M][K],
+ *     scratch that the call may overwrite with the shared expert's unrounded output.
+ *     out = fp16_rne(fmaf(shared_sigma[t], y_shared[t][n], routed slot chain)).
+ * Requirements: those of the routed calls; Is % 16 == 0 (W13) and Is % 128 == 0 (W2); shared_h,
+ * shared_y 16-byte aligned; gate 2-byte aligned. The one-launch form needs Is == I, a 16-byte
+ * aligned gate and the streaming (not the prefill) regime; otherwise the call runs the shared
+ * expert's own launches after the routed one, with the same results.
+ * --------------------------------------------------------------------------------------------- */
+int nvfp4_moe_w13_swiglu_with_shared(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16_t *x,
+                                     const nvfp4_weights *w13, int32_t layout, uint16_t *h,
+                                     const nvfp4_weights *shared_w13, const uint16_t *gate, uint16_t *shared_h,
+                                     float *shared_sigma, void *stream);
+int nvfp4_moe_w2_reduce_with_shared(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16_t *h,
+                                    const nvfp4_weights *w2, const float *topk_weights, const uint16_t *shared_h,
+                                    const nvfp4_weights *shared_w2, const float *shared_sigma, float *shared_y,
+                                    uint16_t *out, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Dense NVFP4 projection (the "QPN" projection, DFlash2 page, "Purpose" and "TP4-only NVFP4
  * verifier follow-up"):
  *   y[m][n] = fp16_rne( global * sum_k x[m][k] * e2m1*e4m3 ),  FP32 accumulation.

@@ -32,7 +32,8 @@ def test_header_declares_the_expected_entry_points():
     assert declared() == sorted([
         "nvfp4_abi_version", "nvfp4_status_str", "nvfp4_moe_plan_bytes", "nvfp4_moe_plan", "nvfp4_moe_route",
         "nvfp4_moe_w13_swiglu", "nvfp4_moe_w2_workspace_bytes", "nvfp4_moe_w2_reduce", "nvfp4_linear",
-        "nvfp4_linear_swiglu", "nvfp4_linear_fp8", "nvfp4_moe_shared_expert", "nvfp4_moe_w2_reduce_shared"])
+        "nvfp4_linear_swiglu", "nvfp4_linear_fp8", "nvfp4_moe_shared_expert", "nvfp4_moe_w2_reduce_shared",
+        "nvfp4_moe_w13_swiglu_with_shared", "nvfp4_moe_w2_reduce_with_shared"])
 
 
 def test_library_exports_every_declared_function():
@@ -98,6 +99,28 @@ def test_argument_checks_fail_closed(L):
                                      fake, fake, fake, fake, null) == 5
     assert L.nvfp4_moe_w2_reduce_shared(fake, 4, 2, 8, fake, C.byref(nvfp4_weights(fake, fake, fake, 8, 256, 128)),
                                         fake, null, fake, fake, fake, 1 << 20, null) == 1
+    # shared expert inside the routed launches: shapes must agree, every pointer is required
+    rw13 = nvfp4_weights(fake, fake, fake, 8, 256, 256)          # E = 8, I = 128, K = 256
+    sw13 = nvfp4_weights(fake, fake, fake, 1, 256, 256)
+    assert L.nvfp4_moe_w13_swiglu_with_shared(fake, 4, 2, 8, fake, C.byref(rw13), 0, fake,
+                                              C.byref(nvfp4_weights(fake, fake, fake, 1, 256, 128)),
+                                              fake, fake, fake, null) == 2   # shared k != K
+    assert L.nvfp4_moe_w13_swiglu_with_shared(fake, 4, 2, 8, fake, C.byref(rw13), 0, fake, C.byref(sw13),
+                                              null, fake, fake, null) == 1   # no gate
+    assert L.nvfp4_moe_w13_swiglu_with_shared(fake, 4, 2, 8, fake, C.byref(rw13), 0, fake, C.byref(sw13),
+                                              odd, fake, fake, null) == 3    # gate not 2-byte aligned
+    assert L.nvfp4_moe_w13_swiglu_with_shared(null, 0, 2, 8, null, C.byref(rw13), 0, null, C.byref(sw13),
+                                              null, null, null, null) == 0   # M = 0
+    rw2 = nvfp4_weights(fake, fake, fake, 8, 256, 128)           # E = 8, K = 256, I = 128
+    assert L.nvfp4_moe_w2_reduce_with_shared(fake, 4, 2, 8, fake, C.byref(rw2), fake, fake,
+                                             C.byref(nvfp4_weights(fake, fake, fake, 1, 128, 128)), fake, fake,
+                                             fake, fake, 1 << 20, null) == 2  # shared rows != K
+    assert L.nvfp4_moe_w2_reduce_with_shared(fake, 4, 2, 8, fake, C.byref(rw2), fake, fake,
+                                             C.byref(nvfp4_weights(fake, fake, fake, 1, 256, 64)), fake, fake,
+                                             fake, fake, 1 << 20, null) == 5  # shared I % 128
+    assert L.nvfp4_moe_w2_reduce_with_shared(fake, 4, 2, 8, fake, C.byref(rw2), fake, fake,
+                                             C.byref(nvfp4_weights(fake, fake, fake, 1, 256, 128)), fake, null,
+                                             fake, fake, 1 << 20, null) == 1  # no shared_y
     # channel-FP8 projection
     from gemm_nvfp4_amd._lib import fp8_channel_weights as f8
     assert L.nvfp4_linear_fp8(fake, 4, C.byref(f8(fake, fake, 64, 96)), fake, null) == 5     # K % 128

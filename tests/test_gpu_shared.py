@@ -104,3 +104,55 @@ def test_zero_shared_term_is_the_routed_output():
     out = G.nvfp4_moe_w2_reduce_shared(res["plan"], sh.m, sh.topk, sh.e, res["h"], d["w2"], d["tw"], zeros_y, zeros_s)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), res["out"].view(torch.int16))
+
+
+def _run_fused(case, shared, layout=0, res=None):
+    """The shared expert inside the routed W13 and W2 launches (nvfp4_moe_*_with_shared), on the
+    same plan and device inputs as `res` (a run_moe result)."""
+    sh = case["shape"]
+    res = run_moe(case, layout) if res is None else res
+    d = res["dev"]
+    w13s, w2s, g = _shared_dev(shared)
+    h, hs, sg = G.nvfp4_moe_w13_swiglu_with_shared(res["plan"], sh.m, sh.topk, sh.e, d["x"], d["w13"], w13s, g,
+                                                   layout=layout)
+    out = G.nvfp4_moe_w2_reduce_with_shared(res["plan"], sh.m, sh.topk, sh.e, h, d["w2"], d["tw"], hs, w2s, sg)
+    torch.cuda.synchronize()
+    return h, hs, sg, out, res
+
+
+@pytest.mark.parametrize("shape,routing,i_shared,layout", [
+    (S.MoEShape(m=5, e=512, topk=10, k=2048, i=512), "uniform", 512, 0),      # token-major W2: shared slot
+    (S.DECODE, "uniform", 512, 0),                                             # expert-major: shared tiles
+    (S.MoEShape(m=17, e=64, topk=4, k=256, i=128), "zipf", 128, 1),           # two shared tiles, 17 tokens
+    (S.MoEShape(m=2, e=32, topk=4, k=2048, i=2048), "uniform", 2048, 0),      # four chunks, token-major
+    (S.MoEShape(m=9, e=32, topk=4, k=2048, i=2048), "repeat_invalid", 2048, 0),  # four chunks, expert-major
+    (S.DECODE, "uniform", 256, 0),                                             # shared I != I: own launches
+    (S.MoEShape(m=600, e=8, topk=2, k=512, i=128), "repeat_invalid", 128, 0),  # prefill: own launches
+])
+def test_fused_shared_equals_separate_launches(shape, routing, i_shared, layout):
+    """The one-launch forms give bitwise the separate launches' h, shared h, gate and output (and
+    fall back to those launches where they do not apply)."""
+    case = S.moe_case(shape, routing=routing, route_pattern=61, weights=None)
+    shared = S.shared_expert(S.rng_for(S.WORKLOAD_IDS["decode"], 53, shape.m), shape.k, i_shared)
+    h, hs, sg, out, res = _run_fused(case, shared, layout)
+    d = res["dev"]
+    w13s, w2s, g = _shared_dev(shared)
+    ys_ref, sg_ref, hs_ref = G.nvfp4_moe_shared_expert(d["x"], w13s, w2s, g, layout=layout)
+    out_ref = G.nvfp4_moe_w2_reduce_shared(res["plan"], shape.m, shape.topk, shape.e, res["h"], d["w2"], d["tw"],
+                                           ys_ref, sg_ref)
+    torch.cuda.synchronize()
+    nv = int(G.plan_fields(res["plan"], shape.m, shape.topk, shape.e)["n_valid"])
+    assert torch.equal(h[:nv].view(torch.int16), res["h"][:nv].view(torch.int16))
+    assert torch.equal(hs.view(torch.int16), hs_ref.view(torch.int16))
+    assert torch.equal(sg.view(torch.int32), sg_ref.view(torch.int32))
+    assert torch.equal(out.view(torch.int16), out_ref.view(torch.int16))
+
+
+def test_fused_shared_matches_oracle(orc):
+    case = S.moe_case(S.DECODE, route_pattern=62)
+    shared = S.shared_expert(S.rng_for(S.WORKLOAD_IDS["decode"], 54, 0), S.DECODE.k, S.DECODE.i)
+    _, _, sg, out, _ = _run_fused(case, shared)
+    ref, _, _ = orc.moe_with_shared(case, shared)
+    assert_rows_close(to_np64(out), ref, "fused moe+shared")
+    sg_ref = orc.shared_gate(case["x"], shared["g"])
+    assert np.all(np.abs(sg.cpu().numpy() - sg_ref) <= 1e-6 + 1e-5 * sg_ref)
