@@ -480,7 +480,7 @@ def main():
         "us_per_layer": head["us_per_layer"], "hbm_frac": head["hbm_frac"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "w13_swiglu_stream_kernel<4, 1>", "us_per_launch": round(k_us, 3),
+                     "kernel": "w13_swiglu_stream_kernel<4, 1, false>", "us_per_launch": round(k_us, 3),
                      "algorithmic_bytes_per_launch": round(k_bytes)},
         "launch_floor_us": round(floor, 3),
         "sweep": sweep, "prefill": prefill, "dense": dense, "dense_fp8": fp8, "mlp": mlp, "with_shared_expert": shared, "route": route, "cpu_baseline": cpu,
