@@ -440,17 +440,18 @@ __global__ __launch_bounds__(256) void reduce_kernel(const int32_t *__restrict__
     if (n >= K) return;
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
     // Slots go in batches of 16: a batch's rows are all loaded before the first fmaf, so their
-    // latencies overlap, then folded in slot order.
+    // latencies overlap, then folded in slot order. Each y row is read exactly once, so the loads
+    // are non-temporal (no cache allocation): at 8192 tokens (671 MB of y) 153 -> 115 us on MI355X.
     constexpr int BATCH = 16;
     for (int k0 = 0; k0 < topk; k0 += BATCH) {
-        float4 y[BATCH];
+        f32x4 y[BATCH];
         float wk[BATCH];
         int pos[BATCH];
 #pragma unroll
         for (int i = 0; i < BATCH; ++i)
             if (k0 + i < topk) {
                 const size_t p = (size_t)t * topk + k0 + i;
-                y[i] = *reinterpret_cast<const float4 *>(ws + p * K + n);
+                y[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(ws + p * K + n));
                 pos[i] = pos_of_pair[p];
                 wk[i] = tw[p];
             }
@@ -458,10 +459,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(const int32_t *__restrict__
         for (int i = 0; i < BATCH; ++i) {
             if (k0 + i < topk && pos[i] >= 0) {
                 const float w = wk[i];
-                s0 = fmaf(w, y[i].x, s0);
-                s1 = fmaf(w, y[i].y, s1);
-                s2 = fmaf(w, y[i].z, s2);
-                s3 = fmaf(w, y[i].w, s3);
+                s0 = fmaf(w, y[i][0], s0);
+                s1 = fmaf(w, y[i][1], s1);
+                s2 = fmaf(w, y[i][2], s2);
+                s3 = fmaf(w, y[i][3], s3);
             }
         }
     }
