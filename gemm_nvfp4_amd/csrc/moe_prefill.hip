@@ -6,11 +6,14 @@
 // byte), so the design goal is MFMA throughput. gfx950 design:
 //   * A block owns one active expert and a slice of its output columns: 128 i values (their gate
 //     and up rows) for W13, or 256 output rows for W2. It walks the expert's bucket rows in passes
-//     of 80. Blocks of one expert are numbered consecutively and mapped to the same XCD, so they
-//     share the expert's activation rows in that XCD's L2.
-//   * One wave per SIMD, up to 512 registers. Each wave owns four 16-wide weight tiles (W13: gate
-//     and up of two i slices; W2: four output tiles) and up to five row tiles: 20 independent
-//     accumulator chains keep the matrix pipe busy. Each A fragment read from LDS feeds 4 MFMAs.
+//     (96 rows for W13, 80 for the multi-chunk W2, 48 for the one-chunk W2). Blocks of one expert
+//     are numbered consecutively and mapped to the same XCD, so they share the expert's activation
+//     rows in that XCD's L2.
+//   * Each wave owns four 16-wide weight tiles (W13: gate and up of two i slices; W2: four output
+//     tiles). W13 runs one wave per SIMD (up to 512 registers) with six row tiles: 24 independent
+//     accumulator chains keep the matrix pipe busy and each A fragment read from LDS feeds 4
+//     MFMAs. The one-chunk W2 runs two blocks per CU with three row tiles, so that one block's
+//     latencies hide behind the other's MFMAs.
 //   * Per 512-element chunk a wave decodes its weights once (gfx950 fp4/fp8 converts plus one
 //     exact fp16 multiply) and reuses each B fragment for all row tiles. Packed weights are loaded
 //     one chunk ahead, a quarter at a time, into the registers the current chunk has finished with.
@@ -292,6 +295,29 @@ __device__ __forceinline__ void pass_dispatch(PrefillShared &sh, const PassSrc &
 
 // ---- W13 + SwiGLU ---------------------------------------------------------------------------------
 // Wave w of block slice nb owns i slices 8*nb + 2w and +1: tiles {gate0, up0, gate1, up1}.
+//
+// The block's passes form one stream, as in the one-chunk W2 kernel below: every pass runs five
+// row tiles (a short last pass computes padding rows that are never stored), and the next pass
+// reuses the same weight rows, so
+//   * the activation quarter ring runs on across passes (quarter g of pass p is stream quarter
+//     p*4S + g); the last two quarters of a pass stage the next pass's first two;
+//   * the weight ring wraps: the last chunk refills its quarters with chunk 0, i.e. the next
+//     pass's first chunk;
+//   * the next pass's row list is loaded at the start of a pass, stored to LDS before the first
+//     quarter's barrier and turned into load offsets after it.
+// No pass waits for a prologue, and the SwiGLU epilogue of pass p runs while pass p + 1's first
+// loads are in flight. The per-element arithmetic is pass_chunks' (chunk chains from +0, chunk
+// sums from -0 in order, global scale last).
+#ifndef NVFP4_W13_R
+#define NVFP4_W13_R 6
+#endif
+constexpr int W13_R = NVFP4_W13_R;  // row tiles per W13 pass
+constexpr int W13_ROWS = 16 * W13_R;
+struct __attribute__((aligned(16))) W13Shared {
+    f16 a[NBUF][W13_ROWS][A_ROW];  // activation quarters, as in PrefillShared
+    int arow[2][W13_ROWS];         // token of each row of pass p, in arow[p & 1]
+};
+
 __global__ __launch_bounds__(256, 1) void w13_swiglu_prefill_kernel(PlanView pv, int topk, const f16 *__restrict__ x,
                                                                      uint32_t x_bytes,
                                                                      const uint8_t *__restrict__ codes,
@@ -299,7 +325,8 @@ __global__ __launch_bounds__(256, 1) void w13_swiglu_prefill_kernel(PlanView pv,
                                                                      const float *__restrict__ gscale, int K, int I,
                                                                      int layout, f16 *__restrict__ h, int a_max)
 {
-    __shared__ PrefillShared sh;
+    constexpr int NR = W13_R;
+    __shared__ W13Shared sh;
     const int itiles = I >> 4;
     const int nblk = (itiles + 7) >> 3;  // 8 i slices per block
     const int lb = xcd_logical_block(a_max * nblk);
@@ -311,12 +338,10 @@ __global__ __launch_bounds__(256, 1) void w13_swiglu_prefill_kernel(PlanView pv,
     const int it0 = nb * 8 + 2 * wave;
     const bool working = it0 < itiles;  // the second slice may be missing (odd itiles): guarded below
     const uint32_t ebytes = (uint32_t)(2 * I) * (uint32_t)(K >> 1);  // one expert's codes
-    PassSrc src;
-    src.act = make_rsrc(x, x_bytes);
-    src.row_bytes = (uint32_t)K * 2;
-    src.codes = make_rsrc(codes + (size_t)e * ebytes, ebytes);
-    src.scales = make_rsrc(scales + (size_t)e * (ebytes >> 3), ebytes >> 3);
-    src.red = K;
+    const rsrc_t act = make_rsrc(x, x_bytes);
+    const rsrc_t rc = make_rsrc(codes + (size_t)e * ebytes, ebytes);
+    const rsrc_t rs = make_rsrc(scales + (size_t)e * (ebytes >> 3), ebytes >> 3);
+    const uint32_t row_bytes = (uint32_t)K * 2;
     uint32_t wo[PF_T];
 #pragma unroll
     for (int t = 0; t < PF_T; ++t) {
@@ -326,27 +351,149 @@ __global__ __launch_bounds__(256, 1) void w13_swiglu_prefill_kernel(PlanView pv,
         wo[t] = (uint32_t)row * (uint32_t)(K >> 1) + 64 * q;
     }
     const float gs = gscale[e];
-
-    for (int rp = 0; rp < cnt; rp += PF_ROWS) {
-        const int rows = min(PF_ROWS, cnt - rp);
-        lds_barrier();  // the previous pass is done with sh.arow
-        for (int r = threadIdx.x; r < rows; r += 256) sh.arow[r] = pv.sorted_pair[base + rp + r] / topk;
-        lds_barrier();
-        pass_dispatch(sh, src, rows, wo, working, n, q, [&](const f32x4 (&tot)[PF_R][PF_T], int nr) {
+    const int S = num_chunks(K), GQ = 4 * S;  // chunks and quarters per pass
+    const int npass = (cnt + W13_ROWS - 1) / W13_ROWS;
+    const int qs = (threadIdx.x >> 2) & 3, ps = threadIdx.x & 3, srow = threadIdx.x >> 4;  // staged piece
+    auto groups_of = [&](int c) { return min(KCHUNK, K - c * KCHUNK) >> 7; };
+    // Token of row threadIdx.x of pass p (rows past the expert's end and passes past the last read
+    // token 0: computed, never stored).
+    auto arow_load = [&](int p) {
+        const int r = p * W13_ROWS + (int)threadIdx.x;
+        return (int)threadIdx.x < W13_ROWS && p < npass && r < cnt ? pv.sorted_pair[base + r] / topk : 0;
+    };
+    auto offsets_of = [&](int p, uint32_t (&vo)[NR]) {
 #pragma unroll
-            for (int r = 0; r < PF_R; ++r) {
-                if (r >= nr) break;
+        for (int i = 0; i < NR; ++i) vo[i] = (uint32_t)sh.arow[p & 1][srow + 16 * i] * row_bytes + 256 * qs + 16 * ps;
+    };
+    // Quarter gl (0 .. 4S-1) of the pass whose row offsets are vo. Lane groups past a short
+    // chunk's end stage zeros (offsets of at least 2^31 are out of range and read as zero).
+    auto stage_load = [&](StageRegs<NR> &st, int gl, const uint32_t (&vo)[NR]) {
+        const uint32_t so = (uint32_t)((gl >> 2) * KCHUNK + AQ * (gl & 3)) * 2;
+        const uint32_t oob = qs < groups_of(gl >> 2) ? 0u : 0x80000000u;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) st.v[i] = bload16(act, vo[i] | oob, so);
+    };
+    auto stage_store = [&](const StageRegs<NR> &st, int buf) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) *reinterpret_cast<u32x4 *>(&sh.a[buf][srow + 16 * i][AQ * qs + 8 * ps]) = st.v[i];
+    };
+    RawChunk w[PF_T];
+    auto load_quarter = [&](int c, int b) {
+#pragma unroll
+        for (int t = 0; t < PF_T; ++t) {
+            w[t].codes[b] = bload16(rc, wo[t] + 16 * b, (uint32_t)c * (KCHUNK / 2));
+            if (b & 1) w[t].scales[b >> 1] = bload4(rs, (wo[t] >> 3) + 4 * (b >> 1), (uint32_t)c * (KCHUNK / 16));
+        }
+    };
+    auto buf_next = [](int v) { return v == NBUF - 1 ? 0 : v + 1; };
+
+    // Prologue: pass 0's rows, its quarters 0 and 1 in LDS, chunk 0's weights in registers.
+    {
+        const int r0 = arow_load(0);
+        if ((int)threadIdx.x < W13_ROWS) sh.arow[0][threadIdx.x] = r0;
+    }
+    __syncthreads();
+    uint32_t vo[NR], vo_next[NR];
+    offsets_of(0, vo);
+    StageRegs<NR> st;
+    stage_load(st, 0, vo);
+    stage_store(st, 0);
+    stage_load(st, 1 < GQ ? 1 : 0, vo);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) load_quarter(0, b);
+    stage_store(st, 1);
+    lds_barrier();
+
+    f32x4 tot[NR][PF_T], ca[NR][PF_T];
+    f16x8 bf[2][PF_T], av[NR];
+    f16x2 raw[PF_T][4];
+    f16x2 sc[PF_T];
+    int cur = 0;  // LDS buffer of the current quarter
+    auto cvt_step = [&](int b, int s) {
+#pragma unroll
+        for (int t = 0; t < PF_T; ++t) e2m1_pairs(raw[t], w[t].codes[b][s]);
+    };
+    auto mul_step = [&](int slot, int c, int b, int s) {
+        if (s == 0) {
+            const bool qv = q < groups_of(c);
+#pragma unroll
+            for (int t = 0; t < PF_T; ++t) sc[t] = qv ? chunk_scales(w[t], b) : f16x2{0, 0};
+        }
+#pragma unroll
+        for (int t = 0; t < PF_T; ++t) bf[slot][t] = scale8(raw[t], sc[t][s >> 1]);
+    };
+    auto a_read = [&](int r, int s, int buf) {
+        return *reinterpret_cast<const f16x8 *>(&sh.a[buf][16 * r + n][AQ * q + 8 * s]);
+    };
+    cvt_step(0, 0);
+    mul_step(0, 0, 0, 0);
+    cvt_step(0, 1);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) av[r] = a_read(r, 0, 0);
+    for (int p = 0; p < npass; ++p) {
+        const int rows = min(W13_ROWS, cnt - p * W13_ROWS);
+        int pr_next = 0;
+        // The chunk sum starts from -0, the exact identity of addition.
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int t = 0; t < PF_T; ++t) tot[r][t] = f32x4{-0.f, -0.f, -0.f, -0.f};
+        for (int c = 0; c < S; ++c) {
+            const int cn = c + 1 < S ? c + 1 : 0;  // the chunk after this one (chunk 0: the next pass)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int b = j >> 2, s = j & 3, slot = j & 1;
+                if (s == 0) {
+                    // Quarter 4c + b + 2, of this pass or the next one.
+                    const int g2 = 4 * c + b + 2;
+                    if (g2 < GQ) stage_load(st, g2, vo);
+                    else stage_load(st, g2 - GQ, vo_next);
+                }
+                if (c == 0 && j == 0) pr_next = arow_load(p + 1);
+                const int sn = (j + 1) & 3, bn = ((j + 1) >> 2) & 3, bufn = s == 3 ? buf_next(cur) : cur;
+                mul_step(slot ^ 1, j < 15 ? c : cn, bn, sn);
+                cvt_step(((j + 2) >> 2) & 3, (j + 2) & 3);
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+#pragma unroll
+                    for (int t = 0; t < PF_T; ++t)
+                        ca[r][t] = mfma_step(av[r], bf[slot][t], j == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : ca[r][t]);
+                    av[r] = a_read(r, sn, bufn);
+                }
+                interleave_step<NR>();
+                __builtin_amdgcn_sched_barrier(0);
+                if (s == 3) {
+                    // Quarter b of this chunk is fully decoded: refill it with the next chunk's bytes.
+                    load_quarter(cn, b);
+                    stage_store(st, buf_next(buf_next(cur)));
+                    // sh.arow[(p + 1) & 1] was last read two passes ago (offsets of pass p - 1).
+                    if (c == 0 && b == 0 && (int)threadIdx.x < W13_ROWS) sh.arow[(p + 1) & 1][threadIdx.x] = pr_next;
+                    lds_barrier();
+                    if (c == 0 && b == 0) offsets_of(p + 1, vo_next);
+                    cur = buf_next(cur);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int t = 0; t < PF_T; ++t) tot[r][t] += ca[r][t];
+        }
+        if (working) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int row = 16 * r + 4 * q + j;
                     if (row < rows) {
-                        f16 *hr = h + (size_t)(base + rp + row) * I + it0 * 16 + n;
+                        f16 *hr = h + (size_t)(base + p * W13_ROWS + row) * I + it0 * 16 + n;
                         hr[0] = f16_of_f32(swiglu(tot[r][0][j] * gs, tot[r][1][j] * gs));
                         if (it0 + 1 < itiles) hr[16] = f16_of_f32(swiglu(tot[r][2][j] * gs, tot[r][3][j] * gs));
                     }
                 }
-            }
-        });
+        }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) vo[i] = vo_next[i];
     }
 }
 
