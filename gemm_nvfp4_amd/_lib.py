@@ -57,6 +57,8 @@ _SIGS = {
     "nvfp4_moe_w2_reduce_with_shared": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _vp, _vp,
                                                   C.POINTER(nvfp4_weights), _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_linear_swiglu": (C.c_int, [_vp, _i32, C.POINTER(nvfp4_weights), _i32, _vp, _vp]),
+    "nvfp4_moe_plan_w13_swiglu": (C.c_int, [_vp, _i32, _i32, _i32, _vp, _sz, _vp, C.POINTER(nvfp4_weights), _i32, _vp,
+                                            _vp]),
     "nvfp4_linear_fp8": (C.c_int, [_vp, _i32, C.POINTER(fp8_channel_weights), _vp, _vp]),
 }
 
@@ -184,6 +186,22 @@ def nvfp4_moe_w13_swiglu(plan: torch.Tensor, M: int, topk: int, E: int, x: torch
     return h
 
 
+def nvfp4_moe_plan_w13_swiglu(topk_ids: torch.Tensor, E: int, x: torch.Tensor, w13: NVFP4Tensor, layout: int = 0,
+                              plan: torch.Tensor | None = None, h: torch.Tensor | None = None, stream=None):
+    """nvfp4_moe_plan followed by nvfp4_moe_w13_swiglu, one launch for small batches. Returns (plan, h)."""
+    M, topk = topk_ids.shape
+    I = w13.rows // 2
+    if plan is None:
+        plan = torch.empty(max(nvfp4_moe_plan_bytes(M, topk, E), 4) // 4, dtype=torch.int32, device=x.device)
+    if h is None:
+        h = torch.empty((M * topk, I), dtype=torch.float16, device=x.device)
+    d = w13.desc()
+    _check("nvfp4_moe_plan_w13_swiglu", lib().nvfp4_moe_plan_w13_swiglu(
+        _dev(topk_ids, "topk_ids", torch.int32), M, topk, E, _dev(plan, "plan", torch.int32), plan.numel() * 4,
+        _dev(x, "x", torch.float16), C.byref(d), layout, _dev(h, "h", torch.float16), _stream(stream)))
+    return plan, h
+
+
 def nvfp4_moe_w2_workspace_bytes(M: int, topk: int, K: int) -> int:
     return int(lib().nvfp4_moe_w2_workspace_bytes(M, topk, K))
 
@@ -297,8 +315,8 @@ def nvfp4_linear_swiglu(x: torch.Tensor, w13: NVFP4Tensor, layout: int = 0, h: t
 
 
 class MoELayer:
-    """One MoE layer call (plan, W13+SwiGLU, W2+reduce) with its buffers allocated once, so the
-    three launches can be replayed (or captured in a HIP graph) without allocation."""
+    """One MoE layer call (plan + W13+SwiGLU, then W2+reduce) with its buffers allocated once, so
+    the launches can be replayed (or captured in a HIP graph) without allocation."""
 
     def __init__(self, M: int, topk: int, w13: NVFP4Tensor, w2: NVFP4Tensor, layout: int = 0, device="cuda"):
         self.M, self.topk, self.E = M, topk, w13.groups
@@ -311,9 +329,8 @@ class MoELayer:
 
     def __call__(self, x, topk_ids, topk_weights, w13: NVFP4Tensor | None = None, w2: NVFP4Tensor | None = None,
                  stream=None):
-        nvfp4_moe_plan(topk_ids, self.E, plan=self.plan, stream=stream)
-        nvfp4_moe_w13_swiglu(self.plan, self.M, self.topk, self.E, x, w13 or self.w13, self.layout, h=self.h,
-                             stream=stream)
+        nvfp4_moe_plan_w13_swiglu(topk_ids, self.E, x, w13 or self.w13, self.layout, plan=self.plan, h=self.h,
+                                  stream=stream)
         nvfp4_moe_w2_reduce(self.plan, self.M, self.topk, self.E, self.h, w2 or self.w2, topk_weights,
                             out=self.out, ws=self.ws, stream=stream)
         return self.out

@@ -100,6 +100,42 @@ NVFP4_API int nvfp4_moe_w13_swiglu(const void *plan, int32_t M, int32_t topk, in
     return nvfp4::run_w13(nvfp4::plan_view(plan, L), L.T, topk, x, *w13, layout, h, s);
 }
 
+NVFP4_API int nvfp4_moe_plan_w13_swiglu(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E, void *plan,
+                                        size_t plan_bytes, const uint16_t *x, const nvfp4_weights *w13,
+                                        int32_t layout, uint16_t *h, void *stream)
+{
+    // Every check of nvfp4_moe_plan and nvfp4_moe_w13_swiglu, before anything is enqueued.
+    if (!plan_shape_ok(M, topk, E)) return NVFP4_ERR_SHAPE;
+    if (layout != 0 && layout != 1) return NVFP4_ERR_SHAPE;
+    if (E > nvfp4::MAX_EXPERTS) return NVFP4_ERR_UNSUPPORTED;
+    int st = check_weights(w13);
+    if (st != NVFP4_OK) return st;
+    if (w13->groups != E || w13->rows % 2 != 0) return NVFP4_ERR_SHAPE;
+    const int K = w13->k, I = w13->rows / 2;
+    if (K % 128 != 0 || K > nvfp4::MAX_MOE_RED || I % 16 != 0) return NVFP4_ERR_UNSUPPORTED;
+    if (M == 0) return NVFP4_OK;
+    if (!topk_ids || !plan || !x || !h) return NVFP4_ERR_NULL;
+    if (!aligned(topk_ids, 4) || !aligned(plan, 16) || !aligned(x, 16) || !aligned(h, 16)) return NVFP4_ERR_ALIGN;
+    const PlanLayout L = nvfp4::plan_layout(M, topk, E);
+    if (plan_bytes < (size_t)L.words * sizeof(int32_t)) return NVFP4_ERR_WORKSPACE;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t *pl = static_cast<int32_t *>(plan);
+    const bool prefill = nvfp4::use_prefill(M, L.P, E, K, I);
+    if (!prefill && nvfp4::use_fused_plan(L.P, E)) {
+        nvfp4::FusedPlan fp;
+        fp.ids = topk_ids;
+        fp.plan = pl;
+        fp.L = L;
+        fp.M = M;
+        fp.E = E;
+        return nvfp4::run_w13(nvfp4::plan_view(plan, L), L.T, topk, x, *w13, layout, h, s, {}, fp);
+    }
+    st = nvfp4::run_plan(topk_ids, M, topk, E, pl, L, s);
+    if (st != NVFP4_OK) return st;
+    if (prefill) return nvfp4::run_w13_prefill(nvfp4::plan_view(plan, L), L.A, M, topk, x, *w13, layout, h, s);
+    return nvfp4::run_w13(nvfp4::plan_view(plan, L), L.T, topk, x, *w13, layout, h, s);
+}
+
 NVFP4_API size_t nvfp4_moe_w2_workspace_bytes(int32_t M, int32_t topk, int32_t K)
 {
     if (M < 0 || topk < 1 || topk > nvfp4::MAX_TOPK || K < 1) return 0;

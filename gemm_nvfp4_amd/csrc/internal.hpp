@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <tuple>
+#include <type_traits>
 #include <utility>
 
 #include "../../include/nvfp4moe.h"
@@ -107,8 +108,18 @@ struct SharedW13 {
     float *sigma = nullptr;          // [M]
     int32_t M = 0;
 };
+// The plan built inside the W13 launch (ids == nullptr: read pv): block 0 writes it to `plan`.
+constexpr int FUSED_PLAN_PAIRS = 256;     // one pair per thread of a W13 block
+constexpr int FUSED_PLAN_EXPERTS = 1024;  // four experts per thread in the scans
+struct FusedPlan {
+    const int32_t *ids = nullptr;  // [M*topk]
+    int32_t *plan = nullptr;
+    PlanLayout L{};
+    int32_t M = 0, E = 0;
+};
+inline bool use_fused_plan(int64_t P, int32_t E) { return P <= FUSED_PLAN_PAIRS && E <= FUSED_PLAN_EXPERTS; }
 int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, const nvfp4_weights &w,
-            int32_t layout, uint16_t *h, hipStream_t s, SharedW13 shx = {});
+            int32_t layout, uint16_t *h, hipStream_t s, SharedW13 shx = {}, FusedPlan fp = {});
 // The shared expert's contribution to the MoE output (both pointers NULL: none): FP32 y [M][K] and
 // the per-token gate sigma [M], added after the routed slots as one more fmaf.
 struct SharedTerm {

@@ -29,6 +29,7 @@
 //   * A last pass sums each token's slots in slot order with fmaf and rounds to fp16 once.
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
+#include "plan_device.hpp"
 
 namespace nvfp4 {
 namespace {
@@ -114,6 +115,114 @@ __device__ __forceinline__ void stage_tiles(const PlanView &pv, TileStage &st, i
     __syncthreads();
 }
 
+// ---- the routing plan inside the W13 launch (nvfp4_moe_plan_w13_swiglu) ----------------------------
+// For small batches the plan's own launch is a large share of the layer, so every W13 block builds
+// the plan of the ids in LDS (one pair per thread) and stages its row tiles from there; block 0
+// also writes the plan buffer, word for word what nvfp4_moe_plan writes, for W2 and the caller.
+// The steps are those of the one-block plan kernel: a ticket per pair while counting, scans over
+// the experts, the group's pairs listed in ticket order, and each pair's stable rank as the number
+// of group members with a smaller index.
+struct PlanLds {
+    int cnt[FUSED_PLAN_EXPERTS];
+    int off[FUSED_PLAN_EXPERTS + 1];
+    int tfirst[FUSED_PLAN_EXPERTS];
+    int slot[FUSED_PLAN_PAIRS];
+    int wsum[12];
+    int bad;
+};
+
+// Builds the plan of fp.ids (P <= 256 pairs, E <= 1024 experts) in LDS on a 256-thread block, and
+// in fp.plan if this is block 0. Returns the row-tile count. id and rank: this thread's pair's
+// expert (-1 for none) and its rank among the expert's pairs.
+__device__ int fused_plan(const FusedPlan &fp, PlanLds &pl, int topk, int &id, int &rank)
+{
+    const int tid = threadIdx.x, P = (int)fp.L.P, E = fp.E;
+    const bool writer = blockIdx.x == 0;
+    const int raw = tid < P ? fp.ids[tid] : -1;
+    for (int e = tid; e < E; e += 256) pl.cnt[e] = 0;
+    if (tid == 0) pl.bad = 0;
+    __syncthreads();
+    id = -1;
+    int ticket = 0;
+    if (tid < P) {
+        if (raw >= 0 && raw < E) {
+            id = raw;
+            ticket = atomicAdd(&pl.cnt[raw], 1);
+        } else if (raw != -1) {
+            atomicAdd(&pl.bad, 1);
+        }
+    }
+    __syncthreads();
+    constexpr int EPT = FUSED_PLAN_EXPERTS / 256;
+    const int ept = (E + 255) / 256, e0 = tid * ept, ne = min(ept, E - e0);
+    int c[EPT];
+    int3 sums{0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        c[i] = i < ne ? pl.cnt[e0 + i] : 0;
+        sums.x += c[i];
+        sums.y += c[i] > 0;
+        sums.z += (c[i] + PLAN_TILE_ROWS - 1) / PLAN_TILE_ROWS;
+    }
+    int3 tot;
+    const int3 pre = block_excl_scan3<4>(sums, pl.wsum, &tot);
+    if (writer) {
+        write_expert_lists(fp.plan, fp.L, e0, ne, c, pre.x, pre.y, pre.z, pl.off, pl.tfirst);
+    } else {
+        int cpre = pre.x, tpre = pre.z;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            if (i >= ne) continue;
+            pl.off[e0 + i] = cpre;
+            pl.tfirst[e0 + i] = tpre;
+            cpre += c[i];
+            tpre += (c[i] + PLAN_TILE_ROWS - 1) / PLAN_TILE_ROWS;
+        }
+    }
+    if (tid == 0) {
+        pl.off[E] = tot.x;
+        if (writer) write_totals(fp.plan, fp.L, E, tot);
+    }
+    __syncthreads();
+    if (id >= 0) pl.slot[pl.off[id] + ticket] = tid;  // the group's pairs, in ticket order
+    __syncthreads();
+    rank = 0;
+    if (id >= 0) {
+        const int o = pl.off[id], n = pl.cnt[id];
+        for (int i = 0; i < n; ++i) rank += pl.slot[o + i] < tid;
+        if (writer) place_pair(fp.plan, fp.L, tid, id, o + rank, rank, pl.tfirst[id]);
+    } else if (writer && tid < P) {
+        fp.plan[fp.L.pos_of_pair + tid] = -1;
+        fp.plan[fp.L.pair_expert + tid] = -1;
+    }
+    if (writer && tid == 0) write_header_tail(fp.plan, fp.L, pl.bad, fp.M, topk, E);
+    return tot.z;
+}
+
+// stage_tiles from the LDS plan: rows default to pair 0 / token 0 (padding), then every pair of a
+// staged tile writes its row and the first pair of each tile the tile's expert, rows and base.
+__device__ void stage_tiles_fused(const PlanLds &pl, TileStage &st, int t_lo, int ntl, int topk, int id, int rank)
+{
+    for (int i = threadIdx.x; i < ntl * 16; i += 256) {
+        st.pair[i >> 4][i & 15] = 0;
+        st.arow[i >> 4][i & 15] = 0;
+    }
+    __syncthreads();
+    if (id >= 0) {
+        const int t = pl.tfirst[id] + rank / PLAN_TILE_ROWS - t_lo, r = rank % PLAN_TILE_ROWS;
+        if (t >= 0 && t < ntl) {
+            st.pair[t][r] = threadIdx.x;
+            st.arow[t][r] = threadIdx.x / topk;
+            if (r == 0) {
+                st.e[t] = id;
+                st.cnt[t] = min(PLAN_TILE_ROWS, pl.cnt[id] - rank);
+                st.base[t] = pl.off[id] + rank;
+            }
+        }
+    }
+    __syncthreads();
+}
+
 // Tuning of the streaming kernels: TP 16-row weight-tile pairs per wave per unit, *_OCC resident
 // 256-thread blocks per CU.
 #ifndef NVFP4_W13_TP
@@ -194,14 +303,17 @@ __device__ __forceinline__ void mma_chunk(const RawChunk (&w)[NW], const f16x8 a
 // while unit u computes; barriers order LDS only, so they do not wait for those loads.
 //
 // SH: the shared expert's tiles come first (SharedW13); without it the kernel has none of their code.
-template <int SPLIT, int TP, bool SH>
+//
+// FP: the launch builds the plan itself from fp.ids (fused_plan) instead of reading pv.
+template <int SPLIT, int TP, bool SH, bool FP = false>
 __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanView pv, int topk, const f16 *__restrict__ x,
                                                                              const uint8_t *__restrict__ codes,
                                                                              const uint8_t *__restrict__ scales,
                                                                              const float *__restrict__ gscale, int K, int I,
                                                                              int layout, f16 *__restrict__ h, int first,
-                                                                             SharedW13 shx)
+                                                                             SharedW13 shx, FusedPlan fp)
 {
+    static_assert(!(SH && FP), "the shared expert's tiles take the plan from pv");
     using G = Geo<SPLIT>;
     constexpr int SL = G::GROUPS * TP;  // i slices per unit
     __shared__ float part[4][2 * TP][16][LDS_ROW];
@@ -210,9 +322,14 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
     const int upt = (itiles + SL - 1) / SL;  // units per row tile
     const int Ts = SH ? (shx.M + 15) >> 4 : 0;  // shared expert tiles, before the plan's
     int64_t u0, u1;
+    __shared__ std::conditional_t<FP, PlanLds, int> pl;
+    int fid = -1, frank = 0;
+    int T;
+    if constexpr (FP) T = fused_plan(fp, pl, topk, fid, frank);
+    else T = pv.hdr[3];
     // Shared expert: block b computes the gates of tokens b, b + G, ... (wave 0). The first one's
     // loads are issued before the tile staging, which hides their latency.
-    const bool has_units = unit_range((int64_t)(Ts + pv.hdr[3]) * upt, first, u0, u1);
+    const bool has_units = unit_range((int64_t)(Ts + T) * upt, first, u0, u1);
     if constexpr (SH) {
         const f16 *gv = reinterpret_cast<const f16 *>(shx.gate);
         const bool gate0 = (int)blockIdx.x < shx.M && threadIdx.x < 64;
@@ -233,7 +350,8 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
     const int t_lo = (int)(u0 / upt);
     const G g(K);
     const size_t crow = (size_t)K >> 1, srow = (size_t)K >> 4;
-    if constexpr (!SH) stage_tiles<SH>(pv, st, t_lo, (int)((u1 - 1) / upt) - t_lo + 1, topk);
+    if constexpr (FP) stage_tiles_fused(pl, st, t_lo, (int)((u1 - 1) / upt) - t_lo + 1, topk, fid, frank);
+    else if constexpr (!SH) stage_tiles<SH>(pv, st, t_lo, (int)((u1 - 1) / upt) - t_lo + 1, topk);
 
     int cur = -1;
     f16x8 af[4][4];
@@ -721,7 +839,9 @@ int split_for(int k)
 unsigned stream_grid(int occ, int64_t units_max, int64_t t_max, int *cus_out)
 {
     int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
     *cus_out = cus;
     static_assert(MAX_RANGE_TILES == 16, "the bound below assumes 16 staged row tiles");
     int64_t g = occ * (int64_t)cus;
@@ -734,7 +854,7 @@ unsigned stream_grid(int occ, int64_t units_max, int64_t t_max, int *cus_out)
 }  // namespace
 
 int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, const nvfp4_weights &w, int32_t layout,
-            uint16_t *h, hipStream_t s, SharedW13 shx)
+            uint16_t *h, hipStream_t s, SharedW13 shx, FusedPlan fp)
 {
     const int K = w.k, I = w.rows / 2;
     const int split = split_for(K);
@@ -746,10 +866,17 @@ int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, 
     const int first = W13_OCC > 1 ? cus : (int)grid.x;  // one block per CU resident first
     const f16 *xp = reinterpret_cast<const f16 *>(x);
     f16 *hp = reinterpret_cast<f16 *>(h);
+    if (fp.ids) {  // the plan built in the launch (no shared expert: checked by the caller)
+        switch (split) {
+        case 1: return launch(w13_swiglu_stream_kernel<1, W13_TP, false, true>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx, fp);
+        case 2: return launch(w13_swiglu_stream_kernel<2, W13_TP, false, true>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx, fp);
+        default: return launch(w13_swiglu_stream_kernel<4, W13_TP, false, true>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx, fp);
+        }
+    }
     switch (split) {
-    case 1: return launch(shx.M > 0 ? w13_swiglu_stream_kernel<1, W13_TP, true> : w13_swiglu_stream_kernel<1, W13_TP, false>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx);
-    case 2: return launch(shx.M > 0 ? w13_swiglu_stream_kernel<2, W13_TP, true> : w13_swiglu_stream_kernel<2, W13_TP, false>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx);
-    default: return launch(shx.M > 0 ? w13_swiglu_stream_kernel<4, W13_TP, true> : w13_swiglu_stream_kernel<4, W13_TP, false>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx);
+    case 1: return launch(shx.M > 0 ? w13_swiglu_stream_kernel<1, W13_TP, true> : w13_swiglu_stream_kernel<1, W13_TP, false>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx, fp);
+    case 2: return launch(shx.M > 0 ? w13_swiglu_stream_kernel<2, W13_TP, true> : w13_swiglu_stream_kernel<2, W13_TP, false>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx, fp);
+    default: return launch(shx.M > 0 ? w13_swiglu_stream_kernel<4, W13_TP, true> : w13_swiglu_stream_kernel<4, W13_TP, false>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx, fp);
     }
 }
 

@@ -18,21 +18,10 @@
 // The router (top-k selection and softmax weights from router logits) runs one wave per token. At
 // decode sizes it shares the small path's block, so routing and planning are one launch.
 #include "internal.hpp"
+#include "plan_device.hpp"
 
 namespace nvfp4 {
 namespace {
-
-// Inclusive scan of one int across a wave64.
-__device__ __forceinline__ int wave_incl_scan(int v)
-{
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(v, o, 64);
-        if (lane >= o) v += y;
-    }
-    return v;
-}
 
 // Exclusive scan of one int per thread over a block of nwaves*64 threads. `wsum` is LDS scratch
 // of at least nwaves ints. Ends with a barrier, so `wsum` can be reused at once.
@@ -51,36 +40,6 @@ __device__ __forceinline__ int block_excl_scan(int v, int *wsum, int nwaves, int
     __syncthreads();
     *total = tot;
     return pre + incl - v;
-}
-
-// Three exclusive scans at once over a 1024-thread block (one pair of barriers). `wsum` is LDS
-// scratch of 48 ints.
-__device__ __forceinline__ int3 block_excl_scan3(int3 v, int *wsum, int3 *total)
-{
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int ix = wave_incl_scan(v.x), iy = wave_incl_scan(v.y), iz = wave_incl_scan(v.z);
-    if (lane == 63) {
-        wsum[wid] = ix;
-        wsum[16 + wid] = iy;
-        wsum[32 + wid] = iz;
-    }
-    __syncthreads();
-    int3 pre{0, 0, 0}, tot{0, 0, 0};
-#pragma unroll
-    for (int w = 0; w < 16; ++w) {
-        const int sx = wsum[w], sy = wsum[16 + w], sz = wsum[32 + w];
-        if (w < wid) {
-            pre.x += sx;
-            pre.y += sy;
-            pre.z += sz;
-        }
-        tot.x += sx;
-        tot.y += sy;
-        tot.z += sz;
-    }
-    __syncthreads();
-    *total = tot;
-    return int3{pre.x + ix - v.x, pre.y + iy - v.y, pre.z + iz - v.z};
 }
 
 // Stable rank of this thread's pair among the block's earlier pairs: how many of ids4[0 .. tid)
@@ -121,62 +80,12 @@ __device__ void build_lists(const int *cnt, int E, int32_t *plan, const PlanLayo
         sums.z += (c[i] + PLAN_TILE_ROWS - 1) / PLAN_TILE_ROWS;
     }
     int3 tot;
-    const int3 pre = block_excl_scan3(sums, wsum, &tot);
-    int cpre = pre.x, apre = pre.y, tpre = pre.z;
-    int32_t *counts = plan + L.counts, *offsets = plan + L.offsets, *active = plan + L.active;
-    int32_t *tile_e = plan + L.tile_expert, *tile_r = plan + L.tile_row0, *tile_b = plan + L.tile_base;
-    int32_t *tile_n = plan + L.tile_rows;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = e0 + i;
-        if (i >= ept || e >= E) continue;
-        counts[e] = c[i];
-        offsets[e] = cpre;
-        off_lds[e] = cpre;
-        tile_first[e] = tpre;
-        if (c[i] > 0) {
-            active[apre++] = e;
-            for (int r = 0; r < c[i]; r += PLAN_TILE_ROWS) {
-                const int rows = min(PLAN_TILE_ROWS, c[i] - r);
-                tile_e[tpre] = e;
-                tile_r[tpre] = r;
-                tile_b[tpre] = cpre + r;
-                tile_n[tpre] = rows;
-                ++tpre;
-            }
-        }
-        cpre += c[i];
-    }
+    const int3 pre = block_excl_scan3<16>(sums, wsum, &tot);
+    write_expert_lists(plan, L, e0, min(ept, E - e0), c, pre.x, pre.y, pre.z, off_lds, tile_first);
     if (threadIdx.x == 0) {
-        offsets[E] = tot.x;
+        write_totals(plan, L, E, tot);
         off_lds[E] = tot.x;
-        int32_t *hdr = plan + L.hdr;
-        hdr[0] = tot.x;
-        hdr[1] = tot.y;
-        hdr[3] = tot.z;
     }
-}
-
-// Records a valid pair's place: sorted_pair, pos_of_pair, its expert and its row in its tile's pair
-// list.
-__device__ __forceinline__ void place_pair(int32_t *plan, const PlanLayout &L, int64_t p, int e, int pos,
-                                           int row_in_expert, int first_tile)
-{
-    plan[L.sorted_pair + pos] = (int32_t)p;
-    plan[L.pos_of_pair + p] = pos;
-    plan[L.pair_expert + p] = e;
-    const int64_t t = first_tile + row_in_expert / PLAN_TILE_ROWS;
-    plan[L.tile_pair + t * PLAN_TILE_ROWS + row_in_expert % PLAN_TILE_ROWS] = (int32_t)p;
-}
-
-__device__ __forceinline__ void write_header_tail(int32_t *plan, const PlanLayout &L, int n_bad, int M, int topk, int E)
-{
-    int32_t *hdr = plan + L.hdr;
-    hdr[2] = n_bad;
-    hdr[4] = M;
-    hdr[5] = topk;
-    hdr[6] = E;
-    hdr[7] = PLAN_TILE_ROWS;
 }
 
 // ---- small path: P <= 1024, one block -----------------------------------------------------------

@@ -151,6 +151,22 @@ int nvfp4_moe_w13_swiglu(const void *plan, int32_t M, int32_t topk, int32_t E,
                          uint16_t *h, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Routing plan and grouped W13 + SwiGLU in one call: the results of nvfp4_moe_plan(topk_ids, ...,
+ * plan) followed by nvfp4_moe_w13_swiglu(plan, ...), bit for bit (the plan is built once and both
+ * W13 and W2 read it, as on the no-MTP page, "Scope and related PRs": "grouped W2 reusing the same
+ * integer plan ... avoids repeated planning").
+ *   topk_ids, plan, plan_bytes   as for nvfp4_moe_plan (plan is written: W2 takes it afterwards)
+ *   x, w13, layout, h            as for nvfp4_moe_w13_swiglu
+ * With M*topk <= 256, E <= 1024 and the decode (non-prefill) regime, it is one launch: every W13
+ * block builds the plan of the ids in LDS and one block writes the plan buffer. Otherwise it
+ * enqueues the plan and the W13 launch. Errors: those of the two calls, all checked before anything
+ * is enqueued; M = 0 is an OK no-op.
+ * --------------------------------------------------------------------------------------------- */
+int nvfp4_moe_plan_w13_swiglu(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E,
+                              void *plan, size_t plan_bytes, const uint16_t *x,
+                              const nvfp4_weights *w13, int32_t layout, uint16_t *h, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Grouped W2 with the top-k-weighted reduction ("W2/reduction fusion", no-MTP page, "Scope and
  * related PRs").
  *   h             fp16 [M*topk][I]  W13 output in bucket order

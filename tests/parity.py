@@ -65,10 +65,10 @@ def dev_moe(case, device="cuda"):
     }
 
 
-def run_moe(case, layout=0, dev=None, poison=True):
-    """plan -> W13 -> W2 on the GPU. Buffers are poisoned first (0x7E00 = fp16 NaN, 0xFFFF words)
-    so that every element that must be written is seen to be written. Returns a dict of device
-    tensors."""
+def run_moe(case, layout=0, dev=None, poison=True, fused=False):
+    """plan -> W13 -> W2 on the GPU (fused: plan and W13 through nvfp4_moe_plan_w13_swiglu). Buffers
+    are poisoned first (0x7E00 = fp16 NaN, 0xFFFF words) so that every element that must be written
+    is seen to be written. Returns a dict of device tensors."""
     import gemm_nvfp4_amd as G
     sh = case["shape"]
     d = dev or dev_moe(case)
@@ -82,8 +82,11 @@ def run_moe(case, layout=0, dev=None, poison=True):
         h.view(torch.int16).fill_(0x7E00)
         out.view(torch.int16).fill_(0x7E00)
         ws.fill_(0xFF)
-    G.nvfp4_moe_plan(d["ids"], sh.e, plan=plan)
-    G.nvfp4_moe_w13_swiglu(plan, sh.m, sh.topk, sh.e, d["x"], d["w13"], layout, h=h)
+    if fused:
+        G.nvfp4_moe_plan_w13_swiglu(d["ids"], sh.e, d["x"], d["w13"], layout, plan=plan, h=h)
+    else:
+        G.nvfp4_moe_plan(d["ids"], sh.e, plan=plan)
+        G.nvfp4_moe_w13_swiglu(plan, sh.m, sh.topk, sh.e, d["x"], d["w13"], layout, h=h)
     G.nvfp4_moe_w2_reduce(plan, sh.m, sh.topk, sh.e, h, d["w2"], d["tw"], out=out, ws=ws)
     torch.cuda.synchronize()
     return {"plan": plan, "h": h, "out": out, "ws": ws, "dev": d}
