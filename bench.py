@@ -145,21 +145,20 @@ def moe_layer_timing(M, steps, warmup, W13, W2, routes):
 
 
 def w13_kernel_timing(M, launches, W13, routes):
-    """Average duration of the grouped W13 + SwiGLU kernel alone (HIP events around a graph of
-    back-to-back launches on the capture/replay stream) and its algorithmic bytes per launch."""
+    """Average duration of the layer's grouped W13 + SwiGLU launch alone, the one that builds the
+    routing plan itself (HIP events around a graph of back-to-back launches on the capture/replay
+    stream), and its algorithmic bytes per launch."""
     import torch
     import gemm_nvfp4_amd as G
     R, P = len(W13), len(routes.x)
-    plans, hs = [], []
-    for p in range(P):
-        plans.append(G.nvfp4_moe_plan(routes.ids[p], E))
+    plan = torch.empty(max(G.nvfp4_moe_plan_bytes(M, TOPK, E), 4) // 4, dtype=torch.int32, device="cuda")
     h = torch.empty((M * TOPK, I), dtype=torch.float16, device="cuda")
     torch.cuda.synchronize()
 
     def build():
         for i in range(launches):
             p = i % P
-            G.nvfp4_moe_w13_swiglu(plans[p], M, TOPK, E, routes.x[p], W13[i % R], 0, h=h)
+            G.nvfp4_moe_plan_w13_swiglu(routes.ids[p], E, routes.x[p], W13[i % R], 0, plan=plan, h=h)
 
     ms = time_graph(build, launches)
     algo = [routes.active[p] * W13_EXPERT_BYTES + M * K * 2 + routes.valid[p] * I * 2 for p in range(P)]
@@ -170,7 +169,7 @@ def w13_kernel_timing(M, launches, W13, routes):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w13_swiglu_stream_decode16_traffic.txt")
 KERNEL_SOURCES = ("gemm_nvfp4_amd/csrc/moe_gemm.hip", "gemm_nvfp4_amd/csrc/nvfp4_device.hpp",
-                  "gemm_nvfp4_amd/csrc/internal.hpp")
+                  "gemm_nvfp4_amd/csrc/internal.hpp", "gemm_nvfp4_amd/csrc/plan_device.hpp")
 
 
 def kernel_source_hash():
@@ -204,10 +203,10 @@ def traffic_mode(W13):
     for _ in range(3):
         dst.copy_(src)
     routes = Routes(16, 12, 1000)
-    plans = [G.nvfp4_moe_plan(routes.ids[p], E) for p in range(12)]
+    plan = torch.empty(max(G.nvfp4_moe_plan_bytes(16, TOPK, E), 4) // 4, dtype=torch.int32, device="cuda")
     h = torch.empty((16 * TOPK, I), dtype=torch.float16, device="cuda")
     for i in range(12):
-        G.nvfp4_moe_w13_swiglu(plans[i], 16, TOPK, E, routes.x[i], W13[i % len(W13)], 0, h=h)
+        G.nvfp4_moe_plan_w13_swiglu(routes.ids[i], E, routes.x[i], W13[i % len(W13)], 0, plan=plan, h=h)
     torch.cuda.synchronize()
     algo = [routes.active[p] * W13_EXPERT_BYTES + 16 * K * 2 + routes.valid[p] * I * 2 for p in range(12)]
     log(f"traffic mode done: copy 268435456 B x3; W13 x12, algorithmic bytes/launch {np.mean(algo):.0f}")
@@ -480,7 +479,7 @@ def main():
         "us_per_layer": head["us_per_layer"], "hbm_frac": head["hbm_frac"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "w13_swiglu_stream_kernel<4, 1, false>", "us_per_launch": round(k_us, 3),
+                     "kernel": "w13_swiglu_stream_kernel<4, 1, false, true> (routing plan built in the launch)", "us_per_launch": round(k_us, 3),
                      "algorithmic_bytes_per_launch": round(k_bytes)},
         "launch_floor_us": round(floor, 3),
         "sweep": sweep, "prefill": prefill, "dense": dense, "dense_fp8": fp8, "mlp": mlp, "with_shared_expert": shared, "route": route, "cpu_baseline": cpu,
