@@ -626,7 +626,7 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
         const int p = t * topk + threadIdx.x;
         const int j = pv.pos_of_pair[p];
         s_row[threadIdx.x] = j;
-        s_e[threadIdx.x] = j >= 0 ? pv.pair_expert[p] : -1;
+        s_e[threadIdx.x] = pv.pair_expert[p];  // -1 for a skipped pair: loaded beside pos_of_pair, not after it
         s_w[threadIdx.x] = tw[p];
     }
     __syncthreads();
@@ -733,7 +733,7 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_shared_kernel(PlanView 
         const int p = t * topk + threadIdx.x;
         const int j = pv.pos_of_pair[p];
         s_row[threadIdx.x] = j;
-        s_e[threadIdx.x] = j >= 0 ? pv.pair_expert[p] : -1;
+        s_e[threadIdx.x] = pv.pair_expert[p];  // -1 for a skipped pair: loaded beside pos_of_pair, not after it
         s_w[threadIdx.x] = tw[p];
     } else if ((int)threadIdx.x == topk) {
         s_row[topk] = t;
