@@ -90,9 +90,10 @@ class Routes:
             self.valid.append(int(((ids >= 0) & (ids < E)).sum()))
 
 
-def time_graph(build_fn, steps, warmup_fn=None):
+def time_graph(build_fn, steps, warmup_fn=None, more=None, trials=0):
     """Capture build_fn() (which enqueues `steps` steps) in one graph, replay once untimed, then time
-    one replay with HIP events on the replay stream. Returns elapsed ms."""
+    one replay with HIP events on the replay stream. Returns elapsed ms. With trials > 0 the graph is
+    replayed that many more times, each timed alone, and the figures are appended to `more`."""
     import torch
     if warmup_fn is not None:
         warmup_fn()
@@ -108,6 +109,12 @@ def time_graph(build_fn, steps, warmup_fn=None):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1)
+    for _ in range(trials):
+        t0.record()
+        g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        more.append(t0.elapsed_time(t1))
     del g
     return ms
 
@@ -120,8 +127,9 @@ def weight_sets(n, seed0=1000):
     return w13, w2
 
 
-def moe_layer_timing(M, steps, warmup, W13, W2, routes):
-    """µs per MoE layer and weight GB/s over `steps` graph-captured layer calls."""
+def moe_layer_timing(M, steps, warmup, W13, W2, routes, trials=0):
+    """µs per MoE layer and weight GB/s over `steps` graph-captured layer calls (the first timed
+    replay). With trials > 0, also the median, p10 and p90 of that many further replays."""
     import gemm_nvfp4_amd as G
     R, P = len(W13), len(routes.x)
     layer = G.MoELayer(M, TOPK, W13[0], W2[0])
@@ -134,14 +142,41 @@ def moe_layer_timing(M, steps, warmup, W13, W2, routes):
         for i in range(warmup):
             step(i)
 
-    ms = time_graph(lambda: [step(i) for i in range(steps)], steps, warm)
+    more = []
+    ms = time_graph(lambda: [step(i) for i in range(steps)], steps, warm, more=more, trials=trials)
     wbytes = sum(routes.active[i % P] * EXPERT_BYTES for i in range(steps))
     pairs = sum(routes.valid[i % P] for i in range(steps))
     us = ms * 1e3 / steps
-    return {"M": M, "us_per_layer": round(us, 3), "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1),
-            "hbm_frac": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "tflops": round(pairs * FLOP_PER_PAIR / (ms * 1e-3) / 1e12, 2),
-            "mean_active_experts": round(float(np.mean(routes.active)), 2), "steps": steps}
+    r = {"M": M, "us_per_layer": round(us, 3), "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1),
+         "hbm_frac": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+         "tflops": round(pairs * FLOP_PER_PAIR / (ms * 1e-3) / 1e12, 2),
+         "mean_active_experts": round(float(np.mean(routes.active)), 2), "steps": steps}
+    if more:
+        q = np.percentile(np.array(more) * 1e3 / steps, [10, 50, 90])
+        r["trials"] = {"n": len(more), "us_per_layer_p10": round(float(q[0]), 3),
+                       "us_per_layer_median": round(float(q[1]), 3), "us_per_layer_p90": round(float(q[2]), 3)}
+    return r
+
+
+def eager_latency(M, W13, W2, routes, calls=20):
+    """Median µs of single eager layer calls (host launch work included), each bracketed by HIP
+    events and a synchronize."""
+    import torch
+    import gemm_nvfp4_amd as G
+    layer = G.MoELayer(M, TOPK, W13[0], W2[0])
+    P = len(routes.x)
+    for i in range(3):
+        layer(routes.x[i % P], routes.ids[i % P], routes.tw[i % P], W13[i % len(W13)], W2[i % len(W2)])
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    us = []
+    for i in range(calls):
+        t0.record()
+        layer(routes.x[i % P], routes.ids[i % P], routes.tw[i % P], W13[i % len(W13)], W2[i % len(W2)])
+        t1.record()
+        torch.cuda.synchronize()
+        us.append(t0.elapsed_time(t1) * 1e3)
+    return round(float(np.median(us)), 3)
 
 
 def w13_kernel_timing(M, launches, W13, routes):
@@ -399,9 +434,28 @@ def cpu_baseline(W13, W2, seconds):
         el = time.perf_counter() - t0
         if el >= seconds or done >= 200:
             break
+    # The same on one thread, for a few layers.
+    done1, wbytes1, t1 = 0, 0, time.perf_counter()
+    while True:
+        rng = S.rng_for(S.WORKLOAD_IDS["decode"], 0, 1000 + done1)
+        case = {"shape": S.DECODE, "x": S.activations(rng, 16, K), "ids": S.routing_uniform(rng, 16, TOPK, E),
+                "topk_weights": S.softmax_weights(rng, 16, TOPK), "w13": w13, "w2": w2}
+        pl = O.plan(case["ids"], E, 16)
+        O.moe_grouped(case, pl, nthreads=1)
+        done1 += 1
+        wbytes1 += pl["n_active"] * EXPERT_BYTES
+        el1 = time.perf_counter() - t1
+        if el1 >= seconds / 3 or done1 >= 50:
+            break
+    model = "unknown"
+    try:
+        model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": round(wbytes / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} route patterns of the 16-token decode layer (fp64 grouped oracle, "
-                      f"{el:.1f} s wall, {el / done * 1e3:.1f} ms per layer)"}
+                      f"{el:.1f} s wall, {el / done * 1e3:.1f} ms per layer)",
+            "one_thread_GBps": round(wbytes1 / el1 / 1e9, 4), "nproc": os.cpu_count(), "cpu_model": model}
 
 
 def main():
@@ -426,8 +480,10 @@ def main():
         return
 
     routes16 = Routes(16, args.patterns, 1000)
-    head = moe_layer_timing(16, args.steps, args.warmup, W13, W2, routes16)
+    head = moe_layer_timing(16, args.steps, args.warmup, W13, W2, routes16, trials=20)
     log(f"headline M=16: {head}")
+    eager = {"M1_us": eager_latency(1, W13, W2, Routes(1, 8, 4000)), "M16_us": eager_latency(16, W13, W2, routes16)}
+    log(f"eager single-call latency: {eager}")
     k_us, k_bytes = w13_kernel_timing(16, args.steps, W13, routes16)
     achieved = k_bytes / (k_us * 1e-6) / 1e9
     log(f"w13 kernel: {k_us:.3f} us/launch, {k_bytes / 1e6:.2f} MB/launch -> {achieved:.1f} GB/s")
@@ -481,7 +537,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "w13_swiglu_stream_kernel<4, 1, false, true> (routing plan built in the launch)", "us_per_launch": round(k_us, 3),
                      "algorithmic_bytes_per_launch": round(k_bytes)},
-        "launch_floor_us": round(floor, 3),
+        "launch_floor_us": round(floor, 3), "eager_layer_latency": eager, "trials": head.get("trials"),
         "sweep": sweep, "prefill": prefill, "dense": dense, "dense_fp8": fp8, "mlp": mlp, "with_shared_expert": shared, "route": route, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
