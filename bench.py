@@ -292,7 +292,7 @@ def dense_timing(copies=64, launches=256):
 
 def shared_layer_timing(steps, W13, W2, routes, i_shared=512):
     """The 16-token decode layer with a shared expert (K=2048, 512 intermediate columns) and its gate:
-    plan, W13, shared expert, W2 with the shared term. Weight sets rotate as in the headline; the
+    plan + W13 (one launch), shared expert, W2 with the shared term. Weight sets rotate as in the headline; the
     shared expert rotates over as many copies. Three forms: the shared expert's own launches in the
     same stream (serial), on a second stream (overlapped), and inside the routed launches (fused)."""
     import torch
@@ -311,9 +311,8 @@ def shared_layer_timing(steps, W13, W2, routes, i_shared=512):
 
     def step_fused(i):  # the shared expert as extra tiles of the routed W13 and W2 launches
         p, r = i % P, i % R
-        G.nvfp4_moe_plan(routes.ids[p], E, plan=layer.plan)
-        G.nvfp4_moe_w13_swiglu_with_shared(layer.plan, M, TOPK, E, routes.x[p], W13[r], sw13[r], g, h=layer.h,
-                                           shared_h=hs, shared_sigma=sg)
+        G.nvfp4_moe_plan_w13_swiglu_with_shared(routes.ids[p], E, routes.x[p], W13[r], sw13[r], g, plan=layer.plan,
+                                                h=layer.h, shared_h=hs, shared_sigma=sg)
         G.nvfp4_moe_w2_reduce_with_shared(layer.plan, M, TOPK, E, layer.h, W2[r], routes.tw[p], hs, sw2[r], sg,
                                           shared_y=ys, out=layer.out, ws=layer.ws)
 
@@ -329,8 +328,7 @@ def shared_layer_timing(steps, W13, W2, routes, i_shared=512):
                                           stream=side)
         else:
             G.nvfp4_moe_shared_expert(routes.x[p], sw13[r], sw2[r], g, h=hs, shared_y=ys, shared_sigma=sg)
-        G.nvfp4_moe_plan(routes.ids[p], E, plan=layer.plan)
-        G.nvfp4_moe_w13_swiglu(layer.plan, M, TOPK, E, routes.x[p], W13[r], 0, h=layer.h)
+        G.nvfp4_moe_plan_w13_swiglu(routes.ids[p], E, routes.x[p], W13[r], 0, plan=layer.plan, h=layer.h)
         if overlap:
             cur.wait_stream(side)
         G.nvfp4_moe_w2_reduce_shared(layer.plan, M, TOPK, E, layer.h, W2[r], routes.tw[p], ys, sg, out=layer.out,

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     nvfp4_moe_plan,
     nvfp4_moe_plan_bytes,
     nvfp4_moe_plan_w13_swiglu,
+    nvfp4_moe_plan_w13_swiglu_with_shared,
     nvfp4_moe_route,
     nvfp4_moe_shared_expert,
     nvfp4_moe_w13_swiglu,

@@ -54,6 +54,9 @@ _SIGS = {
                                              _vp, _vp, _sz, _vp]),
     "nvfp4_moe_w13_swiglu_with_shared": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _i32, _vp,
                                                    C.POINTER(nvfp4_weights), _vp, _vp, _vp, _vp]),
+    "nvfp4_moe_plan_w13_swiglu_with_shared": (C.c_int, [_vp, _i32, _i32, _i32, _vp, _sz, _vp,
+                                                        C.POINTER(nvfp4_weights), _i32, _vp, C.POINTER(nvfp4_weights),
+                                                        _vp, _vp, _vp, _vp]),
     "nvfp4_moe_w2_reduce_with_shared": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _vp, _vp,
                                                   C.POINTER(nvfp4_weights), _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_linear_swiglu": (C.c_int, [_vp, _i32, C.POINTER(nvfp4_weights), _i32, _vp, _vp]),
@@ -380,6 +383,30 @@ def nvfp4_moe_w13_swiglu_with_shared(plan: torch.Tensor, M: int, topk: int, E: i
         _dev(shared_h, "shared_h", torch.float16), _dev(shared_sigma, "shared_sigma", torch.float32),
         _stream(stream)))
     return h, shared_h, shared_sigma
+
+
+def nvfp4_moe_plan_w13_swiglu_with_shared(topk_ids: torch.Tensor, E: int, x: torch.Tensor, w13: NVFP4Tensor,
+                                          shared_w13: NVFP4Tensor, gate: torch.Tensor, layout: int = 0,
+                                          plan: torch.Tensor | None = None, h: torch.Tensor | None = None,
+                                          shared_h: torch.Tensor | None = None,
+                                          shared_sigma: torch.Tensor | None = None, stream=None):
+    """nvfp4_moe_plan followed by nvfp4_moe_w13_swiglu_with_shared (one launch for small batches).
+    Returns (plan, h, shared_h, shared_sigma)."""
+    M, topk = topk_ids.shape
+    I, Is = w13.rows // 2, shared_w13.rows // 2
+    dev = x.device
+    if plan is None:
+        plan = torch.empty(max(nvfp4_moe_plan_bytes(M, topk, E), 4) // 4, dtype=torch.int32, device=dev)
+    h = torch.empty((M * topk, I), dtype=torch.float16, device=dev) if h is None else h
+    shared_h = torch.empty((M, Is), dtype=torch.float16, device=dev) if shared_h is None else shared_h
+    shared_sigma = torch.empty((M,), dtype=torch.float32, device=dev) if shared_sigma is None else shared_sigma
+    d, ds = w13.desc(), shared_w13.desc()
+    _check("nvfp4_moe_plan_w13_swiglu_with_shared", lib().nvfp4_moe_plan_w13_swiglu_with_shared(
+        _dev(topk_ids, "topk_ids", torch.int32), M, topk, E, _dev(plan, "plan", torch.int32), plan.numel() * 4,
+        _dev(x, "x", torch.float16), C.byref(d), layout, _dev(h, "h", torch.float16), C.byref(ds),
+        _dev(gate, "gate", torch.float16), _dev(shared_h, "shared_h", torch.float16),
+        _dev(shared_sigma, "shared_sigma", torch.float32), _stream(stream)))
+    return plan, h, shared_h, shared_sigma
 
 
 def nvfp4_moe_w2_reduce_with_shared(plan: torch.Tensor, M: int, topk: int, E: int, h: torch.Tensor, w2: NVFP4Tensor,

@@ -259,6 +259,54 @@ NVFP4_API int nvfp4_moe_w13_swiglu_with_shared(const void *plan, int32_t M, int3
     return st;
 }
 
+NVFP4_API int nvfp4_moe_plan_w13_swiglu_with_shared(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E,
+                                                    void *plan, size_t plan_bytes, const uint16_t *x,
+                                                    const nvfp4_weights *w13, int32_t layout, uint16_t *h,
+                                                    const nvfp4_weights *shared_w13, const uint16_t *gate,
+                                                    uint16_t *shared_h, float *shared_sigma, void *stream)
+{
+    // Every check of nvfp4_moe_plan and nvfp4_moe_w13_swiglu_with_shared, before anything is enqueued.
+    if (!plan_shape_ok(M, topk, E) || (layout != 0 && layout != 1)) return NVFP4_ERR_SHAPE;
+    if (E > nvfp4::MAX_EXPERTS) return NVFP4_ERR_UNSUPPORTED;
+    int st = check_weights(w13);
+    if (st == NVFP4_OK) st = check_weights(shared_w13);
+    if (st != NVFP4_OK) return st;
+    if (w13->groups != E || w13->rows % 2 != 0 || shared_w13->groups != 1 || shared_w13->rows % 2 != 0 ||
+        shared_w13->k != w13->k)
+        return NVFP4_ERR_SHAPE;
+    const int K = w13->k, I = w13->rows / 2, Is = shared_w13->rows / 2;
+    if (K % 128 != 0 || K > nvfp4::MAX_MOE_RED || I % 16 != 0 || Is % 16 != 0) return NVFP4_ERR_UNSUPPORTED;
+    if (M == 0) return NVFP4_OK;
+    if (!topk_ids || !plan || !x || !h || !gate || !shared_h || !shared_sigma) return NVFP4_ERR_NULL;
+    if (!aligned(topk_ids, 4) || !aligned(plan, 16) || !aligned(x, 16) || !aligned(h, 16) ||
+        !aligned(shared_h, 16) || !aligned(gate, 2) || !aligned(shared_sigma, 4))
+        return NVFP4_ERR_ALIGN;
+    const PlanLayout L = nvfp4::plan_layout(M, topk, E);
+    if (plan_bytes < (size_t)L.words * sizeof(int32_t)) return NVFP4_ERR_WORKSPACE;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!nvfp4::use_prefill(M, L.P, E, K, I) && Is == I && aligned(gate, 16) && nvfp4::use_fused_plan(L.P, E)) {
+        nvfp4::SharedW13 shx;
+        shx.codes = shared_w13->codes;
+        shx.scales = shared_w13->scales;
+        shx.gscale = shared_w13->global_scale;
+        shx.h = shared_h;
+        shx.gate = gate;
+        shx.sigma = shared_sigma;
+        shx.M = M;
+        nvfp4::FusedPlan fp;
+        fp.ids = topk_ids;
+        fp.plan = static_cast<int32_t *>(plan);
+        fp.L = L;
+        fp.M = M;
+        fp.E = E;
+        return nvfp4::run_w13(nvfp4::plan_view(plan, L), L.T, topk, x, *w13, layout, h, s, shx, fp);
+    }
+    st = nvfp4::run_plan(topk_ids, M, topk, E, static_cast<int32_t *>(plan), L, s);
+    if (st != NVFP4_OK) return st;
+    return nvfp4_moe_w13_swiglu_with_shared(plan, M, topk, E, x, w13, layout, h, shared_w13, gate, shared_h,
+                                            shared_sigma, stream);
+}
+
 NVFP4_API int nvfp4_moe_w2_reduce_with_shared(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16_t *h,
                                               const nvfp4_weights *w2, const float *topk_weights,
                                               const uint16_t *shared_h, const nvfp4_weights *shared_w2,

@@ -201,15 +201,27 @@ __device__ int fused_plan(const FusedPlan &fp, PlanLds &pl, int topk, int &id, i
 
 // stage_tiles from the LDS plan: rows default to pair 0 / token 0 (padding), then every pair of a
 // staged tile writes its row and the first pair of each tile the tile's expert, rows and base.
-__device__ void stage_tiles_fused(const PlanLds &pl, TileStage &st, int t_lo, int ntl, int topk, int id, int rank)
+// The first Ts tiles are the shared expert's, staged as stage_tiles stages them (tokens 16t ..
+// 16t+15 of Ms).
+__device__ void stage_tiles_fused(const PlanLds &pl, TileStage &st, int t_lo, int ntl, int topk, int id, int rank,
+                                  int Ts = 0, int Ms = 0)
 {
     for (int i = threadIdx.x; i < ntl * 16; i += 256) {
-        st.pair[i >> 4][i & 15] = 0;
-        st.arow[i >> 4][i & 15] = 0;
+        const int tg = t_lo + (i >> 4), r = i & 15;
+        st.pair[i >> 4][r] = 0;
+        st.arow[i >> 4][r] = tg < Ts ? 16 * tg + (r < Ms - 16 * tg ? r : 0) : 0;
+    }
+    if ((int)threadIdx.x < ntl) {
+        const int tg = t_lo + threadIdx.x;
+        if (tg < Ts) {
+            st.e[threadIdx.x] = -1;
+            st.cnt[threadIdx.x] = min(16, Ms - 16 * tg);
+            st.base[threadIdx.x] = 16 * tg;
+        }
     }
     __syncthreads();
     if (id >= 0) {
-        const int t = pl.tfirst[id] + rank / PLAN_TILE_ROWS - t_lo, r = rank % PLAN_TILE_ROWS;
+        const int t = Ts + pl.tfirst[id] + rank / PLAN_TILE_ROWS - t_lo, r = rank % PLAN_TILE_ROWS;
         if (t >= 0 && t < ntl) {
             st.pair[t][r] = threadIdx.x;
             st.arow[t][r] = threadIdx.x / topk;
@@ -313,7 +325,6 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
                                                                              int layout, f16 *__restrict__ h, int first,
                                                                              SharedW13 shx, FusedPlan fp)
 {
-    static_assert(!(SH && FP), "the shared expert's tiles take the plan from pv");
     using G = Geo<SPLIT>;
     constexpr int SL = G::GROUPS * TP;  // i slices per unit
     __shared__ float part[4][2 * TP][16][LDS_ROW];
@@ -335,8 +346,11 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
         const bool gate0 = (int)blockIdx.x < shx.M && threadIdx.x < 64;
         WaveDotRegs gr;
         if (gate0) wave_dot_load(gr, x + (size_t)blockIdx.x * K, gv, K);
-        if (has_units) stage_tiles<SH>(pv, st, t_lo_of(u0, upt), (int)((u1 - 1) / upt) - t_lo_of(u0, upt) + 1, topk, Ts,
-                                       shx.M);
+        if (has_units) {
+            const int tl = t_lo_of(u0, upt), nl = (int)((u1 - 1) / upt) - tl + 1;
+            if constexpr (FP) stage_tiles_fused(pl, st, tl, nl, topk, fid, frank, Ts, shx.M);
+            else stage_tiles<SH>(pv, st, tl, nl, topk, Ts, shx.M);
+        }
         if (gate0) {
             const float z = wave_dot_sum(gr, K);
             if (threadIdx.x == 0) shx.sigma[blockIdx.x] = 1.0f / (1.0f + expf(-z));
@@ -350,8 +364,10 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
     const int t_lo = (int)(u0 / upt);
     const G g(K);
     const size_t crow = (size_t)K >> 1, srow = (size_t)K >> 4;
-    if constexpr (FP) stage_tiles_fused(pl, st, t_lo, (int)((u1 - 1) / upt) - t_lo + 1, topk, fid, frank);
-    else if constexpr (!SH) stage_tiles<SH>(pv, st, t_lo, (int)((u1 - 1) / upt) - t_lo + 1, topk);
+    if constexpr (!SH) {
+        if constexpr (FP) stage_tiles_fused(pl, st, t_lo, (int)((u1 - 1) / upt) - t_lo + 1, topk, fid, frank);
+        else stage_tiles<SH>(pv, st, t_lo, (int)((u1 - 1) / upt) - t_lo + 1, topk);
+    }
 
     int cur = -1;
     f16x8 af[4][4];
@@ -866,11 +882,11 @@ int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, 
     const int first = W13_OCC > 1 ? cus : (int)grid.x;  // one block per CU resident first
     const f16 *xp = reinterpret_cast<const f16 *>(x);
     f16 *hp = reinterpret_cast<f16 *>(h);
-    if (fp.ids) {  // the plan built in the launch (no shared expert: checked by the caller)
+    if (fp.ids) {  // the plan built in the launch
         switch (split) {
-        case 1: return launch(w13_swiglu_stream_kernel<1, W13_TP, false, true>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx, fp);
-        case 2: return launch(w13_swiglu_stream_kernel<2, W13_TP, false, true>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx, fp);
-        default: return launch(w13_swiglu_stream_kernel<4, W13_TP, false, true>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx, fp);
+        case 1: return launch(shx.M > 0 ? w13_swiglu_stream_kernel<1, W13_TP, true, true> : w13_swiglu_stream_kernel<1, W13_TP, false, true>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx, fp);
+        case 2: return launch(shx.M > 0 ? w13_swiglu_stream_kernel<2, W13_TP, true, true> : w13_swiglu_stream_kernel<2, W13_TP, false, true>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx, fp);
+        default: return launch(shx.M > 0 ? w13_swiglu_stream_kernel<4, W13_TP, true, true> : w13_swiglu_stream_kernel<4, W13_TP, false, true>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx, fp);
         }
     }
     switch (split) {

@@ -226,6 +226,17 @@ int nvfp4_moe_w13_swiglu_with_shared(const void *plan, int32_t M, int32_t topk, 
                                      const nvfp4_weights *w13, int32_t layout, uint16_t *h,
                                      const nvfp4_weights *shared_w13, const uint16_t *gate, uint16_t *shared_h,
                                      float *shared_sigma, void *stream);
+/* nvfp4_moe_plan_w13_swiglu_with_shared: nvfp4_moe_plan followed by
+ * nvfp4_moe_w13_swiglu_with_shared, bit for bit, as nvfp4_moe_plan_w13_swiglu is for the routed
+ * call: topk_ids, plan and plan_bytes as for nvfp4_moe_plan, the rest as for
+ * nvfp4_moe_w13_swiglu_with_shared. One launch when that call's one-launch form applies and
+ * M*topk <= 256, E <= 1024; otherwise the plan is enqueued first. Errors: those of the two calls,
+ * all checked before anything is enqueued. */
+int nvfp4_moe_plan_w13_swiglu_with_shared(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E,
+                                          void *plan, size_t plan_bytes, const uint16_t *x,
+                                          const nvfp4_weights *w13, int32_t layout, uint16_t *h,
+                                          const nvfp4_weights *shared_w13, const uint16_t *gate,
+                                          uint16_t *shared_h, float *shared_sigma, void *stream);
 int nvfp4_moe_w2_reduce_with_shared(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16_t *h,
                                     const nvfp4_weights *w2, const float *topk_weights, const uint16_t *shared_h,
                                     const nvfp4_weights *shared_w2, const float *shared_sigma, float *shared_y,

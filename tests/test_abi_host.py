@@ -33,7 +33,8 @@ def test_header_declares_the_expected_entry_points():
         "nvfp4_abi_version", "nvfp4_status_str", "nvfp4_moe_plan_bytes", "nvfp4_moe_plan", "nvfp4_moe_route",
         "nvfp4_moe_w13_swiglu", "nvfp4_moe_w2_workspace_bytes", "nvfp4_moe_w2_reduce", "nvfp4_linear",
         "nvfp4_linear_swiglu", "nvfp4_linear_fp8", "nvfp4_moe_shared_expert", "nvfp4_moe_w2_reduce_shared",
-        "nvfp4_moe_w13_swiglu_with_shared", "nvfp4_moe_w2_reduce_with_shared", "nvfp4_moe_plan_w13_swiglu"])
+        "nvfp4_moe_w13_swiglu_with_shared", "nvfp4_moe_w2_reduce_with_shared", "nvfp4_moe_plan_w13_swiglu",
+        "nvfp4_moe_plan_w13_swiglu_with_shared"])
 
 
 def test_library_exports_every_declared_function():
@@ -132,6 +133,18 @@ def test_argument_checks_fail_closed(L):
     assert L.nvfp4_moe_plan_w13_swiglu(null, 4, 2, 8, fake, 1 << 20, fake, C.byref(ew13), 0, fake, null) == 1
     assert L.nvfp4_moe_plan_w13_swiglu(fake, 4, 2, 8, fake, 1 << 20, odd, C.byref(ew13), 0, fake, null) == 3
     assert L.nvfp4_moe_plan_w13_swiglu(fake, 4, 2, 8, fake, 16, fake, C.byref(ew13), 0, fake, null) == 4
+    # plan + W13 with the shared expert in one call
+    assert L.nvfp4_moe_plan_w13_swiglu_with_shared(fake, 4, 2, 8, fake, 1 << 20, fake, C.byref(rw13), 0, fake,
+                                                   C.byref(nvfp4_weights(fake, fake, fake, 1, 256, 128)),
+                                                   fake, fake, fake, null) == 2   # shared k != K
+    assert L.nvfp4_moe_plan_w13_swiglu_with_shared(fake, 4, 2, 8, fake, 1 << 20, fake, C.byref(rw13), 0, fake,
+                                                   C.byref(sw13), null, fake, fake, null) == 1   # no gate
+    assert L.nvfp4_moe_plan_w13_swiglu_with_shared(odd, 4, 2, 8, fake, 1 << 20, fake, C.byref(rw13), 0, fake,
+                                                   C.byref(sw13), fake, fake, fake, null) == 3   # ids unaligned
+    assert L.nvfp4_moe_plan_w13_swiglu_with_shared(fake, 4, 2, 8, fake, 16, fake, C.byref(rw13), 0, fake,
+                                                   C.byref(sw13), fake, fake, fake, null) == 4   # plan too small
+    assert L.nvfp4_moe_plan_w13_swiglu_with_shared(null, 0, 2, 8, null, 0, null, C.byref(rw13), 0, null,
+                                                   C.byref(sw13), null, null, null, null) == 0   # M = 0
     # channel-FP8 projection
     from gemm_nvfp4_amd._lib import fp8_channel_weights as f8
     assert L.nvfp4_linear_fp8(fake, 4, C.byref(f8(fake, fake, 64, 96)), fake, null) == 5     # K % 128

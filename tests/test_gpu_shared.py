@@ -156,3 +156,33 @@ def test_fused_shared_matches_oracle(orc):
     assert_rows_close(to_np64(out), ref, "fused moe+shared")
     sg_ref = orc.shared_gate(case["x"], shared["g"])
     assert np.all(np.abs(sg.cpu().numpy() - sg_ref) <= 1e-6 + 1e-5 * sg_ref)
+
+
+@pytest.mark.parametrize("shape,routing,i_shared,layout", [
+    (S.MoEShape(m=5, e=512, topk=10, k=2048, i=512), "uniform", 512, 0),      # one launch
+    (S.DECODE, "repeat_invalid", 512, 1),                                      # one launch, bad ids
+    (S.MoEShape(m=17, e=64, topk=4, k=256, i=128), "zipf", 128, 0),           # two shared tiles, one launch
+    (S.MoEShape(m=26, e=512, topk=10, k=2048, i=512), "uniform", 512, 0),     # 260 pairs: plan launched first
+    (S.DECODE, "uniform", 256, 0),                                             # shared I != I: own launches
+])
+def test_plan_in_shared_w13_launch_equals_separate_calls(shape, routing, i_shared, layout):
+    """nvfp4_moe_plan_w13_swiglu_with_shared gives the plan buffer word for word and h, shared h and
+    the gates bitwise as nvfp4_moe_plan followed by nvfp4_moe_w13_swiglu_with_shared."""
+    case = S.moe_case(shape, routing=routing, route_pattern=67, weights=None)
+    shared = S.shared_expert(S.rng_for(S.WORKLOAD_IDS["decode"], 59, shape.m), shape.k, i_shared)
+    d = dev_moe(case)
+    w13s, _, g = _shared_dev(shared)
+    words = max(G.nvfp4_moe_plan_bytes(shape.m, shape.topk, shape.e), 4) // 4
+    plan_a = torch.full((words,), -1, dtype=torch.int32, device="cuda")
+    plan_b = plan_a.clone()
+    _, h_a, hs_a, sg_a = G.nvfp4_moe_plan_w13_swiglu_with_shared(d["ids"], shape.e, d["x"], d["w13"], w13s, g,
+                                                                layout=layout, plan=plan_a)
+    G.nvfp4_moe_plan(d["ids"], shape.e, plan=plan_b)
+    h_b, hs_b, sg_b = G.nvfp4_moe_w13_swiglu_with_shared(plan_b, shape.m, shape.topk, shape.e, d["x"], d["w13"],
+                                                         w13s, g, layout=layout)
+    torch.cuda.synchronize()
+    assert torch.equal(plan_a, plan_b)
+    nv = int(G.plan_fields(plan_b, shape.m, shape.topk, shape.e)["n_valid"])
+    assert torch.equal(h_a[:nv].view(torch.int16), h_b[:nv].view(torch.int16))
+    assert torch.equal(hs_a.view(torch.int16), hs_b.view(torch.int16))
+    assert torch.equal(sg_a.view(torch.int32), sg_b.view(torch.int32))
