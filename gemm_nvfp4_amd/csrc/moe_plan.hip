@@ -320,17 +320,70 @@ __global__ __launch_bounds__(256) void plan_scan_chunks_kernel(int E, int32_t *_
     if (lane == 0) plan[L.counts + e] = running;
 }
 
-// 3) one block: offsets, active list, tiles and the header.
+// 3) one block: offsets, active list, tiles and the header. The same words as build_lists, but the
+//    row tiles (thousands at prefill sizes) are written tile-parallel: tile t finds its expert by
+//    binary search over the tile starts, so a wave's stores are contiguous.
 __global__ __launch_bounds__(1024) void plan_lists_kernel(int M, int topk, int E, int32_t *__restrict__ plan, PlanLayout L)
 {
     __shared__ int off[MAX_EXPERTS + 1];
+    __shared__ int tfirst[MAX_EXPERTS + 1];
     __shared__ int wsum[48];
     __shared__ int cnt[MAX_EXPERTS];
     for (int e = threadIdx.x; e < E; e += 1024) cnt[e] = plan[L.counts + e];
     int bad = 0;
     for (int64_t g = threadIdx.x; g < L.G; g += 1024) bad += plan[L.badc + g];
     __syncthreads();
-    build_lists(cnt, E, plan, L, off, plan + L.tile_first, wsum);
+    const int ept = (E + 1023) / 1024, e0 = threadIdx.x * ept, ne = min(ept, E - e0);
+    int c[4];
+    int3 sums{0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        c[i] = i < ne ? cnt[e0 + i] : 0;
+        sums.x += c[i];
+        sums.y += c[i] > 0;
+        sums.z += (c[i] + PLAN_TILE_ROWS - 1) / PLAN_TILE_ROWS;
+    }
+    int3 tot;
+    const int3 pre = block_excl_scan3<16>(sums, wsum, &tot);
+    {
+        int cpre = pre.x, apre = pre.y, tpre = pre.z;
+        int32_t *counts = plan + L.counts, *offsets = plan + L.offsets, *active = plan + L.active;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i >= ne) continue;
+            const int e = e0 + i;
+            counts[e] = c[i];
+            offsets[e] = cpre;
+            off[e] = cpre;
+            plan[L.tile_first + e] = tpre;
+            tfirst[e] = tpre;
+            if (c[i] > 0) active[apre++] = e;
+            cpre += c[i];
+            tpre += (c[i] + PLAN_TILE_ROWS - 1) / PLAN_TILE_ROWS;
+        }
+    }
+    if (threadIdx.x == 0) {
+        write_totals(plan, L, E, tot);
+        off[E] = tot.x;
+        tfirst[E] = tot.z;
+    }
+    __syncthreads();
+    int32_t *tile_e = plan + L.tile_expert, *tile_r = plan + L.tile_row0, *tile_b = plan + L.tile_base;
+    int32_t *tile_n = plan + L.tile_rows;
+    for (int t = threadIdx.x; t < tot.z; t += 1024) {
+        // the last expert whose first tile is <= t: experts without tiles have empty ranges
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tfirst[mid] <= t) lo = mid;
+            else hi = mid - 1;
+        }
+        const int r = (t - tfirst[lo]) * PLAN_TILE_ROWS;
+        tile_e[t] = lo;
+        tile_r[t] = r;
+        tile_b[t] = off[lo] + r;
+        tile_n[t] = min(PLAN_TILE_ROWS, cnt[lo] - r);
+    }
     int total_bad;
     block_excl_scan(bad, wsum, 16, &total_bad);
     if (threadIdx.x == 0) write_header_tail(plan, L, total_bad, M, topk, E);
