@@ -121,3 +121,32 @@ def test_prefill_layer_graph_replays():
                 outs[i].copy_(o)
 
     _check_replays(run_calls, len(routes), lambda: layer(*routes[1]))
+
+
+@pytest.mark.parametrize("m", [1, 16, 1024])
+def test_graph_replay_with_new_routing_and_activations(m):
+    """A captured layer reads its inputs from the captured buffers: after new ids, routing weights
+    and activations are copied into them in place, a replay gives bitwise the eager result for the
+    new inputs (decode with the plan in W13, and the prefill regime)."""
+    d = _weights()
+    layer = G.MoELayer(m, 10, d["w13"], d["w2"])
+    routes = _routes(m, 4, 500 + m)
+    x, ids, tw = (t.clone() for t in routes[0])
+    out = torch.empty((m, 2048), dtype=torch.float16, device="cuda")
+    layer(x, ids, tw)  # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out.copy_(layer(x, ids, tw))
+    for i in range(1, 4):
+        xn, idn, twn = routes[i]
+        ref = layer(xn, idn, twn).clone()  # eager, on the new inputs
+        x.copy_(xn)
+        ids.copy_(idn)
+        tw.copy_(twn)
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay with routes[{i}]"
+    del g
