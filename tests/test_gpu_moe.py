@@ -165,3 +165,36 @@ def test_moe_maximum_reduction_lengths(orc, m):
               "tw": d["tw"][t:t + 1].contiguous(), "w13": d["w13"], "w2": d["w2"]}
         single = run_moe(one, 0, dev=dd)["out"][0]
         assert torch.equal(single.view(torch.int16), res["out"][t].view(torch.int16)), f"token {t}"
+
+
+def test_moe_general_negative_subnormal_and_nan_scales(orc):
+    """Block scales beyond powers of two: E4M3 bytes with mantissa bits, negative and subnormal
+    ones (0x01..0x30 and their negatives). A NaN scale (0x7F) in one W2 row makes that output column
+    NaN and nothing else; a NaN scale in a W13 gate row makes the token's whole output NaN (its h row
+    feeds every W2 row). NaN propagates by IEEE rules, as in the oracle."""
+    sb = np.array([b for b in range(0x01, 0x31)] + [0x80 | b for b in range(0x01, 0x31)], dtype=np.uint8)
+    case = S.moe_case(S.TINY, workload="tiny", route_pattern=11, scale_bytes=sb)
+    e0, e1 = int(case["ids"][0, 0]), int(case["ids"][0, 1])
+    assert e0 != e1 and e0 >= 0 and e1 >= 0
+    w2c, w2s, w2g = case["w2"]
+    w2s = w2s.copy()
+    w2s[e1, 5, 3] = 0x7F  # W2 row 5 of the second slot's expert
+    case = dict(case, w2=(w2c, w2s, w2g))
+    res = run_moe(case, 0)
+    pl = orc.plan(case["ids"], S.TINY.e, 16)
+    h_ref, out_ref = orc.moe_grouped(case, pl)
+    out = to_np64(res["out"])
+    assert np.isnan(out[0, 5]) and np.isnan(out_ref[0, 5])
+    assert np.isfinite(np.delete(out[0], 5)).all()
+    assert_rows_close(to_np64(res["h"][: pl["n_valid"]]), h_ref, "general scales h")
+    assert_rows_close(out, out_ref, "general scales out (NaN column)")
+    # NaN in a W13 gate row of the first slot's expert
+    w13c, w13s, w13g = case["w13"]
+    w13s = w13s.copy()
+    w13s[e0, 7, 2] = 0x7F
+    case2 = dict(case, w13=(w13c, w13s, w13g), w2=(w2c, case["w2"][1].copy(), w2g))
+    case2["w2"][1][e1, 5, 3] = 0x08
+    res2 = run_moe(case2, 0)
+    h2_ref, out2_ref = orc.moe_grouped(case2, orc.plan(case2["ids"], S.TINY.e, 16))
+    assert np.isnan(to_np64(res2["out"])).all() and np.isnan(out2_ref).all()
+    assert_rows_close(to_np64(res2["h"][: pl["n_valid"]]), h2_ref, "NaN gate row h")
