@@ -9,11 +9,14 @@ from ._lib import (  # noqa: F401
     NVFP4Error,
     NVFP4Tensor,
     header_functions,
+    layer_workspace_parts,
     lib,
     nvfp4_abi_version,
     nvfp4_linear,
     nvfp4_linear_fp8,
     nvfp4_linear_swiglu,
+    nvfp4_moe_layer,
+    nvfp4_moe_layer_workspace_bytes,
     nvfp4_moe_plan,
     nvfp4_moe_plan_bytes,
     nvfp4_moe_plan_w13_swiglu,

@@ -63,6 +63,9 @@ _SIGS = {
     "nvfp4_moe_plan_w13_swiglu": (C.c_int, [_vp, _i32, _i32, _i32, _vp, _sz, _vp, C.POINTER(nvfp4_weights), _i32, _vp,
                                             _vp]),
     "nvfp4_linear_fp8": (C.c_int, [_vp, _i32, C.POINTER(fp8_channel_weights), _vp, _vp]),
+    "nvfp4_moe_layer_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "nvfp4_moe_layer": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _i32,
+                                  C.POINTER(nvfp4_weights), _vp, _vp, _vp, _sz, _vp]),
 }
 
 
@@ -109,6 +112,28 @@ def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> int:
 def _stream(stream) -> int:
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+def _shape(t: torch.Tensor, name: str, shape: tuple):
+    """Raise unless t has exactly this shape (the library reads and writes by these sizes)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _rows(t: torch.Tensor, name: str, min_rows: int, cols: int):
+    """Raise unless t is [>= min_rows, cols] (bucket-order buffers may be longer than needed)."""
+    if t.dim() != 2 or t.shape[1] != cols or t.shape[0] < min_rows:
+        raise ValueError(f"{name} must have shape [>= {min_rows}, {cols}], got {tuple(t.shape)}")
+
+
+def _bytes(t: torch.Tensor, name: str, need: int):
+    if t.numel() * t.element_size() < need:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, {need} needed")
+
+
+def _plan_ok(plan: torch.Tensor, M: int, topk: int, E: int):
+    """The W13/W2 calls take no plan size: check here that the buffer is large enough."""
+    _bytes(plan, "plan", nvfp4_moe_plan_bytes(M, topk, E))
 
 
 class NVFP4Tensor:
@@ -180,8 +205,11 @@ def nvfp4_moe_w13_swiglu(plan: torch.Tensor, M: int, topk: int, E: int, x: torch
                          layout: int = 0, h: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Grouped W13 + SwiGLU. Returns h fp16 [M*topk, I] in bucket order (rows >= n_valid untouched)."""
     I = w13.rows // 2
+    _shape(x, "x", (M, w13.k))
+    _plan_ok(plan, M, topk, E)
     if h is None:
         h = torch.empty((M * topk, I), dtype=torch.float16, device=x.device)
+    _rows(h, "h", M * topk, I)
     d = w13.desc()
     _check("nvfp4_moe_w13_swiglu", lib().nvfp4_moe_w13_swiglu(
         _dev(plan, "plan", torch.int32), M, topk, E, _dev(x, "x", torch.float16), C.byref(d), layout,
@@ -194,10 +222,12 @@ def nvfp4_moe_plan_w13_swiglu(topk_ids: torch.Tensor, E: int, x: torch.Tensor, w
     """nvfp4_moe_plan followed by nvfp4_moe_w13_swiglu, one launch for small batches. Returns (plan, h)."""
     M, topk = topk_ids.shape
     I = w13.rows // 2
+    _shape(x, "x", (M, w13.k))
     if plan is None:
         plan = torch.empty(max(nvfp4_moe_plan_bytes(M, topk, E), 4) // 4, dtype=torch.int32, device=x.device)
     if h is None:
         h = torch.empty((M * topk, I), dtype=torch.float16, device=x.device)
+    _rows(h, "h", M * topk, I)
     d = w13.desc()
     _check("nvfp4_moe_plan_w13_swiglu", lib().nvfp4_moe_plan_w13_swiglu(
         _dev(topk_ids, "topk_ids", torch.int32), M, topk, E, _dev(plan, "plan", torch.int32), plan.numel() * 4,
@@ -214,8 +244,12 @@ def nvfp4_moe_w2_reduce(plan: torch.Tensor, M: int, topk: int, E: int, h: torch.
                         stream=None) -> torch.Tensor:
     """Grouped W2 + slot-ordered top-k weighted reduction. Returns out fp16 [M, K]."""
     K = w2.rows
+    _plan_ok(plan, M, topk, E)
+    _rows(h, "h", M * topk, w2.k)
+    _shape(topk_weights, "topk_weights", (M, topk))
     if out is None:
         out = torch.empty((M, K), dtype=torch.float16, device=h.device)
+    _shape(out, "out", (M, K))
     if ws is None:
         ws = torch.empty(max(nvfp4_moe_w2_workspace_bytes(M, topk, K), 4), dtype=torch.uint8, device=h.device)
     d = w2.desc()
@@ -233,9 +267,13 @@ def nvfp4_moe_shared_expert(x: torch.Tensor, w13: NVFP4Tensor, w2: NVFP4Tensor, 
     M, K = x.shape
     I = w13.rows // 2
     dev = x.device
+    _shape(gate, "gate", (K,))
     h = torch.empty((M, I), dtype=torch.float16, device=dev) if h is None else h
     shared_y = torch.empty((M, K), dtype=torch.float32, device=dev) if shared_y is None else shared_y
     shared_sigma = torch.empty((M,), dtype=torch.float32, device=dev) if shared_sigma is None else shared_sigma
+    _shape(h, "h", (M, I))
+    _shape(shared_y, "shared_y", (M, K))
+    _shape(shared_sigma, "shared_sigma", (M,))
     d13, d2 = w13.desc(), w2.desc()
     _check("nvfp4_moe_shared_expert", lib().nvfp4_moe_shared_expert(
         _dev(x, "x", torch.float16), M, C.byref(d13), layout, C.byref(d2), _dev(gate, "gate", torch.float16),
@@ -251,7 +289,13 @@ def nvfp4_moe_w2_reduce_shared(plan: torch.Tensor, M: int, topk: int, E: int, h:
     """Grouped W2 + slot-order reduction with the shared expert added last. Returns out fp16 [M, K]."""
     K = w2.rows
     dev = h.device
+    _plan_ok(plan, M, topk, E)
+    _rows(h, "h", M * topk, w2.k)
+    _shape(topk_weights, "topk_weights", (M, topk))
+    _shape(shared_y, "shared_y", (M, K))
+    _shape(shared_sigma, "shared_sigma", (M,))
     out = torch.empty((M, K), dtype=torch.float16, device=dev) if out is None else out
+    _shape(out, "out", (M, K))
     if ws is None:
         ws = torch.empty(max(nvfp4_moe_w2_workspace_bytes(M, topk, K), 256), dtype=torch.uint8, device=dev)
     d = w2.desc()
@@ -266,8 +310,10 @@ def nvfp4_moe_w2_reduce_shared(plan: torch.Tensor, M: int, topk: int, E: int, h:
 def nvfp4_linear(x: torch.Tensor, w: NVFP4Tensor, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Dense NVFP4 projection y = x W^T. x fp16 [M, K]; returns fp16 [M, N]."""
     M = x.shape[0]
+    _shape(x, "x", (M, w.k))
     if y is None:
         y = torch.empty((M, w.rows), dtype=torch.float16, device=x.device)
+    _shape(y, "y", (M, w.rows))
     d = w.desc()
     _check("nvfp4_linear", lib().nvfp4_linear(_dev(x, "x", torch.float16), M, C.byref(d),
                                               _dev(y, "y", torch.float16), _stream(stream)))
@@ -296,8 +342,10 @@ class FP8ChannelTensor:
 def nvfp4_linear_fp8(x: torch.Tensor, w: FP8ChannelTensor, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Channel-FP8 dense projection y = fp16(s * (x @ e4m3(W)^T)) of fp16 x [M, K]; returns y [M, N]."""
     M = x.shape[0]
+    _shape(x, "x", (M, w.k))
     if y is None:
         y = torch.empty((M, w.rows), dtype=torch.float16, device=x.device)
+    _shape(y, "y", (M, w.rows))
     d = w.desc()
     _check("nvfp4_linear_fp8", lib().nvfp4_linear_fp8(_dev(x, "x", torch.float16), M, C.byref(d),
                                                       _dev(y, "y", torch.float16), _stream(stream)))
@@ -309,33 +357,82 @@ def nvfp4_linear_swiglu(x: torch.Tensor, w13: NVFP4Tensor, layout: int = 0, h: t
     """Gated dense projection h = fp16(silu(x Wg^T) * (x Wu^T)) of fp16 x [M, K]; returns h [M, I]."""
     M = x.shape[0]
     I = w13.rows // 2
+    _shape(x, "x", (M, w13.k))
     if h is None:
         h = torch.empty((M, I), dtype=torch.float16, device=x.device)
+    _shape(h, "h", (M, I))
     d = w13.desc()
     _check("nvfp4_linear_swiglu", lib().nvfp4_linear_swiglu(_dev(x, "x", torch.float16), M, C.byref(d), layout,
                                                             _dev(h, "h", torch.float16), _stream(stream)))
     return h
 
 
+def nvfp4_moe_layer_workspace_bytes(M: int, topk: int, E: int, K: int, I: int) -> int:
+    return int(lib().nvfp4_moe_layer_workspace_bytes(M, topk, E, K, I))
+
+
+def layer_workspace_parts(M: int, topk: int, E: int, I: int) -> tuple[int, int]:
+    """Byte offsets of h and of the W2 workspace inside the layer workspace (the plan is at 0)."""
+    h_off = nvfp4_moe_plan_bytes(M, topk, E)
+    return h_off, h_off + (M * topk * I * 2 + 255) // 256 * 256
+
+
+def nvfp4_moe_layer(topk_ids: torch.Tensor, E: int, x: torch.Tensor, w13: NVFP4Tensor, w2: NVFP4Tensor,
+                    topk_weights: torch.Tensor, layout: int = 0, out: torch.Tensor | None = None,
+                    ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The whole MoE layer (plan, W13 + SwiGLU, W2 + slot-order reduction) in one library call.
+    Returns out fp16 [M, K]; ws (uint8) then holds the plan, h and the W2 workspace."""
+    M, topk = topk_ids.shape
+    K, I = w13.k, w13.rows // 2
+    _shape(x, "x", (M, K))
+    _shape(topk_weights, "topk_weights", (M, topk))
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float16, device=x.device)
+    _shape(out, "out", (M, K))
+    need = nvfp4_moe_layer_workspace_bytes(M, topk, E, K, I)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _bytes(ws, "ws", need)
+    d13, d2 = w13.desc(), w2.desc()
+    _check("nvfp4_moe_layer", lib().nvfp4_moe_layer(
+        _dev(topk_ids, "topk_ids", torch.int32), M, topk, E, _dev(x, "x", torch.float16), C.byref(d13), layout,
+        C.byref(d2), _dev(topk_weights, "topk_weights", torch.float32), _dev(out, "out", torch.float16),
+        _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream)))
+    return out
+
+
 class MoELayer:
-    """One MoE layer call (plan + W13+SwiGLU, then W2+reduce) with its buffers allocated once, so
-    the launches can be replayed (or captured in a HIP graph) without allocation."""
+    """One MoE layer call (nvfp4_moe_layer: plan + W13+SwiGLU, then W2+reduce) with its buffers
+    allocated once, so the call can be replayed (or captured in a HIP graph) without allocation.
+    plan, h and ws are views into the one layer workspace."""
 
     def __init__(self, M: int, topk: int, w13: NVFP4Tensor, w2: NVFP4Tensor, layout: int = 0, device="cuda"):
         self.M, self.topk, self.E = M, topk, w13.groups
         self.K, self.I = w13.k, w13.rows // 2
+        if w2.groups != self.E or w2.rows != self.K or w2.k != self.I:
+            raise ValueError("w2 must be [E, K, I] for w13 [E, 2I, K]")
         self.w13, self.w2, self.layout = w13, w2, layout
-        self.plan = torch.empty(max(nvfp4_moe_plan_bytes(M, topk, self.E), 4) // 4, dtype=torch.int32, device=device)
-        self.h = torch.empty((M * topk, self.I), dtype=torch.float16, device=device)
-        self.ws = torch.empty(max(nvfp4_moe_w2_workspace_bytes(M, topk, self.K), 4), dtype=torch.uint8, device=device)
+        need = nvfp4_moe_layer_workspace_bytes(M, topk, self.E, self.K, self.I)
+        self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        h_off, w2_off = layer_workspace_parts(M, topk, self.E, self.I)
+        self.plan = self.workspace[:h_off].view(torch.int32)
+        self.h = self.workspace[h_off:h_off + M * topk * self.I * 2].view(torch.float16).view(M * topk, self.I)
+        self.ws = self.workspace[w2_off:]
         self.out = torch.empty((M, self.K), dtype=torch.float16, device=device)
+
+    def _same(self, w: NVFP4Tensor, ref: NVFP4Tensor, name: str):
+        if (w.groups, w.rows, w.k) != (ref.groups, ref.rows, ref.k):
+            raise ValueError(f"{name} override must have the layer's shape {(ref.groups, ref.rows, ref.k)}")
 
     def __call__(self, x, topk_ids, topk_weights, w13: NVFP4Tensor | None = None, w2: NVFP4Tensor | None = None,
                  stream=None):
-        nvfp4_moe_plan_w13_swiglu(topk_ids, self.E, x, w13 or self.w13, self.layout, plan=self.plan, h=self.h,
-                                  stream=stream)
-        nvfp4_moe_w2_reduce(self.plan, self.M, self.topk, self.E, self.h, w2 or self.w2, topk_weights,
-                            out=self.out, ws=self.ws, stream=stream)
+        if w13 is not None:
+            self._same(w13, self.w13, "w13")
+        if w2 is not None:
+            self._same(w2, self.w2, "w2")
+        _shape(topk_ids, "topk_ids", (self.M, self.topk))
+        nvfp4_moe_layer(topk_ids, self.E, x, w13 or self.w13, w2 or self.w2, topk_weights, self.layout, out=self.out,
+                        ws=self.workspace, stream=stream)
         return self.out
 
 
@@ -373,9 +470,15 @@ def nvfp4_moe_w13_swiglu_with_shared(plan: torch.Tensor, M: int, topk: int, E: i
     Returns (h fp16 [M*topk, I] in bucket order, shared_h fp16 [M, Is], shared_sigma FP32 [M])."""
     I, Is = w13.rows // 2, shared_w13.rows // 2
     dev = x.device
+    _shape(x, "x", (M, w13.k))
+    _shape(gate, "gate", (w13.k,))
+    _plan_ok(plan, M, topk, E)
     h = torch.empty((M * topk, I), dtype=torch.float16, device=dev) if h is None else h
     shared_h = torch.empty((M, Is), dtype=torch.float16, device=dev) if shared_h is None else shared_h
     shared_sigma = torch.empty((M,), dtype=torch.float32, device=dev) if shared_sigma is None else shared_sigma
+    _rows(h, "h", M * topk, I)
+    _shape(shared_h, "shared_h", (M, Is))
+    _shape(shared_sigma, "shared_sigma", (M,))
     d, ds = w13.desc(), shared_w13.desc()
     _check("nvfp4_moe_w13_swiglu_with_shared", lib().nvfp4_moe_w13_swiglu_with_shared(
         _dev(plan, "plan", torch.int32), M, topk, E, _dev(x, "x", torch.float16), C.byref(d), layout,
@@ -395,11 +498,16 @@ def nvfp4_moe_plan_w13_swiglu_with_shared(topk_ids: torch.Tensor, E: int, x: tor
     M, topk = topk_ids.shape
     I, Is = w13.rows // 2, shared_w13.rows // 2
     dev = x.device
+    _shape(x, "x", (M, w13.k))
+    _shape(gate, "gate", (w13.k,))
     if plan is None:
         plan = torch.empty(max(nvfp4_moe_plan_bytes(M, topk, E), 4) // 4, dtype=torch.int32, device=dev)
     h = torch.empty((M * topk, I), dtype=torch.float16, device=dev) if h is None else h
     shared_h = torch.empty((M, Is), dtype=torch.float16, device=dev) if shared_h is None else shared_h
     shared_sigma = torch.empty((M,), dtype=torch.float32, device=dev) if shared_sigma is None else shared_sigma
+    _rows(h, "h", M * topk, I)
+    _shape(shared_h, "shared_h", (M, Is))
+    _shape(shared_sigma, "shared_sigma", (M,))
     d, ds = w13.desc(), shared_w13.desc()
     _check("nvfp4_moe_plan_w13_swiglu_with_shared", lib().nvfp4_moe_plan_w13_swiglu_with_shared(
         _dev(topk_ids, "topk_ids", torch.int32), M, topk, E, _dev(plan, "plan", torch.int32), plan.numel() * 4,
@@ -418,8 +526,15 @@ def nvfp4_moe_w2_reduce_with_shared(plan: torch.Tensor, M: int, topk: int, E: in
     and its term added last. Returns out fp16 [M, K]."""
     K = w2.rows
     dev = h.device
+    _plan_ok(plan, M, topk, E)
+    _rows(h, "h", M * topk, w2.k)
+    _shape(topk_weights, "topk_weights", (M, topk))
+    _shape(shared_h, "shared_h", (M, shared_w2.k))
+    _shape(shared_sigma, "shared_sigma", (M,))
     out = torch.empty((M, K), dtype=torch.float16, device=dev) if out is None else out
     shared_y = torch.empty((M, K), dtype=torch.float32, device=dev) if shared_y is None else shared_y
+    _shape(out, "out", (M, K))
+    _shape(shared_y, "shared_y", (M, K))
     if ws is None:
         ws = torch.empty(max(nvfp4_moe_w2_workspace_bytes(M, topk, K), 256), dtype=torch.uint8, device=dev)
     d, ds = w2.desc(), shared_w2.desc()

@@ -100,6 +100,48 @@ NVFP4_API int nvfp4_moe_w13_swiglu(const void *plan, int32_t M, int32_t topk, in
     return nvfp4::run_w13(nvfp4::plan_view(plan, L), L.T, topk, x, *w13, layout, h, s);
 }
 
+namespace {
+
+// The plan and W13 after every check passed: one launch (the plan built in the W13 launch) for
+// small decode batches, else the plan's launches and then the regime's W13 kernel.
+int enqueue_plan_w13(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E, int32_t *pl, const uint16_t *x,
+                     const nvfp4_weights &w13, int32_t layout, uint16_t *h, hipStream_t s)
+{
+    const int K = w13.k, I = w13.rows / 2;
+    const PlanLayout L = nvfp4::plan_layout(M, topk, E);
+    const bool prefill = nvfp4::use_prefill(M, L.P, E, K, I);
+    if (!prefill && nvfp4::use_fused_plan(L.P, E)) {
+        nvfp4::FusedPlan fp;
+        fp.ids = topk_ids;
+        fp.plan = pl;
+        fp.L = L;
+        fp.M = M;
+        fp.E = E;
+        return nvfp4::run_w13(nvfp4::plan_view(pl, L), L.T, topk, x, w13, layout, h, s, {}, fp);
+    }
+    int st = nvfp4::run_plan(topk_ids, M, topk, E, pl, L, s);
+    if (st != NVFP4_OK) return st;
+    if (prefill) return nvfp4::run_w13_prefill(nvfp4::plan_view(pl, L), L.A, M, topk, x, w13, layout, h, s);
+    return nvfp4::run_w13(nvfp4::plan_view(pl, L), L.T, topk, x, w13, layout, h, s);
+}
+
+// W2 and the reduction after every check passed.
+int enqueue_w2(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16_t *h, const nvfp4_weights &w2,
+               const float *topk_weights, uint16_t *out, void *ws, hipStream_t s, nvfp4::SharedTerm sh)
+{
+    const int K = w2.rows, I = w2.k;
+    const PlanLayout L = nvfp4::plan_layout(M, topk, E);
+    const nvfp4::PlanView pv = nvfp4::plan_view(plan, L);
+    if (nvfp4::use_prefill(M, L.P, E, K, I)) {
+        const int st = nvfp4::run_w2_prefill(pv, L.A, L.P, h, w2, static_cast<float *>(ws), s);
+        if (st != NVFP4_OK) return st;
+        return nvfp4::run_reduce(pv, M, topk, K, topk_weights, static_cast<const float *>(ws), out, s, sh);
+    }
+    return nvfp4::run_w2(pv, L.T, M, topk, h, w2, topk_weights, out, static_cast<float *>(ws), s, sh);
+}
+
+}  // namespace
+
 NVFP4_API int nvfp4_moe_plan_w13_swiglu(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E, void *plan,
                                         size_t plan_bytes, const uint16_t *x, const nvfp4_weights *w13,
                                         int32_t layout, uint16_t *h, void *stream)
@@ -118,22 +160,8 @@ NVFP4_API int nvfp4_moe_plan_w13_swiglu(const int32_t *topk_ids, int32_t M, int3
     if (!aligned(topk_ids, 4) || !aligned(plan, 16) || !aligned(x, 16) || !aligned(h, 16)) return NVFP4_ERR_ALIGN;
     const PlanLayout L = nvfp4::plan_layout(M, topk, E);
     if (plan_bytes < (size_t)L.words * sizeof(int32_t)) return NVFP4_ERR_WORKSPACE;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    int32_t *pl = static_cast<int32_t *>(plan);
-    const bool prefill = nvfp4::use_prefill(M, L.P, E, K, I);
-    if (!prefill && nvfp4::use_fused_plan(L.P, E)) {
-        nvfp4::FusedPlan fp;
-        fp.ids = topk_ids;
-        fp.plan = pl;
-        fp.L = L;
-        fp.M = M;
-        fp.E = E;
-        return nvfp4::run_w13(nvfp4::plan_view(plan, L), L.T, topk, x, *w13, layout, h, s, {}, fp);
-    }
-    st = nvfp4::run_plan(topk_ids, M, topk, E, pl, L, s);
-    if (st != NVFP4_OK) return st;
-    if (prefill) return nvfp4::run_w13_prefill(nvfp4::plan_view(plan, L), L.A, M, topk, x, *w13, layout, h, s);
-    return nvfp4::run_w13(nvfp4::plan_view(plan, L), L.T, topk, x, *w13, layout, h, s);
+    return enqueue_plan_w13(topk_ids, M, topk, E, static_cast<int32_t *>(plan), x, *w13, layout, h,
+                            static_cast<hipStream_t>(stream));
 }
 
 NVFP4_API size_t nvfp4_moe_w2_workspace_bytes(int32_t M, int32_t topk, int32_t K)
@@ -161,15 +189,7 @@ int w2_reduce(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16
         return NVFP4_ERR_ALIGN;
     if (sh.y && (!aligned(sh.y, 16) || !aligned(sh.sigma, 4))) return NVFP4_ERR_ALIGN;
     if (ws_bytes < nvfp4_moe_w2_workspace_bytes(M, topk, K)) return NVFP4_ERR_WORKSPACE;
-    const PlanLayout L = nvfp4::plan_layout(M, topk, E);
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    const nvfp4::PlanView pv = nvfp4::plan_view(plan, L);
-    if (nvfp4::use_prefill(M, L.P, E, K, I)) {
-        const int st = nvfp4::run_w2_prefill(pv, L.A, L.P, h, *w2, static_cast<float *>(ws), s);
-        if (st != NVFP4_OK) return st;
-        return nvfp4::run_reduce(pv, M, topk, w2->rows, topk_weights, static_cast<const float *>(ws), out, s, sh);
-    }
-    return nvfp4::run_w2(pv, L.T, M, topk, h, *w2, topk_weights, out, static_cast<float *>(ws), s, sh);
+    return enqueue_w2(plan, M, topk, E, h, *w2, topk_weights, out, ws, static_cast<hipStream_t>(stream), sh);
 }
 
 }  // namespace
@@ -193,6 +213,88 @@ NVFP4_API int nvfp4_moe_w2_reduce_shared(const void *plan, int32_t M, int32_t to
     return w2_reduce(plan, M, topk, E, h, w2, topk_weights, out, ws, ws_bytes, stream, sh);
 }
 
+namespace {
+
+// Byte offsets of the layer workspace's parts: plan, h, W2 workspace (each a multiple of 256).
+struct LayerParts {
+    size_t h, w2, total;
+};
+
+LayerParts layer_parts(int32_t M, int32_t topk, int32_t E, int32_t K, int32_t I)
+{
+    LayerParts p;
+    p.h = nvfp4_moe_plan_bytes(M, topk, E);
+    const size_t hb = (size_t)M * topk * I * 2;
+    p.w2 = p.h + ((hb + 255) & ~(size_t)255);
+    p.total = p.w2 + nvfp4_moe_w2_workspace_bytes(M, topk, K);
+    return p;
+}
+
+bool layer_shape_ok(int32_t M, int32_t topk, int32_t E, int32_t K, int32_t I)
+{
+    return plan_shape_ok(M, topk, E) && K >= 16 && I >= 1;
+}
+
+// Every check of nvfp4_moe_plan_w13_swiglu and nvfp4_moe_w2_reduce for the layer call, except the
+// workspace size. Returns the status; on OK, *K_out and *I_out are the layer's sizes.
+int check_layer(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E, const uint16_t *x,
+                const nvfp4_weights *w13, int32_t layout, const nvfp4_weights *w2, const float *topk_weights,
+                const uint16_t *out, int32_t *K_out, int32_t *I_out)
+{
+    if (!plan_shape_ok(M, topk, E) || (layout != 0 && layout != 1)) return NVFP4_ERR_SHAPE;
+    if (E > nvfp4::MAX_EXPERTS) return NVFP4_ERR_UNSUPPORTED;
+    int st = check_weights(w13);
+    if (st == NVFP4_OK) st = check_weights(w2);
+    if (st != NVFP4_OK) return st;
+    if (w13->groups != E || w13->rows % 2 != 0 || w2->groups != E) return NVFP4_ERR_SHAPE;
+    const int K = w13->k, I = w13->rows / 2;
+    if (w2->rows != K || w2->k != I) return NVFP4_ERR_SHAPE;
+    if (K % 128 != 0 || K > nvfp4::MAX_MOE_RED || I % 128 != 0 || I > nvfp4::MAX_MOE_RED)
+        return NVFP4_ERR_UNSUPPORTED;
+    *K_out = K;
+    *I_out = I;
+    if (M == 0) return NVFP4_OK;
+    if (!topk_ids || !x || !topk_weights || !out) return NVFP4_ERR_NULL;
+    if (!aligned(topk_ids, 4) || !aligned(x, 16) || !aligned(topk_weights, 4) || !aligned(out, 16))
+        return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+// The layer on a workspace that passed every check: plan + W13, then W2 + reduction.
+int enqueue_layer(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E, const uint16_t *x,
+                  const nvfp4_weights &w13, int32_t layout, const nvfp4_weights &w2, const float *topk_weights,
+                  uint16_t *out, uint8_t *ws, hipStream_t s)
+{
+    const LayerParts parts = layer_parts(M, topk, E, w13.k, w13.rows / 2);
+    int32_t *plan = reinterpret_cast<int32_t *>(ws);
+    uint16_t *h = reinterpret_cast<uint16_t *>(ws + parts.h);
+    const int st = enqueue_plan_w13(topk_ids, M, topk, E, plan, x, w13, layout, h, s);
+    if (st != NVFP4_OK) return st;
+    return enqueue_w2(plan, M, topk, E, h, w2, topk_weights, out, ws + parts.w2, s, {});
+}
+
+}  // namespace
+
+NVFP4_API size_t nvfp4_moe_layer_workspace_bytes(int32_t M, int32_t topk, int32_t E, int32_t K, int32_t I)
+{
+    if (!layer_shape_ok(M, topk, E, K, I)) return 0;
+    return layer_parts(M, topk, E, K, I).total;
+}
+
+NVFP4_API int nvfp4_moe_layer(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E, const uint16_t *x,
+                              const nvfp4_weights *w13, int32_t layout, const nvfp4_weights *w2,
+                              const float *topk_weights, uint16_t *out, void *ws, size_t ws_bytes, void *stream)
+{
+    int32_t K = 0, I = 0;
+    const int st = check_layer(topk_ids, M, topk, E, x, w13, layout, w2, topk_weights, out, &K, &I);
+    if (st != NVFP4_OK || M == 0) return st;
+    if (!ws) return NVFP4_ERR_NULL;
+    if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
+    if (ws_bytes < layer_parts(M, topk, E, K, I).total) return NVFP4_ERR_WORKSPACE;
+    return enqueue_layer(topk_ids, M, topk, E, x, *w13, layout, *w2, topk_weights, out, static_cast<uint8_t *>(ws),
+                         static_cast<hipStream_t>(stream));
+}
+
 NVFP4_API int nvfp4_moe_shared_expert(const uint16_t *x, int32_t M, const nvfp4_weights *w13, int32_t layout,
                                       const nvfp4_weights *w2, const uint16_t *gate, uint16_t *h, float *shared_y,
                                       float *shared_sigma, void *stream)
@@ -211,7 +313,8 @@ NVFP4_API int nvfp4_moe_shared_expert(const uint16_t *x, int32_t M, const nvfp4_
     if (!aligned(x, 16) || !aligned(h, 16) || !aligned(shared_y, 16) || !aligned(gate, 2) || !aligned(shared_sigma, 4))
         return NVFP4_ERR_ALIGN;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    st = nvfp4::run_linear_swiglu(x, M, *w13, layout, h, s);
+    st = nvfp4::linear_prepare();
+    if (st == NVFP4_OK) st = nvfp4::run_linear_swiglu(x, M, *w13, layout, h, s);
     if (st == NVFP4_OK) st = nvfp4::run_linear_f32(h, M, *w2, shared_y, s);
     if (st == NVFP4_OK) st = nvfp4::run_shared_gate(x, M, K, gate, shared_sigma, s);
     return st;
@@ -252,6 +355,8 @@ NVFP4_API int nvfp4_moe_w13_swiglu_with_shared(const void *plan, int32_t M, int3
         return nvfp4::run_w13(pv, L.T, topk, x, *w13, layout, h, s, shx);
     }
     // Separate launches: the routed regime's W13, then the shared expert's gate/up and its gate.
+    st = nvfp4::linear_prepare();
+    if (st != NVFP4_OK) return st;
     st = nvfp4::use_prefill(M, L.P, E, K, I) ? nvfp4::run_w13_prefill(pv, L.A, M, topk, x, *w13, layout, h, s)
                                               : nvfp4::run_w13(pv, L.T, topk, x, *w13, layout, h, s);
     if (st == NVFP4_OK) st = nvfp4::run_linear_swiglu(x, M, *shared_w13, layout, shared_h, s);
@@ -301,7 +406,8 @@ NVFP4_API int nvfp4_moe_plan_w13_swiglu_with_shared(const int32_t *topk_ids, int
         fp.E = E;
         return nvfp4::run_w13(nvfp4::plan_view(plan, L), L.T, topk, x, *w13, layout, h, s, shx, fp);
     }
-    st = nvfp4::run_plan(topk_ids, M, topk, E, static_cast<int32_t *>(plan), L, s);
+    st = nvfp4::linear_prepare();  // the call below may run the shared expert's own launches
+    if (st == NVFP4_OK) st = nvfp4::run_plan(topk_ids, M, topk, E, static_cast<int32_t *>(plan), L, s);
     if (st != NVFP4_OK) return st;
     return nvfp4_moe_w13_swiglu_with_shared(plan, M, topk, E, x, w13, layout, h, shared_w13, gate, shared_h,
                                             shared_sigma, stream);
@@ -343,7 +449,8 @@ NVFP4_API int nvfp4_moe_w2_reduce_with_shared(const void *plan, int32_t M, int32
         return nvfp4::run_w2(pv, L.T, M, topk, h, *w2, topk_weights, out, static_cast<float *>(ws), s, {}, shw);
     }
     // Separate launches: the shared expert's down projection, then W2 + reduction with its term.
-    st = nvfp4::run_linear_f32(shared_h, M, *shared_w2, shared_y, s);
+    st = nvfp4::linear_prepare();
+    if (st == NVFP4_OK) st = nvfp4::run_linear_f32(shared_h, M, *shared_w2, shared_y, s);
     if (st != NVFP4_OK) return st;
     nvfp4::SharedTerm sh;
     sh.y = shared_y;

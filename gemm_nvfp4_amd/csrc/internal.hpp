@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <tuple>
 #include <type_traits>
 #include <utility>
@@ -26,9 +27,34 @@ constexpr int MAX_TOPK = 32;
 // Largest reduction lengths with a kernel: the MoE kernels split at most four 512-element chunks
 // over a block's waves; the dense kernel keeps one LDS partial tile per chunk.
 constexpr int MAX_MOE_RED = 2048;
+// The dense kernels keep one FP32 partial tile per (chunk, row tile, weight tile) in LDS:
+// S * 2 * NW * 16 * 20 * 4 bytes for S = K/512 chunks and NW weight tiles per wave, within the
+// 160 KiB of a gfx950 CU. Two weight tiles per wave therefore fit up to K = 16384 and one up to
+// K = 32768; the plain projection takes one tile per wave beyond 16384.
 constexpr int MAX_LINEAR_K = 32768;
-constexpr int MAX_LINEAR_SWIGLU_K = 16384;  // two partial tiles per chunk: 160 KiB of LDS at most
-constexpr int MAX_LINEAR_FP8_K = 16384;     // likewise for the channel-FP8 projection
+constexpr int MAX_LINEAR_SWIGLU_K = 16384;  // always two weight tiles per wave (gate and up)
+constexpr int MAX_LINEAR_FP8_K = 16384;     // two weight tiles per wave when N % 32 == 0
+constexpr size_t MAX_LDS_BYTES = 160 * 1024;
+constexpr size_t linear_lds_bytes(int k, int nw) { return (size_t)((k + 511) / 512) * 2 * nw * 16 * 20 * 4; }
+// Weight tiles per wave of the plain dense projection: two when the rows pair up and the partial
+// tiles fit in LDS, else one.
+constexpr int linear_tiles(int rows, int k) { return rows % 32 == 0 && linear_lds_bytes(k, 2) <= MAX_LDS_BYTES ? 2 : 1; }
+
+// CU count of the current device, queried from the runtime once per device and cached.
+inline int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
 
 struct PlanLayout {
     int64_t P, A, T, G;
@@ -141,6 +167,9 @@ struct SharedW2 {
 int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uint16_t *h, const nvfp4_weights &w,
            const float *topk_weights, uint16_t *out, float *ws, hipStream_t s, SharedTerm sh = {},
            SharedW2 shw = {});
+// Lets the dense kernels use the CU's whole LDS; idempotent, cheap after the first call on a device.
+// Entry points that enqueue several launches call it before the first one.
+int linear_prepare();
 int run_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, uint16_t *y, hipStream_t s);
 int run_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights &w, uint16_t *y, hipStream_t s);
 int run_linear_swiglu(const uint16_t *x, int32_t M, const nvfp4_weights &w, int32_t layout, uint16_t *h,

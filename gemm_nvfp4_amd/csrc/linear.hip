@@ -244,6 +244,36 @@ __global__ __launch_bounds__(8 * 64) void linear_fp8_kernel(const f16 *__restric
     }
 }
 
+template <typename KernelT>
+hipError_t allow_lds(KernelT *kernel)
+{
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)MAX_LDS_BYTES);
+}
+
+}  // namespace
+
+// Opt every dense kernel into the CU's whole LDS (beyond the 64 KiB default), once per device.
+int linear_prepare()
+{
+    static std::atomic<int> done[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return NVFP4_ERR_LAUNCH;
+    if (dev < 64 && done[dev].load(std::memory_order_acquire)) return NVFP4_OK;
+    hipError_t e = allow_lds(linear_kernel<1, false, f16>);
+    if (e == hipSuccess) e = allow_lds(linear_kernel<2, false, f16>);
+    if (e == hipSuccess) e = allow_lds(linear_kernel<1, false, float>);
+    if (e == hipSuccess) e = allow_lds(linear_kernel<2, false, float>);
+    if (e == hipSuccess) e = allow_lds(linear_kernel<2, true, f16>);
+    if (e == hipSuccess) e = allow_lds(linear_fp8_kernel<1>);
+    if (e == hipSuccess) e = allow_lds(linear_fp8_kernel<2>);
+    if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
+    if (dev < 64) done[dev].store(1, std::memory_order_release);
+    return NVFP4_OK;
+}
+
+namespace {
+
 template <int NW>
 int launch_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights &w, uint16_t *y, hipStream_t s)
 {
@@ -251,11 +281,9 @@ int launch_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights &w
     const int S = num_chunks(K);
     const int waves = S < 8 ? S : 8;
     const size_t shmem = (size_t)S * ROW_GROUP * NW * 16 * LDS_ROW * sizeof(float);
-    if (shmem > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(linear_fp8_kernel<NW>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-        if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
-    }
+    if (shmem > MAX_LDS_BYTES) return NVFP4_ERR_UNSUPPORTED;  // the entry point admits no such K
+    const int st = linear_prepare();
+    if (st != NVFP4_OK) return st;
     return launch(linear_fp8_kernel<NW>, dim3((unsigned)(N / (16 * NW))), dim3((unsigned)(waves * 64)), shmem, s,
                   reinterpret_cast<const f16 *>(x), M, w.codes, w.channel_scale, N, K, reinterpret_cast<f16 *>(y));
 }
@@ -267,11 +295,10 @@ int launch_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, int N, i
     const int S = num_chunks(K);
     const int waves = S < max_waves<NW>() ? S : max_waves<NW>();
     const size_t shmem = (size_t)S * ROW_GROUP * NW * 16 * LDS_ROW * sizeof(float);
-    if (shmem > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(linear_kernel<NW, GATED, OUT>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-        if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
-    }
+    static_assert(ROW_GROUP == 2 && LDS_ROW == 20, "linear_lds_bytes assumes this partial-tile layout");
+    if (shmem != linear_lds_bytes(K, NW) || shmem > MAX_LDS_BYTES) return NVFP4_ERR_UNSUPPORTED;
+    const int st = linear_prepare();
+    if (st != NVFP4_OK) return st;
     const int blocks = GATED ? N / 16 : N / (16 * NW);
     return launch(linear_kernel<NW, GATED, OUT>, dim3((unsigned)blocks), dim3((unsigned)(waves * 64)), shmem, s,
                   reinterpret_cast<const f16 *>(x), M, w.codes, w.scales, w.global_scale, N, K, layout,
@@ -282,16 +309,13 @@ int launch_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, int N, i
 
 int run_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, uint16_t *y, hipStream_t s)
 {
-#ifndef NVFP4_LINEAR_TILES
-#define NVFP4_LINEAR_TILES 2
-#endif
-    if (NVFP4_LINEAR_TILES == 2 && w.rows % 32 == 0) return launch_linear<2, false>(x, M, w, w.rows, 0, y, s);
+    if (linear_tiles(w.rows, w.k) == 2) return launch_linear<2, false>(x, M, w, w.rows, 0, y, s);
     return launch_linear<1, false>(x, M, w, w.rows, 0, y, s);
 }
 
 int run_linear_f32(const uint16_t *x, int32_t M, const nvfp4_weights &w, float *y, hipStream_t s)
 {
-    if (w.rows % 32 == 0) return launch_linear<2, false, float>(x, M, w, w.rows, 0, y, s);
+    if (linear_tiles(w.rows, w.k) == 2) return launch_linear<2, false, float>(x, M, w, w.rows, 0, y, s);
     return launch_linear<1, false, float>(x, M, w, w.rows, 0, y, s);
 }
 

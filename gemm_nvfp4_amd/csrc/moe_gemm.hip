@@ -854,10 +854,7 @@ int split_for(int k)
 // *cus_out: the device's CU count.
 unsigned stream_grid(int occ, int64_t units_max, int64_t t_max, int *cus_out)
 {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
+    const int cus = device_cus();
     *cus_out = cus;
     static_assert(MAX_RANGE_TILES == 16, "the bound below assumes 16 staged row tiles");
     int64_t g = occ * (int64_t)cus;

@@ -32,7 +32,10 @@
  *     threads on different streams are safe. Two calls that write the same buffer must be ordered
  *     by the caller (for example, the same stream).
  *   - Errors fail closed: a nonzero status is returned, nothing is enqueued, and no output is
- *     touched. Status codes are NVFP4_* below; nvfp4_status_str() names them.
+ *     touched. Status codes are NVFP4_* below; nvfp4_status_str() names them. Every argument and
+ *     every launch's resources (grid, LDS) are checked before the first launch of a call, so the
+ *     one exception is NVFP4_ERR_LAUNCH from a call that enqueues several kernels: the runtime may
+ *     reject a later launch after earlier ones were enqueued, and the outputs are then undefined.
  *   - M = 0 is a successful no-op.
  *   - Arithmetic does not depend on M or on other tokens. A token's output is bitwise the same
  *     whether it runs alone or in any batch (for the MoE: with the same routing row and weights).
@@ -106,7 +109,9 @@ const char *nvfp4_status_str(int status);
  * sorted_pair; they let a kernel reach a tile's rows with one dependent load.
  *
  * The plan stays valid until the caller overwrites it. W13 and W2 only read it, and must be given
- * the same M, topk and E. Requirements: 1 <= topk <= 32, 1 <= E <= 4096, M*topk <= 2^26.
+ * the same M, topk and E. They take no plan size: the buffer must be one that nvfp4_moe_plan (or a
+ * call that builds the plan) wrote for that M, topk and E, else their reads are undefined.
+ * Requirements: 1 <= topk <= 32, 1 <= E <= 4096, M*topk <= 2^26.
  * --------------------------------------------------------------------------------------------- */
 size_t nvfp4_moe_plan_bytes(int32_t M, int32_t topk, int32_t E);
 int nvfp4_moe_plan(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E,
@@ -159,8 +164,9 @@ int nvfp4_moe_w13_swiglu(const void *plan, int32_t M, int32_t topk, int32_t E,
  *   x, w13, layout, h            as for nvfp4_moe_w13_swiglu
  * With M*topk <= 256, E <= 1024 and the decode (non-prefill) regime, it is one launch: every W13
  * block builds the plan of the ids in LDS and one block writes the plan buffer. Otherwise it
- * enqueues the plan and the W13 launch. Errors: those of the two calls, all checked before anything
- * is enqueued; M = 0 is an OK no-op.
+ * enqueues the plan and the W13 launch. Requirements: those of the two calls (K % 128 == 0,
+ * K <= 2048, I % 16 == 0). Errors: those of the two calls, all checked before anything is
+ * enqueued; M = 0 is an OK no-op.
  * --------------------------------------------------------------------------------------------- */
 int nvfp4_moe_plan_w13_swiglu(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E,
                               void *plan, size_t plan_bytes, const uint16_t *x,
@@ -186,6 +192,30 @@ int nvfp4_moe_w2_reduce(const void *plan, int32_t M, int32_t topk, int32_t E,
                         uint16_t *out, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * The whole MoE layer in one call: routing plan, grouped W13 + SwiGLU, grouped W2 and the
+ * slot-order reduction (no-MTP page, "Latest grouped-MoE screen", which times grouped W13 and
+ * grouped W2 together as one complete call). The results are bitwise those of
+ * nvfp4_moe_plan_w13_swiglu followed by nvfp4_moe_w2_reduce with the same arguments; one host call
+ * enqueues every launch.
+ *   topk_ids, M, topk, E   as for nvfp4_moe_plan
+ *   x, w13, layout         as for nvfp4_moe_w13_swiglu (K = w13->k, I = w13->rows / 2)
+ *   w2                     groups = E, rows = K, k = I
+ *   topk_weights, out      as for nvfp4_moe_w2_reduce
+ *   ws                     device workspace, at least nvfp4_moe_layer_workspace_bytes(M, topk, E, K,
+ *                          I) bytes, 16-byte aligned, contents ignored on entry. On return it holds
+ *                          the plan at byte 0 (nvfp4_moe_plan_bytes(M, topk, E) bytes, the layout of
+ *                          nvfp4_moe_plan), h (fp16 [M*topk][I], bucket order) at the next multiple of
+ *                          256 bytes, and the W2 workspace after that, also at a multiple of 256.
+ * Requirements: K % 128 == 0, K <= 2048, I % 128 == 0, I <= 2048, 1 <= topk <= 32, E <= 4096;
+ * topk_ids and topk_weights 4-byte aligned; x, out and codes 16-byte aligned. Errors: those of
+ * the calls it replaces, all checked before anything is enqueued; M = 0 is an OK no-op.
+ * --------------------------------------------------------------------------------------------- */
+size_t nvfp4_moe_layer_workspace_bytes(int32_t M, int32_t topk, int32_t E, int32_t K, int32_t I);
+int nvfp4_moe_layer(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E, const uint16_t *x,
+                    const nvfp4_weights *w13, int32_t layout, const nvfp4_weights *w2,
+                    const float *topk_weights, uint16_t *out, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Shared expert and shared gate (the "shared gate" among the fused MoE parts, no-MTP page, "Scope
  * and related PRs"; no formula is printed, so this is the plain reading): a dense NVFP4 gated MLP
  * on every token, scaled by sigmoid(x . g) and added to the routed output.
@@ -193,7 +223,8 @@ int nvfp4_moe_w2_reduce(const void *plan, int32_t M, int32_t topk, int32_t E,
  *     nvfp4_linear_swiglu); w2 groups = 1, rows = K, k = I; gate fp16 [K];
  *     h fp16 [M][I] (scratch, the gated MLP's h), shared_y FP32 [M][K] = W2 h (unrounded, global
  *     scale applied), shared_sigma FP32 [M] = 1 / (1 + exp(-sum_k x[m][k] gate[k])).
- *     Requirements: K % 128 == 0, K <= 16384, I % 128 == 0; x, h, shared_y 16-byte aligned.
+ *     Requirements: K % 128 == 0, K <= 16384, I % 128 == 0, I <= 32768; x, h, shared_y 16-byte
+ *     aligned.
  *   nvfp4_moe_w2_reduce_shared: nvfp4_moe_w2_reduce with the shared expert as one more slot after
  *     the routed ones: s = (routed fmaf chain); s = fmaf(shared_sigma[t], shared_y[t][n], s);
  *     out = fp16_rne(s). shared_y 16-byte aligned.
@@ -217,8 +248,9 @@ int nvfp4_moe_w2_reduce_shared(const void *plan, int32_t M, int32_t topk, int32_
  *     above), shared_w2 (groups = 1, rows = K, k = Is), shared_sigma, and shared_y FP32 [M][K],
  *     scratch that the call may overwrite with the shared expert's unrounded output.
  *     out = fp16_rne(fmaf(shared_sigma[t], y_shared[t][n], routed slot chain)).
- * Requirements: those of the routed calls; Is % 16 == 0 (W13) and Is % 128 == 0 (W2); shared_h,
- * shared_y 16-byte aligned; gate 2-byte aligned. The one-launch form needs Is == I, a 16-byte
+ * Requirements: those of the routed calls (K <= 2048 and I <= 2048 among them); Is % 16 == 0
+ * (W13) and Is % 128 == 0, Is <= 32768 (W2); shared_h, shared_y 16-byte aligned; gate 2-byte
+ * aligned. The one-launch form needs Is == I, a 16-byte
  * aligned gate and the streaming (not the prefill) regime; otherwise the call runs the shared
  * expert's own launches after the routed one, with the same results.
  * --------------------------------------------------------------------------------------------- */
@@ -248,7 +280,7 @@ int nvfp4_moe_w2_reduce_with_shared(const void *plan, int32_t M, int32_t topk, i
  *   y[m][n] = fp16_rne( global * sum_k x[m][k] * e2m1*e4m3 ),  FP32 accumulation.
  *   x  fp16 [M][K],  w  groups = 1, rows = N, k = K,  y  fp16 [M][N].
  * Any M works. The streaming kernel is tuned for M <= 32, the pages' admitted range.
- * Requirements: K % 128 == 0; N % 16 == 0; x, y, codes 16-byte aligned.
+ * Requirements: K % 128 == 0 and K <= 32768; N % 16 == 0; x, y, codes 16-byte aligned.
  * --------------------------------------------------------------------------------------------- */
 int nvfp4_linear(const uint16_t *x, int32_t M, const nvfp4_weights *w, uint16_t *y, void *stream);
 

@@ -12,7 +12,9 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvfp4moe.h")
-LIB = os.path.join(ROOT, "gemm_nvfp4_amd", "libnvfp4moe.so")
+# NVFP4_TEST_LIB: another build of the same library to check instead (the host-sanitizer build,
+# see tests/test_sanitizers.py).
+LIB = os.environ.get("NVFP4_TEST_LIB") or os.path.join(ROOT, "gemm_nvfp4_amd", "libnvfp4moe.so")
 
 
 @pytest.fixture(scope="module")
@@ -20,7 +22,12 @@ def L():
     if not os.path.exists(LIB):
         pytest.fail(f"{LIB} is not built (python gemm_nvfp4_amd/build.py)")
     from gemm_nvfp4_amd import _lib
-    return _lib.lib()
+    if not os.environ.get("NVFP4_TEST_LIB"):
+        return _lib.lib()
+    lib = C.CDLL(LIB)
+    for name, (res, args) in _lib._SIGS.items():
+        getattr(lib, name).restype, getattr(lib, name).argtypes = res, args
+    return lib
 
 
 def declared():
@@ -34,7 +41,7 @@ def test_header_declares_the_expected_entry_points():
         "nvfp4_moe_w13_swiglu", "nvfp4_moe_w2_workspace_bytes", "nvfp4_moe_w2_reduce", "nvfp4_linear",
         "nvfp4_linear_swiglu", "nvfp4_linear_fp8", "nvfp4_moe_shared_expert", "nvfp4_moe_w2_reduce_shared",
         "nvfp4_moe_w13_swiglu_with_shared", "nvfp4_moe_w2_reduce_with_shared", "nvfp4_moe_plan_w13_swiglu",
-        "nvfp4_moe_plan_w13_swiglu_with_shared"])
+        "nvfp4_moe_plan_w13_swiglu_with_shared", "nvfp4_moe_layer_workspace_bytes", "nvfp4_moe_layer"])
 
 
 def test_library_exports_every_declared_function():
@@ -153,3 +160,52 @@ def test_argument_checks_fail_closed(L):
     assert L.nvfp4_linear_fp8(fake, 4, C.byref(f8(odd, fake, 64, 128)), fake, null) == 3
     assert L.nvfp4_linear_fp8(fake, -1, C.byref(f8(fake, fake, 64, 128)), fake, null) == 2
     assert L.nvfp4_linear_fp8(null, 0, C.byref(f8(fake, fake, 64, 128)), null, null) == 0
+
+
+def test_dense_reduction_length_admission(L):
+    """The dense kernels keep one FP32 partial tile per chunk in LDS. The plain projection admits
+    K <= 32768 (one weight tile per wave past 16384, so the tiles fit in 160 KiB); the gated and
+    channel-FP8 forms keep two tiles per wave and admit K <= 16384. Beyond: ERR_UNSUPPORTED before
+    any launch. M = 0 reaches every check without launching."""
+    from gemm_nvfp4_amd._lib import nvfp4_weights, fp8_channel_weights as f8
+    fake, null = C.c_void_p(0x1000), None
+    for k, want in ((16384, 0), (16512, 0), (16896, 0), (32768, 0), (32896, 5), (65536, 5)):
+        for rows in (64, 48):  # paired 16-row tiles, and a single one
+            w = nvfp4_weights(fake, fake, fake, 1, rows, k)
+            assert L.nvfp4_linear(null, 0, C.byref(w), null, null) == want, (k, rows)
+    for k, want in ((16384, 0), (16896, 5), (32768, 5)):
+        assert L.nvfp4_linear_swiglu(null, 0, C.byref(nvfp4_weights(fake, fake, fake, 1, 64, k)), 0, null, null) == want
+        assert L.nvfp4_linear_fp8(null, 0, C.byref(f8(fake, fake, 64, k)), null, null) == want
+    # shared expert: gate/up K <= 16384 (two tiles), down I <= 32768 (one tile past 16384)
+    for K, I, want in ((2048, 16896, 0), (2048, 32768, 0), (2048, 32896, 5), (16896, 512, 5)):
+        w13 = nvfp4_weights(fake, fake, fake, 1, 2 * I, K)
+        w2 = nvfp4_weights(fake, fake, fake, 1, K, I)
+        assert L.nvfp4_moe_shared_expert(null, 0, C.byref(w13), 0, C.byref(w2), null, null, null, null, null) == want
+
+
+def test_layer_call_checks(L):
+    from gemm_nvfp4_amd._lib import nvfp4_weights
+    fake, odd, null = C.c_void_p(0x1000), C.c_void_p(0x1001), None
+    E, K, I = 8, 256, 128
+    w13 = nvfp4_weights(fake, fake, fake, E, 2 * I, K)
+    w2 = nvfp4_weights(fake, fake, fake, E, K, I)
+    need = L.nvfp4_moe_layer_workspace_bytes(4, 2, E, K, I)
+    assert need == (L.nvfp4_moe_plan_bytes(4, 2, E) + (4 * 2 * I * 2 + 255) // 256 * 256
+                    + L.nvfp4_moe_w2_workspace_bytes(4, 2, K))
+    assert L.nvfp4_moe_layer_workspace_bytes(4, 33, E, K, I) == 0
+    args = lambda ids, M, topk, E_, x, a, lay, b, tw, out, ws, wsb: L.nvfp4_moe_layer(  # noqa: E731
+        ids, M, topk, E_, x, C.byref(a), lay, C.byref(b), tw, out, ws, wsb, null)
+    assert args(null, 0, 2, E, null, w13, 0, w2, null, null, null, 0) == 0                # M = 0
+    assert args(fake, -1, 2, E, fake, w13, 0, w2, fake, fake, fake, need) == 2            # M < 0
+    assert args(fake, 4, 2, E, fake, w13, 2, w2, fake, fake, fake, need) == 2             # layout
+    assert args(fake, 4, 2, E, fake, w13, 0, nvfp4_weights(fake, fake, fake, E, K, 2 * I), fake, fake, fake,
+                need) == 2                                                                # w2 not [E][K][I]
+    assert args(fake, 4, 2, E, fake, nvfp4_weights(fake, fake, fake, E, 2 * I, 4096), 0,
+                nvfp4_weights(fake, fake, fake, E, 4096, I), fake, fake, fake, need) == 5  # K > 2048
+    assert args(fake, 4, 2, E, fake, nvfp4_weights(fake, fake, fake, E, 2 * 64, K), 0,
+                nvfp4_weights(fake, fake, fake, E, K, 64), fake, fake, fake, need) == 5    # I % 128
+    assert args(fake, 4, 2, E, fake, w13, 0, w2, null, fake, fake, need) == 1             # no weights
+    assert args(fake, 4, 2, E, fake, w13, 0, w2, fake, fake, null, need) == 1             # no workspace
+    assert args(odd, 4, 2, E, fake, w13, 0, w2, fake, fake, fake, need) == 3              # ids unaligned
+    assert args(fake, 4, 2, E, fake, w13, 0, w2, fake, fake, odd, need) == 3              # ws unaligned
+    assert args(fake, 4, 2, E, fake, w13, 0, w2, fake, fake, fake, need - 1) == 4         # ws too small

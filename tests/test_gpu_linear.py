@@ -85,3 +85,13 @@ def test_linear_m0_is_noop():
     y = G.nvfp4_linear(torch.empty((0, S.DENSE_K), dtype=torch.float16, device="cuda"), w)
     torch.cuda.synchronize()
     assert y.shape == (0, S.DENSE_N)
+
+
+@pytest.mark.parametrize("K", [16896, 32768])
+def test_linear_long_reduction(orc, K):
+    """Past K = 16384 the projection takes one weight tile per wave, so the chunk partials fit in
+    the CU's 160 KiB of LDS (with two tiles, 33 or more chunks would need more). 64 rows pair up, so
+    below that length the two-tile kernel runs; both give the same reduction order."""
+    case = S.dense_case(3, n=64, k=K, weight_set=K)
+    y = _run(case["x"], case["w"])
+    assert_rows_close(to_np64(y), orc.linear(case["x"], case["w"]), f"linear K={K}")
