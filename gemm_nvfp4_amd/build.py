@@ -52,5 +52,37 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_LIB = os.path.join(BUILD, "san", "libnvfp4moe_san.so")
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """A host-sanitizer build of the library for the host-side checks (tests/test_sanitizers.py):
+    abi.hip, which holds every argument check, compiled with AddressSanitizer and
+    UndefinedBehaviorSanitizer on its host code only (the device code is built as usual), linked
+    with the regular objects of the other sources. Loaded into a Python that preloads clang's ASan
+    runtime; it is never launched on a GPU."""
+    if not all(os.path.exists(os.path.join(BUILD, n)) for n in ("linear.o", "moe_gemm.o", "moe_plan.o",
+                                                                 "moe_prefill.o")):
+        build(verbose)
+    san = os.path.join(BUILD, "san")
+    os.makedirs(san, exist_ok=True)
+    host_san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+    obj = os.path.join(san, "abi.o")
+    cmd = [HIPCC] + CFLAGS + host_san + ["-c", os.path.join(CSRC, "abi.hip"), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for abi.hip (host sanitizers):\n{r.stderr}")
+    others = [os.path.join(BUILD, n) for n in ("linear.o", "moe_gemm.o", "moe_plan.o", "moe_prefill.o")]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", SAN_LIB, obj] + others
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build_host_sanitized(verbose=True) if "--sanitize-host" in sys.argv else build(verbose="-v" in sys.argv))

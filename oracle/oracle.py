@@ -21,10 +21,11 @@ _i64, _i32, _dbl, _vp = C.c_int64, C.c_int32, C.c_double, C.c_void_p
 
 
 def lib():
-    """Load liboracle.so, building it first if it is not there."""
+    """Load liboracle.so, building it first if it is not there. NVFP4_ORACLE_LIB names another build
+    of oracle.c to load instead (the sanitizer build of oracle/build.py, for the sanitizer test)."""
     global _LIB
     if _LIB is None:
-        path = os.path.join(HERE, "liboracle.so")
+        path = os.environ.get("NVFP4_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
         if not os.path.exists(path):
             from . import build as _b  # noqa: WPS433
             _b.build()

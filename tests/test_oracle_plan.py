@@ -24,15 +24,31 @@ def numpy_plan(ids, E, BM):
     pos = np.full(P, -1, np.int32)
     pos[sorted_pair] = np.arange(nv, dtype=np.int32)
     active = np.nonzero(counts)[0].astype(np.int32)
-    te, tr = [], []
-    for e in active:
-        for r in range(0, counts[e], BM):
-            te.append(e)
-            tr.append(r)
+    # Row tiles from counts alone: ceil(count / BM) tiles per active expert, numbered from each
+    # expert's first tile (np.repeat and a cumulative sum, not a walk over the rows).
+    per = -(-counts[active] // BM)
+    te = np.repeat(active, per).astype(np.int32)
+    first = np.repeat(np.cumsum(per) - per, per)
+    tr = (BM * (np.arange(int(per.sum())) - first)).astype(np.int32)
     n_bad = int(((flat != -1) & ~valid).sum())
     return dict(counts=counts, offsets=offsets, sorted_pair=sorted_pair, pos_of_pair=pos, active=active,
-                tile_expert=np.array(te, np.int32), tile_row0=np.array(tr, np.int32), n_valid=nv,
-                n_active=len(active), n_bad=n_bad, n_tiles=len(te))
+                tile_expert=te, tile_row0=tr, n_valid=nv, n_active=len(active), n_bad=n_bad, n_tiles=len(te))
+
+
+def check_tiles_partition(pl, E, BM):
+    """The row tiles cover every expert's bucket rows exactly once, in (expert, first row) order,
+    each with 1..BM rows, and their number is the sum of ceil(count / BM) over the experts."""
+    te, tr, counts, offs = pl["tile_expert"], pl["tile_row0"], pl["counts"], pl["offsets"]
+    assert pl["n_tiles"] == sum(-(-int(c) // BM) for c in counts)
+    cover = np.zeros(pl["n_valid"], np.int64)
+    for e, r0 in zip(te.tolist(), tr.tolist()):
+        assert 0 <= e < E and 0 <= r0 < counts[e]
+        rows = min(BM, int(counts[e]) - r0)
+        assert 1 <= rows <= BM
+        cover[offs[e] + r0: offs[e] + r0 + rows] += 1
+    assert np.all(cover == 1)
+    keys = list(zip(te.tolist(), tr.tolist()))
+    assert keys == sorted(keys) and len(set(keys)) == len(keys)
 
 
 def check_invariants(pl, ids, E):
@@ -69,6 +85,7 @@ def test_plan_brute_force_tiny(orc):
                         pl = orc.plan(ids, E, BM)
                         compare(pl, numpy_plan(ids, E, BM))
                         check_invariants(pl, ids, E)
+                        check_tiles_partition(pl, E, BM)
                         n += 1
     assert n > 10000
 
@@ -81,6 +98,7 @@ def test_plan_random_against_numpy(orc, seed):
     pl = orc.plan(ids, E, 16)
     compare(pl, numpy_plan(ids, E, 16))
     check_invariants(pl, ids, E)
+    check_tiles_partition(pl, E, 16)
 
 
 def test_plan_prefill_size(orc):
@@ -89,4 +107,5 @@ def test_plan_prefill_size(orc):
     ids = S.routing_uniform(rng, 8192, 10, 512)
     pl = orc.plan(ids, 512, 16)
     compare(pl, numpy_plan(ids, 512, 16))
+    check_tiles_partition(pl, 512, 16)
     assert pl["n_valid"] == 81920 and pl["n_bad"] == 0
