@@ -16,6 +16,8 @@ from ._lib import (  # noqa: F401
     nvfp4_linear_fp8,
     nvfp4_linear_swiglu,
     nvfp4_moe_layer,
+    NOALLOC_SCRATCH_BYTES,
+    nvfp4_moe_layer_noalloc,
     nvfp4_moe_layer_workspace_bytes,
     nvfp4_moe_plan,
     nvfp4_moe_plan_bytes,

@@ -64,6 +64,8 @@ _SIGS = {
                                             _vp]),
     "nvfp4_linear_fp8": (C.c_int, [_vp, _i32, C.POINTER(fp8_channel_weights), _vp, _vp]),
     "nvfp4_moe_layer_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "nvfp4_moe_layer_noalloc": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _i32,
+                                          C.POINTER(nvfp4_weights), _vp, _vp, _vp]),
     "nvfp4_moe_layer": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _i32,
                                   C.POINTER(nvfp4_weights), _vp, _vp, _vp, _sz, _vp]),
 }
@@ -398,6 +400,26 @@ def nvfp4_moe_layer(topk_ids: torch.Tensor, E: int, x: torch.Tensor, w13: NVFP4T
         _dev(topk_ids, "topk_ids", torch.int32), M, topk, E, _dev(x, "x", torch.float16), C.byref(d13), layout,
         C.byref(d2), _dev(topk_weights, "topk_weights", torch.float32), _dev(out, "out", torch.float16),
         _dev(ws, "ws", torch.uint8), ws.numel(), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20  # NVFP4_NOALLOC_SCRATCH_BYTES of nvfp4moe.h
+
+
+def nvfp4_moe_layer_noalloc(topk_ids: torch.Tensor, E: int, x: torch.Tensor, w13: NVFP4Tensor, w2: NVFP4Tensor,
+                            topk_weights: torch.Tensor, out: torch.Tensor, layout: int = 0, stream=None) -> torch.Tensor:
+    """nvfp4_moe_layer with the library's static device scratch array as its workspace: the call
+    allocates nothing (out is the caller's). Calls that overlap on one GPU race."""
+    M, topk = topk_ids.shape
+    K = w13.k
+    _shape(x, "x", (M, K))
+    _shape(topk_weights, "topk_weights", (M, topk))
+    _shape(out, "out", (M, K))
+    d13, d2 = w13.desc(), w2.desc()
+    _check("nvfp4_moe_layer_noalloc", lib().nvfp4_moe_layer_noalloc(
+        _dev(topk_ids, "topk_ids", torch.int32), M, topk, E, _dev(x, "x", torch.float16), C.byref(d13), layout,
+        C.byref(d2), _dev(topk_weights, "topk_weights", torch.float32), _dev(out, "out", torch.float16),
+        _stream(stream)))
     return out
 
 

@@ -4,6 +4,9 @@
 // "Guarded production engine result").
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "internal.hpp"
 
 #define NVFP4_API extern "C" __attribute__((visibility("default")))
@@ -292,6 +295,60 @@ NVFP4_API int nvfp4_moe_layer(const int32_t *topk_ids, int32_t M, int32_t topk, 
     if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
     if (ws_bytes < layer_parts(M, topk, E, K, I).total) return NVFP4_ERR_WORKSPACE;
     return enqueue_layer(topk_ids, M, topk, E, x, *w13, layout, *w2, topk_weights, out, static_cast<uint8_t *>(ws),
+                         static_cast<hipStream_t>(stream));
+}
+
+// ---- the layer without allocation (nvfp4_moe_layer_noalloc) ------------------------------------
+// For callers that cannot allocate: the layer workspace is this file-scope device array. Each GPU
+// holds its own copy at its own address. In host code `scratch` names only a host-side stand-in,
+// so it is never passed to a kernel or a copy: the device address comes from hipGetSymbolAddress,
+// taken once per device (with that device current) on the first call there, and kept.
+static __device__ __align__(256) uint8_t scratch[NVFP4_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<uint8_t *> scratch_dev[MAX_DEVICES];
+std::mutex scratch_mu;
+
+// Device address of the current device's scratch array, or nullptr (status in *st) if the runtime
+// cannot give it.
+uint8_t *scratch_ptr(int *st)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+        *st = NVFP4_ERR_LAUNCH;
+        return nullptr;
+    }
+    uint8_t *p = scratch_dev[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    p = scratch_dev[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void *addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) {
+            *st = NVFP4_ERR_LAUNCH;
+            return nullptr;
+        }
+        p = static_cast<uint8_t *>(addr);
+        scratch_dev[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+}  // namespace
+
+NVFP4_API int nvfp4_moe_layer_noalloc(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E, const uint16_t *x,
+                                      const nvfp4_weights *w13, int32_t layout, const nvfp4_weights *w2,
+                                      const float *topk_weights, uint16_t *out, void *stream)
+{
+    int32_t K = 0, I = 0;
+    int st = check_layer(topk_ids, M, topk, E, x, w13, layout, w2, topk_weights, out, &K, &I);
+    if (st != NVFP4_OK || M == 0) return st;
+    if (layer_parts(M, topk, E, K, I).total > NVFP4_NOALLOC_SCRATCH_BYTES) return NVFP4_ERR_WORKSPACE;
+    uint8_t *ws = scratch_ptr(&st);
+    if (!ws) return st;
+    return enqueue_layer(topk_ids, M, topk, E, x, *w13, layout, *w2, topk_weights, out, ws,
                          static_cast<hipStream_t>(stream));
 }
 

@@ -28,8 +28,9 @@
  *     on it: no host synchronisation, no device allocation, no device-to-host copy. Every call can
  *     therefore be captured in a HIP graph.
  *   - The caller allocates and owns every buffer (plan, workspace, outputs). The library keeps no
- *     pointer after a call returns and holds no mutable global state, so calls from several host
- *     threads on different streams are safe. Two calls that write the same buffer must be ordered
+ *     pointer after a call returns and holds no mutable global state (except the static device
+ *     array of nvfp4_moe_layer_noalloc), so calls from several host threads on different streams
+ *     are safe. Two calls that write the same buffer must be ordered
  *     by the caller (for example, the same stream).
  *   - Errors fail closed: a nonzero status is returned, nothing is enqueued, and no output is
  *     touched. Status codes are NVFP4_* below; nvfp4_status_str() names them. Every argument and
@@ -214,6 +215,25 @@ size_t nvfp4_moe_layer_workspace_bytes(int32_t M, int32_t topk, int32_t E, int32
 int nvfp4_moe_layer(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E, const uint16_t *x,
                     const nvfp4_weights *w13, int32_t layout, const nvfp4_weights *w2,
                     const float *topk_weights, uint16_t *out, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * nvfp4_moe_layer without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The call
+ * itself allocates nothing: the plan, h and the W2 workspace live in a static device array of
+ * NVFP4_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the process
+ * ends. Arguments, results and requirements are those of nvfp4_moe_layer; the output is bitwise
+ * the same. A shape whose nvfp4_moe_layer_workspace_bytes(M, topk, E, K, I) exceeds the array
+ * returns NVFP4_ERR_WORKSPACE with nothing enqueued (about 100 tokens at 512 experts, top-10,
+ * K = 2048, I = 512). No part of the array needs to start at zero, and every call rewrites what it
+ * reads.
+ * Every call on one GPU shares that GPU's array: two calls that can overlap on one GPU (different
+ * streams, or different host threads without ordering) race and give undefined results; calls on
+ * one stream are ordered and safe.
+ * --------------------------------------------------------------------------------------------- */
+#define NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int nvfp4_moe_layer_noalloc(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E, const uint16_t *x,
+                            const nvfp4_weights *w13, int32_t layout, const nvfp4_weights *w2,
+                            const float *topk_weights, uint16_t *out, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Shared expert and shared gate (the "shared gate" among the fused MoE parts, no-MTP page, "Scope

@@ -41,7 +41,8 @@ def test_header_declares_the_expected_entry_points():
         "nvfp4_moe_w13_swiglu", "nvfp4_moe_w2_workspace_bytes", "nvfp4_moe_w2_reduce", "nvfp4_linear",
         "nvfp4_linear_swiglu", "nvfp4_linear_fp8", "nvfp4_moe_shared_expert", "nvfp4_moe_w2_reduce_shared",
         "nvfp4_moe_w13_swiglu_with_shared", "nvfp4_moe_w2_reduce_with_shared", "nvfp4_moe_plan_w13_swiglu",
-        "nvfp4_moe_plan_w13_swiglu_with_shared", "nvfp4_moe_layer_workspace_bytes", "nvfp4_moe_layer"])
+        "nvfp4_moe_plan_w13_swiglu_with_shared", "nvfp4_moe_layer_workspace_bytes", "nvfp4_moe_layer",
+        "nvfp4_moe_layer_noalloc"])
 
 
 def test_library_exports_every_declared_function():
