@@ -1,8 +1,8 @@
 // moe_gemm.hip -- grouped expert GEMMs of the MoE layer, decode (streaming) regime.
-//   W13 with fused SwiGLU ("expert-grouped multi-row W13/SiLU with intra-CTA Split-K"), then W2
-//   with the top-k-weighted reduction ("grouped W2 reusing the same integer plan", "W2/reduction
-//   fusion"), from the "[Kernel][SM70] Improve Qwen3.8 no-MTP concurrency" page, "Scope and
-//   related PRs".
+//   W13 with fused SwiGLU (an expert-grouped W13 over several rows with SiLU in its epilogue and
+//   the reduction axis split inside a block), then W2 with the top-k-weighted reduction fused in
+//   (W2 reads the plan W13 used), as listed on the "[Kernel][SM70] Improve Qwen3.8 no-MTP
+//   concurrency" page, "Scope and related PRs".
 //
 // At small M the layer reads every active expert's packed weights once and does little math on
 // them. It is bound by HBM bandwidth, so the design goal is many bytes in flight per CU. On

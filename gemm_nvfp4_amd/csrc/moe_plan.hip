@@ -1,7 +1,7 @@
 // moe_plan.hip -- routing plan: top-k id histogram, prefix-sum expert bucketing and a stable
-// scatter into bucket order. W13 and W2 both reuse this integer plan, so planning happens once
-// ("grouped W2 reusing the same integer plan ... avoids repeated planning", "[Kernel][SM70] Improve
-// Qwen3.8 no-MTP concurrency", "Scope and related PRs").
+// scatter into bucket order. W13 and W2 both reuse this integer plan, so planning happens once per
+// layer (the grouped W2 takes W13's plan instead of planning again: "[Kernel][SM70] Improve Qwen3.8
+// no-MTP concurrency", "Scope and related PRs").
 //
 // The plan is a stable counting sort of the valid (token, slot) pairs by expert; ties keep
 // ascending pair index p = t*topk + k. That makes it unique, and every path below produces it

@@ -3,9 +3,9 @@
 // the writers of the plan's documented arrays (layout: PlanLayout in internal.hpp).
 //
 // The plan is a stable counting sort of the valid (token, slot) pairs by expert, ties by
-// ascending pair index p = t*topk + k ("grouped W2 reusing the same integer plan", "[Kernel][SM70]
-// Improve Qwen3.8 no-MTP concurrency", "Scope and related PRs"). Every writer below produces the
-// same words, so every path gives the same plan bit for bit.
+// ascending pair index p = t*topk + k: the one integer plan that W13 and the grouped W2 share
+// ("[Kernel][SM70] Improve Qwen3.8 no-MTP concurrency", "Scope and related PRs"). Every writer
+// below produces the same words, so every path gives the same plan bit for bit.
 #pragma once
 
 #include "internal.hpp"

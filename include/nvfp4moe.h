@@ -87,7 +87,8 @@ int nvfp4_abi_version(void);
 const char *nvfp4_status_str(int status);
 
 /* ---------------------------------------------------------------------------------------------
- * Routing plan ("grouped W2 reusing the same integer plan", no-MTP page, "Scope and related PRs").
+ * Routing plan (the one integer plan that W13 and the grouped W2 share, no-MTP page, "Scope and
+ * related PRs").
  *
  * Input topk_ids int32 [M][topk]. Pair p = t*topk + k. An id in [0, E) routes the pair to that
  * expert. -1 means "no expert", and the pair is skipped. Any other id is also skipped and is
@@ -137,7 +138,7 @@ int nvfp4_moe_route(const float *logits, int32_t M, int32_t E, int32_t topk, int
                     float *topk_weights, void *plan, size_t plan_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
- * Grouped W13 with fused SwiGLU (the "expert-grouped multi-row W13/SiLU", no-MTP page, "Scope and
+ * Grouped W13 with fused SwiGLU (the expert-grouped W13 with SiLU fused, no-MTP page, "Scope and
  * related PRs").
  *   x    fp16 [M][K]          activations (K = w13->k)
  *   w13  groups = E, rows = 2I, k = K
@@ -159,8 +160,7 @@ int nvfp4_moe_w13_swiglu(const void *plan, int32_t M, int32_t topk, int32_t E,
 /* ---------------------------------------------------------------------------------------------
  * Routing plan and grouped W13 + SwiGLU in one call: the results of nvfp4_moe_plan(topk_ids, ...,
  * plan) followed by nvfp4_moe_w13_swiglu(plan, ...), bit for bit (the plan is built once and both
- * W13 and W2 read it, as on the no-MTP page, "Scope and related PRs": "grouped W2 reusing the same
- * integer plan ... avoids repeated planning").
+ * W13 and W2 read it, so the layer plans once: no-MTP page, "Scope and related PRs").
  *   topk_ids, plan, plan_bytes   as for nvfp4_moe_plan (plan is written: W2 takes it afterwards)
  *   x, w13, layout, h            as for nvfp4_moe_w13_swiglu
  * With M*topk <= 256, E <= 1024 and the decode (non-prefill) regime, it is one launch: every W13
@@ -174,7 +174,7 @@ int nvfp4_moe_plan_w13_swiglu(const int32_t *topk_ids, int32_t M, int32_t topk, 
                               const nvfp4_weights *w13, int32_t layout, uint16_t *h, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
- * Grouped W2 with the top-k-weighted reduction ("W2/reduction fusion", no-MTP page, "Scope and
+ * Grouped W2 with the top-k-weighted reduction fused in (no-MTP page, "Scope and
  * related PRs").
  *   h             fp16 [M*topk][I]  W13 output in bucket order
  *   w2            groups = E, rows = K, k = I
