@@ -10,15 +10,20 @@ Infinity Cache cannot serve repeated weights (the rotating-weights lesson of the
 Improve Qwen3.8 no-MTP concurrency" page, "Test Result").
 
 value = weight HBM GB/s: the bytes of the distinct active experts' weights (W13 1,179,648 B plus
-W2 589,824 B per expert) summed over the timed steps, divided by the timed wall time. The JSON line
-also carries:
-  - us_per_layer;
-  - the M = 1..16 sweep;
+W2 589,824 B per expert) summed over the steps of one graph, divided by the median time of 20 (or
+--trials) timed replays of that graph (p10 / median / p90 in `trials`). The JSON line also carries:
+  - us_per_layer and the M = 1..16 sweep (uniform routing);
+  - the routing-stress rows (Zipf, all-singleton, shared ids, repeats + invalid) at M = 1..16;
+  - the tiny layer's latency;
+  - a measured copy-kernel ceiling (torch's copy of the same byte counts) and each GB/s figure's
+    fraction of it beside its fraction of the 8 TB/s peak;
   - the 8192-token prefill in TFLOP/s;
-  - the dense 4352x5120 projection;
-  - the roofline of the dominant kernel (grouped W13 + SwiGLU), timed with HIP events on its
-    launch stream;
+  - the dense 4352x5120 projection, its channel-FP8 form, the dense gated MLP, the router;
+  - the roofline of the dominant kernel (grouped W13 + SwiGLU with the plan built in the
+    launch), timed with HIP events on its launch stream;
   - the fp64 CPU oracle timed on a bounded sample (cpu_baseline).
+--counters decode|prefill runs only a calibration copy and a few eager layer calls, for
+rocprofv3 --pmc counter runs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -64,9 +69,13 @@ def parse():
     p.add_argument("--no-mlp", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
-    p.add_argument("--traffic", action="store_true",
-                   help="counter-collection mode: a 256 MiB device copy (calibration), then 12 eager launches "
-                        "of the headline W13 kernel; prints nothing else")
+    p.add_argument("--trials", type=int, default=20, help="timed replays of each graph (at least 20 for the headline)")
+    p.add_argument("--no-stress", action="store_true")
+    p.add_argument("--counters", choices=("decode", "prefill"), default=None,
+                   help="counter-collection mode for rocprofv3 --pmc runs: a 256 MiB device copy (the calibration "
+                        "kernel), then eager layer calls (decode: 12 calls of the 16-token layer on distinct weight "
+                        "sets; prefill: 2 calls of the 8192-token layer); prints only what it ran")
+    p.add_argument("--traffic", action="store_true", help="same as --counters decode")
     return p.parse_args()
 
 
@@ -90,10 +99,10 @@ class Routes:
             self.valid.append(int(((ids >= 0) & (ids < E)).sum()))
 
 
-def time_graph(build_fn, steps, warmup_fn=None, more=None, trials=0):
-    """Capture build_fn() (which enqueues `steps` steps) in one graph, replay once untimed, then time
-    one replay with HIP events on the replay stream. Returns elapsed ms. With trials > 0 the graph is
-    replayed that many more times, each timed alone, and the figures are appended to `more`."""
+def time_graph(build_fn, steps, warmup_fn=None, trials=20):
+    """Capture build_fn() (which enqueues `steps` steps) in one graph, replay it once untimed, then
+    time `trials` replays, each alone: HIP events on the replay stream around the replay, with a
+    synchronize before and after. Returns the per-replay milliseconds."""
     import torch
     if warmup_fn is not None:
         warmup_fn()
@@ -104,19 +113,27 @@ def time_graph(build_fn, steps, warmup_fn=None, more=None, trials=0):
     g.replay()
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    g.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1)
-    for _ in range(trials):
+    ms = []
+    for _ in range(max(1, trials)):
+        torch.cuda.synchronize()
         t0.record()
         g.replay()
         t1.record()
         torch.cuda.synchronize()
-        more.append(t0.elapsed_time(t1))
+        ms.append(t0.elapsed_time(t1))
     del g
     return ms
+
+
+def med(ms):
+    return float(np.median(ms))
+
+
+def spread(ms, steps):
+    """p10 / median / p90 of per-replay times, in µs per step."""
+    q = np.percentile(np.asarray(ms) * 1e3 / steps, [10, 50, 90])
+    return {"n": len(ms), "us_p10": round(float(q[0]), 3), "us_median": round(float(q[1]), 3),
+            "us_p90": round(float(q[2]), 3)}
 
 
 def weight_sets(n, seed0=1000):
@@ -127,9 +144,9 @@ def weight_sets(n, seed0=1000):
     return w13, w2
 
 
-def moe_layer_timing(M, steps, warmup, W13, W2, routes, trials=0):
-    """µs per MoE layer and weight GB/s over `steps` graph-captured layer calls (the first timed
-    replay). With trials > 0, also the median, p10 and p90 of that many further replays."""
+def moe_layer_timing(M, steps, warmup, W13, W2, routes, trials=20):
+    """µs per MoE layer and weight GB/s over graphs of `steps` layer calls: the median of `trials`
+    timed replays (p10 / p90 beside it)."""
     import gemm_nvfp4_amd as G
     R, P = len(W13), len(routes.x)
     layer = G.MoELayer(M, TOPK, W13[0], W2[0])
@@ -142,20 +159,74 @@ def moe_layer_timing(M, steps, warmup, W13, W2, routes, trials=0):
         for i in range(warmup):
             step(i)
 
-    more = []
-    ms = time_graph(lambda: [step(i) for i in range(steps)], steps, warm, more=more, trials=trials)
+    ms_all = time_graph(lambda: [step(i) for i in range(steps)], steps, warm, trials=trials)
+    ms = med(ms_all)
     wbytes = sum(routes.active[i % P] * EXPERT_BYTES for i in range(steps))
     pairs = sum(routes.valid[i % P] for i in range(steps))
     us = ms * 1e3 / steps
-    r = {"M": M, "us_per_layer": round(us, 3), "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1),
-         "hbm_frac": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-         "tflops": round(pairs * FLOP_PER_PAIR / (ms * 1e-3) / 1e12, 2),
-         "mean_active_experts": round(float(np.mean(routes.active)), 2), "steps": steps}
-    if more:
-        q = np.percentile(np.array(more) * 1e3 / steps, [10, 50, 90])
-        r["trials"] = {"n": len(more), "us_per_layer_p10": round(float(q[0]), 3),
-                       "us_per_layer_median": round(float(q[1]), 3), "us_per_layer_p90": round(float(q[2]), 3)}
-    return r
+    return {"M": M, "us_per_layer": round(us, 3), "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tflops": round(pairs * FLOP_PER_PAIR / (ms * 1e-3) / 1e12, 2),
+            "mean_active_experts": round(float(np.mean(routes.active)), 2), "steps": steps,
+            "trials": spread(ms_all, steps)}
+
+
+def stress_timing(steps, warmup, W13, W2, patterns):
+    """The routing-stress workload (512 experts, top-10, K=2048, I=512) at M = 1, 2, 4, 8, 16 for each
+    routing: Zipf(1.2), all-singleton, every token on the same 10 experts, repeated ids with -1
+    slots. Weight GB/s counts each layer's distinct active experts."""
+    res = []
+    for r, routing in enumerate(("zipf", "singleton", "shared", "repeat_invalid")):
+        for M in (1, 2, 4, 8, 16):
+            routes = Routes(M, patterns, 6000 + 100 * r + M, routing=routing)
+            t = moe_layer_timing(M, steps, warmup, W13, W2, routes)
+            res.append({"routing": routing, "M": M, "us_per_layer": t["us_per_layer"],
+                        "weight_GBps": t["weight_GBps"], "hbm_frac": t["hbm_frac"],
+                        "mean_active_experts": t["mean_active_experts"], "us_p90": t["trials"]["us_p90"]})
+    return res
+
+
+def tiny_timing(steps, copies=64):
+    """The tiny layer (1 token, 8 experts, top-2, K=256, I=128): µs per layer call in a graph that
+    rotates `copies` weight sets. Its 442 KB of weights make it a latency figure, not a roofline one."""
+    import gemm_nvfp4_amd as G
+    from synth import inputs as S
+    sh = S.TINY
+    w13 = [G.NVFP4Tensor(*S.device_nvfp4_weights(11000 + c, sh.e, 2 * sh.i, sh.k)) for c in range(copies)]
+    w2 = [G.NVFP4Tensor(*S.device_nvfp4_weights(11500 + c, sh.e, sh.k, sh.i)) for c in range(copies)]
+    import torch
+    xs, ids, tws = [], [], []
+    for p in range(16):
+        rng = S.rng_for(S.WORKLOAD_IDS["tiny"], 0, 500 + p)
+        xs.append(torch.from_numpy(S.activations(rng, 1, sh.k)).cuda())
+        ids.append(torch.from_numpy(np.ascontiguousarray(S.routing_uniform(rng, 1, sh.topk, sh.e), np.int32)).cuda())
+        tws.append(torch.from_numpy(S.softmax_weights(rng, 1, sh.topk)).cuda())
+    layer = G.MoELayer(1, sh.topk, w13[0], w2[0])
+
+    def step(i):
+        layer(xs[i % 16], ids[i % 16], tws[i % 16], w13[i % copies], w2[i % copies])
+
+    ms = time_graph(lambda: [step(i) for i in range(steps)], steps, lambda: [step(i) for i in range(4)])
+    return {"workload": "1 token, 8 experts, top-2, K=256, I=128", "us_per_layer": round(med(ms) * 1e3 / steps, 3),
+            "trials": spread(ms, steps)}
+
+
+def copy_ceiling(nbytes_list=(12533760, 245194752), sets=8, launches=64):
+    """A plain device copy (torch's copy kernel) of the same byte counts as the dense projection's
+    weights and the 16-token layer's weights, rotating `sets` source/destination pairs. GB/s counts
+    the bytes read plus the bytes written, the HBM traffic of the copy."""
+    import torch
+    res = []
+    for nb in nbytes_list:
+        src = [torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1) for _ in range(sets)]
+        dst = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(sets)]
+        n = launches if nb < (64 << 20) else 16
+        ms = time_graph(lambda: [dst[i % sets].copy_(src[i % sets]) for i in range(n)], n)
+        us = med(ms) * 1e3 / n
+        res.append({"bytes": nb, "copy_us": round(us, 3), "copy_GBps": round(2 * nb / (us * 1e-6) / 1e9, 1)})
+        del src, dst
+        torch.cuda.empty_cache()
+    return res
 
 
 def eager_latency(M, W13, W2, routes, calls=20):
@@ -195,7 +266,7 @@ def w13_kernel_timing(M, launches, W13, routes):
             p = i % P
             G.nvfp4_moe_plan_w13_swiglu(routes.ids[p], E, routes.x[p], W13[i % R], 0, plan=plan, h=h)
 
-    ms = time_graph(build, launches)
+    ms = med(time_graph(build, launches))
     algo = [routes.active[p] * W13_EXPERT_BYTES + M * K * 2 + routes.valid[p] * I * 2 for p in range(P)]
     bytes_per_launch = float(np.mean([algo[i % P] for i in range(launches)]))
     us = ms * 1e3 / launches
@@ -203,6 +274,7 @@ def w13_kernel_timing(M, launches, W13, routes):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w13_swiglu_stream_decode16_traffic.txt")
+ROOFLINE_KERNEL = "w13_swiglu_stream_kernel<4, 1, false, true> (routing plan built in the launch)"
 KERNEL_SOURCES = ("gemm_nvfp4_amd/csrc/moe_gemm.hip", "gemm_nvfp4_amd/csrc/nvfp4_device.hpp",
                   "gemm_nvfp4_amd/csrc/internal.hpp", "gemm_nvfp4_amd/csrc/plan_device.hpp")
 
@@ -228,29 +300,37 @@ def measured_traffic():
     return float(kv["traffic_bytes_per_launch"])
 
 
-def traffic_mode(W13):
-    """Eager launches for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs: a device copy of known size
-    first (the calibration kernel), then the headline W13 kernel on 12 weight sets."""
+def counters_mode(kind, W13, W2):
+    """Eager launches for rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, SQ_*): a device copy of known
+    size first (the calibration kernel), then the layer calls of one workload."""
     import torch
     import gemm_nvfp4_amd as G
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
-    routes = Routes(16, 12, 1000)
-    plan = torch.empty(max(G.nvfp4_moe_plan_bytes(16, TOPK, E), 4) // 4, dtype=torch.int32, device="cuda")
-    h = torch.empty((16 * TOPK, I), dtype=torch.float16, device="cuda")
-    for i in range(12):
-        G.nvfp4_moe_plan_w13_swiglu(routes.ids[i], E, routes.x[i], W13[i % len(W13)], 0, plan=plan, h=h)
     torch.cuda.synchronize()
-    algo = [routes.active[p] * W13_EXPERT_BYTES + 16 * K * 2 + routes.valid[p] * I * 2 for p in range(12)]
-    log(f"traffic mode done: copy 268435456 B x3; W13 x12, algorithmic bytes/launch {np.mean(algo):.0f}")
+    if kind == "decode":
+        M, calls = 16, 12
+        routes = Routes(M, calls, 1000)
+    else:
+        M, calls = 8192, 2
+        routes = Routes(M, calls, 5000)
+    layer = G.MoELayer(M, TOPK, W13[0], W2[0])
+    for i in range(calls):
+        layer(routes.x[i], routes.ids[i], routes.tw[i], W13[i % len(W13)], W2[i % len(W2)])
+    torch.cuda.synchronize()
+    w13 = [routes.active[p] * W13_EXPERT_BYTES + M * K * 2 + routes.valid[p] * I * 2 for p in range(calls)]
+    w2 = [routes.active[p] * W2_EXPERT_BYTES + routes.valid[p] * I * 2 + routes.valid[p] * K * 4 for p in range(calls)]
+    log(f"counters mode ({kind}): copy 268435456 B x3; {calls} layer calls at M={M}; algorithmic bytes per "
+        f"launch: W13 {np.mean(w13):.0f}, W2 (weights + h + FP32 results) {np.mean(w2):.0f}; "
+        f"FLOP per layer {np.mean(routes.valid) * FLOP_PER_PAIR:.4g}")
 
 
 def launch_floor(launches=480):
     import torch
     t = torch.zeros(1, device="cuda")
-    ms = time_graph(lambda: [t.add_(1.0) for _ in range(launches)], launches)
+    ms = med(time_graph(lambda: [t.add_(1.0) for _ in range(launches)], launches))
     return ms * 1e3 / launches
 
 
@@ -264,12 +344,15 @@ def prefill_timing(W13, W2, steps=4):
     def step(i):
         layer(routes.x[i % 2], routes.ids[i % 2], routes.tw[i % 2], W13[i % R], W2[i % R])
 
-    ms = time_graph(lambda: [step(i) for i in range(steps)], steps, lambda: step(0))
+    ms_all = time_graph(lambda: [step(i) for i in range(steps)], steps, lambda: step(0), trials=10)
+    ms = med(ms_all)
     pairs = sum(routes.valid[i % 2] for i in range(steps))
     return {"M": M, "ms_per_layer": round(ms / steps, 3),
             "tflops": round(pairs * FLOP_PER_PAIR / (ms * 1e-3) / 1e12, 2),
             "mfma_frac": round(pairs * FLOP_PER_PAIR / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-            "gflop_per_layer": round(routes.valid[0] * FLOP_PER_PAIR / 1e9, 2)}
+            "gflop_per_layer": round(routes.valid[0] * FLOP_PER_PAIR / 1e9, 2),
+            "trials": {k.replace("us_", "ms_"): round(v / 1e3, 4) if k != "n" else v
+                       for k, v in spread(ms_all, steps).items()}}
 
 
 def dense_timing(copies=64, launches=256):
@@ -283,7 +366,7 @@ def dense_timing(copies=64, launches=256):
     for M in S.DENSE_MS:
         x = torch.from_numpy(S.activations(S.rng_for(1, 0, 1000 + M), M, Kd)).cuda()
         y = torch.empty((M, N), dtype=torch.float16, device="cuda")
-        ms = time_graph(lambda: [G.nvfp4_linear(x, ws[i % copies], y=y) for i in range(launches)], launches)
+        ms = med(time_graph(lambda: [G.nvfp4_linear(x, ws[i % copies], y=y) for i in range(launches)], launches))
         us = ms * 1e3 / launches
         res.append({"M": M, "us": round(us, 3), "weight_GBps": round(wbytes / (us * 1e-6) / 1e9, 1),
                     "hbm_frac": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
@@ -337,7 +420,8 @@ def shared_layer_timing(steps, W13, W2, routes, i_shared=512):
     wbytes = sum(routes.active[i % P] * EXPERT_BYTES + 3 * i_shared * K * 9 // 16 for i in range(steps))
     res = {"M": M, "shared_intermediate": i_shared}
     for name, ov in (("serial", False), ("overlapped", True), ("fused", None)):
-        ms = time_graph(lambda: [step(i, ov) for i in range(steps)], steps, lambda: [step(i, ov) for i in range(8)])
+        ms = med(time_graph(lambda: [step(i, ov) for i in range(steps)], steps,
+                            lambda: [step(i, ov) for i in range(8)]))
         res[f"us_per_layer_{name}"] = round(ms * 1e3 / steps, 3)
         res[f"weight_GBps_{name}"] = round(wbytes / (ms * 1e-3) / 1e9, 1)
     return res
@@ -359,7 +443,8 @@ def fp8_timing(copies=40, launches=192):
     for M in (1, 16, 32):
         x = torch.from_numpy(S.activations(S.rng_for(1, 0, 3000 + M), M, Kd)).cuda()
         y = torch.empty((M, N), dtype=torch.float16, device="cuda")
-        ms = time_graph(lambda: [G.nvfp4_linear_fp8(x, ws[i % copies], y=y) for i in range(launches)], launches)
+        ms = med(time_graph(lambda: [G.nvfp4_linear_fp8(x, ws[i % copies], y=y) for i in range(launches)],
+                            launches))
         us = ms * 1e3 / launches
         res.append({"M": M, "us": round(us, 3), "weight_GBps": round(wbytes / (us * 1e-6) / 1e9, 1),
                     "hbm_frac": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
@@ -382,8 +467,9 @@ def mlp_timing(copies=48, launches=192):
         x = torch.from_numpy(S.activations(S.rng_for(1, 0, 2000 + M), M, Kd)).cuda()
         h = torch.empty((M, Id), dtype=torch.float16, device="cuda")
         y = torch.empty((M, Kd), dtype=torch.float16, device="cuda")
-        g_ms = time_graph(lambda: [G.nvfp4_linear_swiglu(x, w13[i % copies], h=h) for i in range(launches)], launches)
-        d_ms = time_graph(lambda: [G.nvfp4_linear(h, w2[i % copies], y=y) for i in range(launches)], launches)
+        g_ms = med(time_graph(lambda: [G.nvfp4_linear_swiglu(x, w13[i % copies], h=h) for i in range(launches)],
+                              launches))
+        d_ms = med(time_graph(lambda: [G.nvfp4_linear(h, w2[i % copies], y=y) for i in range(launches)], launches))
         g_us, d_us = g_ms * 1e3 / launches, d_ms * 1e3 / launches
         res.append({"M": M, "gate_up_swiglu_us": round(g_us, 3), "down_us": round(d_us, 3),
                     "weight_GBps": round((b13 + b2) / ((g_us + d_us) * 1e-6) / 1e9, 1)})
@@ -404,10 +490,10 @@ def route_timing(launches=256, patterns=8):
         w = torch.empty((M, TOPK), dtype=torch.float32, device="cuda")
         plan = torch.empty(G.nvfp4_moe_plan_bytes(M, TOPK, E) // 4, dtype=torch.int32, device="cuda")
         n = launches if M <= 16 else 16
-        route_ms = time_graph(lambda: [G.nvfp4_moe_route(xs[i % patterns], TOPK, ids=ids, weights=w, plan=plan)
-                                       for i in range(n)], n)
+        route_ms = med(time_graph(lambda: [G.nvfp4_moe_route(xs[i % patterns], TOPK, ids=ids, weights=w, plan=plan)
+                                           for i in range(n)], n))
         id_sets = [G.nvfp4_moe_route(x, TOPK)[0] for x in xs]
-        plan_ms = time_graph(lambda: [G.nvfp4_moe_plan(id_sets[i % patterns], E, plan=plan) for i in range(n)], n)
+        plan_ms = med(time_graph(lambda: [G.nvfp4_moe_plan(id_sets[i % patterns], E, plan=plan) for i in range(n)], n))
         res.append({"M": M, "route_plan_us": round(route_ms * 1e3 / n, 3), "plan_us": round(plan_ms * 1e3 / n, 3)})
     return res
 
@@ -473,12 +559,12 @@ def main():
     W13, W2 = weight_sets(args.weight_sets)
     torch.cuda.synchronize()
     log(f"weight sets: {args.weight_sets} x {E * EXPERT_BYTES / 2**20:.0f} MiB")
-    if args.traffic:
-        traffic_mode(W13)
+    if args.counters or args.traffic:
+        counters_mode(args.counters or "decode", W13, W2)
         return
 
     routes16 = Routes(16, args.patterns, 1000)
-    head = moe_layer_timing(16, args.steps, args.warmup, W13, W2, routes16, trials=20)
+    head = moe_layer_timing(16, args.steps, args.warmup, W13, W2, routes16, trials=max(20, args.trials))
     log(f"headline M=16: {head}")
     eager = {"M1_us": eager_latency(1, W13, W2, Routes(1, 8, 4000)), "M16_us": eager_latency(16, W13, W2, routes16)}
     log(f"eager single-call latency: {eager}")
@@ -487,6 +573,9 @@ def main():
     log(f"w13 kernel: {k_us:.3f} us/launch, {k_bytes / 1e6:.2f} MB/launch -> {achieved:.1f} GB/s")
     floor = launch_floor()
     log(f"graph launch floor: {floor:.3f} us")
+    copies = copy_ceiling()
+    log(f"copy ceiling: {copies}")
+    copy_dense, copy_layer = copies[0]["copy_GBps"], copies[1]["copy_GBps"]
 
     shared = shared_layer_timing(args.steps, W13, W2, routes16)
     log(f"layer with shared expert: {shared}")
@@ -495,8 +584,15 @@ def main():
     if not args.no_sweep:
         for M in (1, 2, 4, 8, 16):
             r = moe_layer_timing(M, args.steps, args.warmup, W13, W2, Routes(M, args.patterns, 3000 + 97 * M))
+            r["copy_frac"] = round(r["weight_GBps"] / copy_layer, 4)
             log(f"sweep: {r}")
             sweep.append(r)
+    stress = None
+    if not args.no_stress:
+        stress = stress_timing(args.steps, args.warmup, W13, W2, args.patterns)
+        log(f"stress: {stress}")
+    tiny = tiny_timing(args.steps)
+    log(f"tiny layer: {tiny}")
     prefill = None
     if not args.no_prefill:
         prefill = prefill_timing(W13, W2)
@@ -504,6 +600,8 @@ def main():
     dense = None
     if not args.no_dense:
         dense = dense_timing()
+        for r in dense:
+            r["copy_frac"] = round(r["weight_GBps"] / copy_dense, 4)
         log(f"dense: {dense}")
     fp8 = None
     if not args.no_dense:
@@ -530,13 +628,17 @@ def main():
                                "512 experts, top-10 uniform, K=2048, I=512",
                    "tokens": 16, "experts": E, "topk": TOPK, "hidden": K, "intermediate": I,
                    "weight_sets": args.weight_sets, "route_patterns": args.patterns},
+        "value_is": "median of the timed replays of one graph of `steps` layer calls",
         "us_per_layer": head["us_per_layer"], "hbm_frac": head["hbm_frac"],
+        "copy_frac": round(head["weight_GBps"] / copy_layer, 4), "trials": head["trials"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "w13_swiglu_stream_kernel<4, 1, false, true> (routing plan built in the launch)", "us_per_launch": round(k_us, 3),
-                     "algorithmic_bytes_per_launch": round(k_bytes)},
-        "launch_floor_us": round(floor, 3), "eager_layer_latency": eager, "trials": head.get("trials"),
-        "sweep": sweep, "prefill": prefill, "dense": dense, "dense_fp8": fp8, "mlp": mlp, "with_shared_expert": shared, "route": route, "cpu_baseline": cpu,
+                     "kernel": ROOFLINE_KERNEL, "us_per_launch": round(k_us, 3),
+                     "algorithmic_bytes_per_launch": round(k_bytes),
+                     "copy_frac": round(achieved / copy_layer, 4)},
+        "copy_ceiling": copies, "launch_floor_us": round(floor, 3), "eager_layer_latency": eager,
+        "sweep": sweep, "stress": stress, "tiny": tiny, "prefill": prefill, "dense": dense, "dense_fp8": fp8,
+        "mlp": mlp, "with_shared_expert": shared, "route": route, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

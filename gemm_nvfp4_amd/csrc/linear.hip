@@ -21,10 +21,11 @@ namespace nvfp4 {
 namespace {
 
 constexpr int LDS_ROW = 20;
-// Waves per block (chunks beyond are taken in turn): ten for the plain form; eight for the gated
-// form, whose two weight tiles per wave need more than the 168 registers ten waves allow.
-template <int NW>
-constexpr int max_waves() { return NW == 1 ? 10 : 8; }
+// Waves per block: one per 512-element chunk up to ten (K = 5120), so every chunk's weights are
+// requested in the first round of loads; longer reductions take further chunks in turn. Ten waves
+// leave 168 registers per wave, which the row-tile loop below stays within by not being unrolled
+// (unrolled, the compiler keeps one row tile's decoded weights live for the next: 222 registers).
+constexpr int MAX_WAVES = 10;
 
 constexpr int ROW_GROUP = 2;    // 16-row tiles of x handled per pass over the weights
 
@@ -34,7 +35,7 @@ constexpr int ROW_GROUP = 2;    // 16-row tiles of x handled per pass over the w
 // OUT is the output type: fp16 (rounded once), or FP32 for a result that is summed further (the
 // shared expert's down projection, added into the MoE output before its one rounding).
 template <int NW, bool GATED, typename OUT = f16>
-__global__ __launch_bounds__(max_waves<NW>() * 64) void linear_kernel(const f16 *__restrict__ x, int M,
+__global__ __launch_bounds__(MAX_WAVES * 64) void linear_kernel(const f16 *__restrict__ x, int M,
                                                                  const uint8_t *__restrict__ codes,
                                                                  const uint8_t *__restrict__ scales,
                                                                  const float *__restrict__ gscale, int N, int K,
@@ -65,28 +66,29 @@ __global__ __launch_bounds__(max_waves<NW>() * 64) void linear_kernel(const f16 
             RawChunk w[NW];
 #pragma unroll
             for (int t = 0; t < NW; ++t) w[t] = load_chunk(cr[t], sr[t], kb, qv ? q : groups - 1);
-#pragma unroll
+#pragma unroll 1
             for (int r = 0; r < ROW_GROUP; ++r) {
                 const int rt = rt0 + r;
                 if (rt >= row_tiles) break;
                 const int m = rt * 16 + n;
                 const bool rv = m < M && qv;
-                // All 16 A fragments are loaded before the chain, unconditionally (rows past M and
-                // lane groups past K re-read valid data of row 0 / lane group 0, then become zeros),
-                // so their latencies overlap instead of adding up.
-                const f16 *xr = x + (size_t)(m < M ? m : 0) * K;
-                const int qa = qv ? q : 0;
+                // All 16 A fragments are loaded before the chain, back to back, so their latencies
+                // overlap. Only lanes of rows below M (and lane groups inside K) load: padding rows
+                // are zeros without a load, so a small batch does not pull duplicate activation
+                // bytes through the CU (each CU's load throughput is the limit here).
+                const f16 *xr = x + (size_t)(rv ? m : 0) * K;
                 f16x8 af[4][4];
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) af[b][s] = a_frag(xr, kb, qa, b, s);
+                    for (int s = 0; s < 4; ++s) af[b][s] = zero8();
+                if (rv) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) af[b][s] = a_frag(xr, kb, q, b, s);
+                }
                 __builtin_amdgcn_sched_barrier(0);  // every load (weights, then A) is issued before the math
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        if (!rv) af[b][s] = zero8();
                 f32x4 acc[NW];
 #pragma unroll
                 for (int t = 0; t < NW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -164,8 +166,11 @@ __device__ __forceinline__ f16x8 b_frag8(const Fp8Chunk &r, int b, int s, bool q
 }
 
 // Two 16-row weight tiles per wave (output columns (nt*2 + t)*16 .. +15), as the NVFP4 kernel.
+// Eight waves: the channel-FP8 chunk holds twice the packed bytes of an NVFP4 one (two weight tiles
+// take 64 registers), so ten waves would spill; at K = 5120 two waves take a second chunk.
+constexpr int FP8_WAVES = 8;
 template <int NW>
-__global__ __launch_bounds__(8 * 64) void linear_fp8_kernel(const f16 *__restrict__ x, int M,
+__global__ __launch_bounds__(FP8_WAVES * 64) void linear_fp8_kernel(const f16 *__restrict__ x, int M,
                                                           const uint8_t *__restrict__ codes,
                                                           const float *__restrict__ chscale, int N, int K,
                                                           f16 *__restrict__ y)
@@ -195,19 +200,20 @@ __global__ __launch_bounds__(8 * 64) void linear_fp8_kernel(const f16 *__restric
                 if (rt >= row_tiles) break;
                 const int m = rt * 16 + n;
                 const bool rv = m < M && qv;
-                const f16 *xr = x + (size_t)(m < M ? m : 0) * K;
-                const int qa = qv ? q : 0;
+                // As in linear_kernel: only valid rows load their A fragments.
+                const f16 *xr = x + (size_t)(rv ? m : 0) * K;
                 f16x8 af[4][4];
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) af[b][s] = a_frag(xr, kb, qa, b, s);
+                    for (int s = 0; s < 4; ++s) af[b][s] = zero8();
+                if (rv) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) af[b][s] = a_frag(xr, kb, q, b, s);
+                }
                 __builtin_amdgcn_sched_barrier(0);  // every load (weights, then A) is issued before the math
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        if (!rv) af[b][s] = zero8();
                 f32x4 acc[NW];
 #pragma unroll
                 for (int t = 0; t < NW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -279,7 +285,7 @@ int launch_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights &w
 {
     const int N = w.rows, K = w.k;
     const int S = num_chunks(K);
-    const int waves = S < 8 ? S : 8;
+    const int waves = S < FP8_WAVES ? S : FP8_WAVES;
     const size_t shmem = (size_t)S * ROW_GROUP * NW * 16 * LDS_ROW * sizeof(float);
     if (shmem > MAX_LDS_BYTES) return NVFP4_ERR_UNSUPPORTED;  // the entry point admits no such K
     const int st = linear_prepare();
@@ -293,7 +299,7 @@ int launch_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, int N, i
 {
     const int K = w.k;
     const int S = num_chunks(K);
-    const int waves = S < max_waves<NW>() ? S : max_waves<NW>();
+    const int waves = S < MAX_WAVES ? S : MAX_WAVES;
     const size_t shmem = (size_t)S * ROW_GROUP * NW * 16 * LDS_ROW * sizeof(float);
     static_assert(ROW_GROUP == 2 && LDS_ROW == 20, "linear_lds_bytes assumes this partial-tile layout");
     if (shmem != linear_lds_bytes(K, NW) || shmem > MAX_LDS_BYTES) return NVFP4_ERR_UNSUPPORTED;

@@ -64,7 +64,13 @@ __device__ __forceinline__ int t_lo_of(int64_t u0, int upt) { return (int)(u0 / 
 // are laid out XCD-major (the blocks of one XCD get consecutive ranges), so that the rounding of
 // U / G to whole units does not fall on the same XCDs every time (an equal split at U/G = 8.5 gave
 // every odd XCD 9 units per block and every even one 8).
-constexpr int FIRST_W = 13, SECOND_W = 7;
+#ifndef NVFP4_FIRST_W
+#define NVFP4_FIRST_W 13
+#endif
+#ifndef NVFP4_SECOND_W
+#define NVFP4_SECOND_W 7
+#endif
+constexpr int FIRST_W = NVFP4_FIRST_W, SECOND_W = NVFP4_SECOND_W;
 
 __device__ __forceinline__ bool unit_range(int64_t U, int first, int64_t &u0, int64_t &u1)
 {
@@ -373,19 +379,23 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
     f16x8 af[4][4];
     // Packed weights of unit u into w. Loads are unconditional (idle waves and missing slices
     // re-read valid rows), so no branch separates them from the waits.
-    auto load_unit = [&](int64_t u, RawChunk (&w)[2 * TP]) {
+    // dummy (block-uniform): the "next unit" of the last unit, whose registers are never used; every
+    // lane then reads the same 64 bytes of row 0 (one cache line per load), so the block's last
+    // unit costs no second copy of its bytes through the CU's memory path.
+    auto load_unit = [&](int64_t u, RawChunk (&w)[2 * TP], bool dummy) {
         const int ti = (int)(u / upt) - t_lo;
         const int it0 = (int)(u % upt) * SL + g.sub * TP;
         const int e = st.e[ti];
         const uint8_t *cb = !SH || e >= 0 ? codes : shx.codes, *sb = !SH || e >= 0 ? scales : shx.scales;
         const size_t eb = !SH || e >= 0 ? (size_t)e * 2 * I : 0;
+        const int q_ld = dummy ? 0 : g.q_ld;
 #pragma unroll
         for (int p = 0; p < TP; ++p) {
             const int i_row = min(it0 + p, itiles - 1) * 16 + g.n;
-            const int rg = layout ? 2 * i_row : i_row;
-            const int ru = layout ? 2 * i_row + 1 : I + i_row;
-            w[2 * p] = load_chunk(cb + (eb + rg) * crow, sb + (eb + rg) * srow, g.kb_ld, g.q_ld);
-            w[2 * p + 1] = load_chunk(cb + (eb + ru) * crow, sb + (eb + ru) * srow, g.kb_ld, g.q_ld);
+            const size_t rg = dummy ? 0 : eb + (layout ? 2 * i_row : i_row);
+            const size_t ru = dummy ? 0 : eb + (layout ? 2 * i_row + 1 : I + i_row);
+            w[2 * p] = load_chunk(cb + rg * crow, sb + rg * srow, g.kb_ld, q_ld);
+            w[2 * p + 1] = load_chunk(cb + ru * crow, sb + ru * srow, g.kb_ld, q_ld);
         }
     };
     // One unit: math on `w` (already loading), next unit's weights into `wn`. Called with the two
@@ -394,15 +404,15 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
         const int ti = (int)(u / upt) - t_lo;
         const int it0 = (int)(u % upt) * SL + g.sub * TP;
         const int e = SH ? __builtin_amdgcn_readfirstlane(st.e[ti]) : st.e[ti], cnt = st.cnt[ti], base = st.base[ti];
-        // With the shared expert the global scale is a select of two loads: read it before the
-        // prefetch below, so that waiting for it never waits for that.
-        float gs = 0.f;
-        if constexpr (SH) gs = e >= 0 ? gscale[e] : shx.gscale[0];
         if (ti != cur) {  // A of this tile's rows, reused by every unit of the tile
             cur = ti;
             load_a_chunk(af, x + (size_t)st.arow[ti][g.n] * K, g.qv && g.n < cnt, g.kb, g.q);
         }
-        load_unit(u + 1 < u1 ? u + 1 : u, wn);  // next unit's weights (the last unit re-reads itself)
+        load_unit(u + 1 < u1 ? u + 1 : u, wn, u + 1 >= u1);  // next unit's weights (after the last: a dummy)
+        // The global scale (a scalar load) is read here, after the LDS reads that address the loads
+        // above: scalar loads and LDS share one wait counter, so an earlier read would hold those
+        // loads back, and here its latency overlaps the MFMA chain.
+        const float gs = SH ? (e >= 0 ? gscale[e] : shx.gscale[0]) : gscale[e];
         __builtin_amdgcn_sched_barrier(0);      // keep those loads ahead of this unit's math
         f32x4 acc[2 * TP];
 #pragma unroll
@@ -417,7 +427,6 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
 #pragma unroll
             for (int j = 0; j < 4; ++j) part[g.wave][t][4 * g.q + j][g.n] = acc[t][j];
         lds_barrier();
-        if constexpr (!SH) gs = gscale[e];
         f16 *hb = !SH || e >= 0 ? h : reinterpret_cast<f16 *>(shx.h);
         const int row = threadIdx.x >> 4, col = threadIdx.x & 15;
 #pragma unroll
@@ -438,7 +447,7 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
         lds_barrier();
     };
     RawChunk wa[2 * TP], wb[2 * TP];
-    load_unit(u0, wa);
+    load_unit(u0, wa, false);
     for (int64_t u = u0; u < u1; u += 2) {
         step(u, wa, wb);
         if (u + 1 < u1) step(u + 1, wb, wa);
@@ -476,16 +485,18 @@ __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, con
     int cur = -1;
     f16x8 af[4][4];
     // Packed weights of unit u into w; unconditional (idle waves re-read valid rows).
-    auto load_unit = [&](int64_t u, RawChunk (&w)[NT]) {
+    // dummy: as in the W13 kernel, the never-used "next unit" of the last unit reads one line.
+    auto load_unit = [&](int64_t u, RawChunk (&w)[NT], bool dummy) {
         const int ti = (int)(u / upt) - t_lo;
         const int nt0 = (int)(u % upt) * UT + g.sub * NT;
         const int e = st.e[ti];
         const uint8_t *cb = !SH || e >= 0 ? codes : shw.codes, *sb = !SH || e >= 0 ? scales : shw.scales;
         const size_t eb = !SH || e >= 0 ? (size_t)e * K : 0;
+        const int q_ld = dummy ? 0 : g.q_ld;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const size_t r = eb + min(nt0 + t, ntiles - 1) * 16 + g.n;
-            w[t] = load_chunk(cb + r * crow, sb + r * srow, g.kb_ld, g.q_ld);
+            const size_t r = dummy ? 0 : eb + min(nt0 + t, ntiles - 1) * 16 + g.n;
+            w[t] = load_chunk(cb + r * crow, sb + r * srow, g.kb_ld, q_ld);
         }
     };
     // One unit: math on `w`, next unit's weights into `wn` (the buffers alternate).
@@ -494,10 +505,6 @@ __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, con
         const int nt0 = (int)(u % upt) * UT + g.sub * NT;
         const int e = SH ? __builtin_amdgcn_readfirstlane(st.e[ti]) : st.e[ti], cnt = st.cnt[ti], base = st.base[ti];
         const bool working = g.chunk && nt0 < ntiles;
-        // With the shared expert the global scale is a select of two loads: read it before the
-        // prefetch below, so that waiting for it never waits for that.
-        float gs = 0.f;
-        if constexpr (SH) gs = e >= 0 ? gscale[e] : shw.gscale[0];
         if (ti != cur) {
             cur = ti;
             const f16 *ha = !SH || e >= 0 ? hin : reinterpret_cast<const f16 *>(shw.h);
@@ -507,13 +514,15 @@ __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, con
         auto out_row = [&](int row) {
             return !SH || e >= 0 ? ws + (size_t)st.pair[ti][row] * K : shw.y + (size_t)(base + row) * K;
         };
-        load_unit(u + 1 < u1 ? u + 1 : u, wn);  // the last unit re-reads itself
+        load_unit(u + 1 < u1 ? u + 1 : u, wn, u + 1 >= u1);  // after the last unit: a dummy
+        // The global scale: a scalar load, read after the LDS reads that address the loads above
+        // (scalar loads and LDS share one wait counter), so its latency overlaps the MFMA chain.
+        const float gs = SH ? (e >= 0 ? gscale[e] : shw.gscale[0]) : gscale[e];
         __builtin_amdgcn_sched_barrier(0);      // keep those loads ahead of this unit's math
         f32x4 acc[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         mma_chunk<NT>(w, af, g.qv, acc);
-        if constexpr (!SH) gs = gscale[e];
         if constexpr (SPLIT == 1) {
             if (working) {
 #pragma unroll
@@ -553,7 +562,7 @@ __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, con
         }
     };
     RawChunk wa[NT], wb[NT];
-    load_unit(u0, wa);
+    load_unit(u0, wa, false);
     for (int64_t u = u0; u < u1; u += 2) {
         step(u, wa, wb);
         if (u + 1 < u1) step(u + 1, wb, wa);
@@ -570,7 +579,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(const int32_t *__restrict__
 {
     const int t = blockIdx.x / blocks_per_token;
     const int nb = blockIdx.x - t * blocks_per_token;
-    const int n = (nb * 256 + threadIdx.x) * 4;
+    const int n = (nb * (int)blockDim.x + (int)threadIdx.x) * 4;
     if (n >= K) return;
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
     // Slots go in batches of 16: a batch's rows are all loaded before the first fmaf, so their
@@ -612,6 +621,32 @@ __global__ __launch_bounds__(256) void reduce_kernel(const int32_t *__restrict__
     *reinterpret_cast<f16x4 *>(out + (size_t)t * K + n) = f16x4{f16_of_f32(s0), f16_of_f32(s1), f16_of_f32(s2), f16_of_f32(s3)};
 }
 
+// Stage the valid slots' h rows (pieces of 8 fp16, 16 bytes) into LDS for the token-major W2
+// kernels: in rounds of up to four pieces per thread, each thread first issues the round's loads,
+// then stores them, so their latencies overlap instead of one round trip per piece. (Four per
+// round: batching eight makes the kernels spill.) One round covers 16 slots of 512 columns.
+template <typename RowOf, typename ValidOf>
+__device__ __forceinline__ void stage_slot_rows(f16 (*s_h)[KCHUNK], int nslot, int pieces, RowOf row_of, ValidOf valid)
+{
+    constexpr int MAXP = 4;
+    const int total = nslot * pieces;
+    for (int base = 0; base < total; base += MAXP * 256) {
+        u32x4 v[MAXP];
+#pragma unroll
+        for (int i = 0; i < MAXP; ++i) {
+            const int idx = base + (int)threadIdx.x + 256 * i;
+            const int k = idx / pieces, pc = idx - k * pieces;
+            if (idx < total && valid(k)) v[i] = *reinterpret_cast<const u32x4 *>(row_of(k) + 8 * pc);
+        }
+#pragma unroll
+        for (int i = 0; i < MAXP; ++i) {
+            const int idx = base + (int)threadIdx.x + 256 * i;
+            const int k = idx / pieces, pc = idx - k * pieces;
+            if (idx < total && valid(k)) *reinterpret_cast<u32x4 *>(&s_h[k][8 * pc]) = v[i];
+        }
+    }
+}
+
 // ---- W2 + reduction, token-major (small batches) -----------------------------------------------------
 // One block per (token t, 16 output rows n-tile); its four waves take the token's slots k = w,
 // w+4, ... For each valid slot the wave runs the same MFMA chain as w2_stream_kernel on a
@@ -650,15 +685,10 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
     const int S = num_chunks(I);
     const size_t crow = (size_t)I >> 1, srow = (size_t)I >> 4;
     if (S == 1) {
-        // One chunk (I <= 512). Stage the valid slots' h rows in LDS (16-byte pieces), and load
-        // each wave's packed rows for up to three slots at once, so the latencies overlap.
+        // One chunk (I <= 512). Each wave issues the packed rows and global scales of up to three
+        // slots at once; then the block stages the valid slots' h rows in LDS while those loads are
+        // in flight, so the weight round trip never waits for the h round trip.
         const int pieces = I >> 3;
-        for (int idx = threadIdx.x; idx < topk * pieces; idx += 256) {
-            const int k = idx / pieces, pc = idx - k * pieces;
-            if (s_e[k] >= 0)
-                *reinterpret_cast<u32x4 *>(&s_h[k][8 * pc]) =
-                    *reinterpret_cast<const u32x4 *>(hin + (size_t)s_row[k] * I + 8 * pc);
-        }
         const int groups = I >> 7;
         const bool qv = q < groups;
         const int q_ld = qv ? q : groups - 1;
@@ -666,13 +696,24 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
         for (int gi = 0; gi < ngroups; ++gi) {
             const int k0 = wave + 12 * gi;
             RawChunk w[3];
+            int eg[3];
+            float gsk[3];
 #pragma unroll
             for (int g = 0; g < 3; ++g) {
                 const int k = k0 + 4 * g;
-                const int e = (k < topk && s_e[k] >= 0) ? s_e[k] : 0;  // idle slots read expert 0, unused
-                const size_t wr = (size_t)e * K + nt * 16 + n;
-                w[g] = load_chunk(codes + wr * crow, scales + wr * srow, 0, q_ld);
+                const bool live = k < topk && s_e[k] >= 0;
+                eg[g] = __builtin_amdgcn_readfirstlane(live ? s_e[k] : 0);
+                // An idle slot's registers are never used: all its lanes read one line of row 0.
+                const size_t wr = live ? (size_t)eg[g] * K + nt * 16 + n : 0;
+                w[g] = load_chunk(codes + wr * crow, scales + wr * srow, 0, live ? q_ld : 0);
             }
+            if (gi == 0)
+                stage_slot_rows(s_h, topk, pieces, [&](int k) { return hin + (size_t)s_row[k] * I; },
+                                [&](int k) { return s_e[k] >= 0; });
+            // The global scales are scalar loads, and scalar loads share a wait counter with LDS:
+            // issued after the staging's LDS reads, they never hold back the h loads.
+#pragma unroll
+            for (int g = 0; g < 3; ++g) gsk[g] = gscale[eg[g]];
             if (gi == 0) __syncthreads();  // s_h staged; it is not written again
 #pragma unroll
             for (int g = 0; g < 3; ++g) {
@@ -688,7 +729,7 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
                     }
                 f32x4 ca[1] = {{0.f, 0.f, 0.f, 0.f}};
                 mma_chunk<1>(reinterpret_cast<const RawChunk(&)[1]>(w[g]), af, qv, ca);
-                if (q == 0) yk[k][n] = ca[0][0] * gscale[s_e[k]];
+                if (q == 0) yk[k][n] = ca[0][0] * gsk[g];
             }
         }
     } else {
@@ -766,15 +807,9 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_shared_kernel(PlanView 
     const int S = num_chunks(I);
     const size_t crow = (size_t)I >> 1, srow = (size_t)I >> 4;
     if (S == 1) {
-        // One chunk (I <= 512). Stage the valid slots' h rows in LDS (16-byte pieces), and load
-        // each wave's packed rows for up to three slots at once, so the latencies overlap.
+        // One chunk (I <= 512), as in w2_token_kernel: weights and global scales first, then the
+        // h rows staged in LDS while they are in flight.
         const int pieces = I >> 3;
-        for (int idx = threadIdx.x; idx < nslot * pieces; idx += 256) {
-            const int k = idx / pieces, pc = idx - k * pieces;
-            if (s_e[k] >= 0)
-                *reinterpret_cast<u32x4 *>(&s_h[k][8 * pc]) =
-                    *reinterpret_cast<const u32x4 *>(slot_h(k) + (size_t)s_row[k] * I + 8 * pc);
-        }
         const int groups = I >> 7;
         const bool qv = q < groups;
         const int q_ld = qv ? q : groups - 1;
@@ -782,14 +817,22 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_shared_kernel(PlanView 
         for (int gi = 0; gi < ngroups; ++gi) {
             const int k0 = wave + 12 * gi;
             RawChunk w[3];
+            int eg[3], kg[3];
+            float gsk[3];
 #pragma unroll
             for (int g = 0; g < 3; ++g) {
                 const int k = k0 + 4 * g;
-                const int e = (k < nslot && s_e[k] >= 0) ? s_e[k] : 0;  // idle slots read expert 0, unused
-                const int ks = k < nslot ? k : 0;
-                const size_t wr = slot_row0(ks, e) + n;
-                w[g] = load_chunk(slot_codes(ks) + wr * crow, slot_scales(ks) + wr * srow, 0, q_ld);
+                const bool live = k < nslot && s_e[k] >= 0;
+                eg[g] = __builtin_amdgcn_readfirstlane(live ? s_e[k] : 0);
+                kg[g] = k < nslot ? k : 0;
+                const size_t wr = live ? slot_row0(kg[g], eg[g]) + n : 0;  // idle slot: one line of row 0
+                w[g] = load_chunk(slot_codes(kg[g]) + wr * crow, slot_scales(kg[g]) + wr * srow, 0, live ? q_ld : 0);
             }
+            if (gi == 0)
+                stage_slot_rows(s_h, nslot, pieces, [&](int k) { return slot_h(k) + (size_t)s_row[k] * I; },
+                                [&](int k) { return s_e[k] >= 0; });
+#pragma unroll
+            for (int g = 0; g < 3; ++g) gsk[g] = kg[g] < topk ? gscale[eg[g]] : shw.gscale[0];  // after the LDS reads
             if (gi == 0) __syncthreads();  // s_h staged; it is not written again
 #pragma unroll
             for (int g = 0; g < 3; ++g) {
@@ -805,7 +848,7 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_shared_kernel(PlanView 
                     }
                 f32x4 ca[1] = {{0.f, 0.f, 0.f, 0.f}};
                 mma_chunk<1>(reinterpret_cast<const RawChunk(&)[1]>(w[g]), af, qv, ca);
-                if (q == 0) yk[k][n] = ca[0][0] * slot_gs(k);
+                if (q == 0) yk[k][n] = ca[0][0] * gsk[g];
             }
         }
     } else {
@@ -932,9 +975,12 @@ int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uin
 int run_reduce(const PlanView &pv, int32_t M, int32_t topk, int32_t K, const float *topk_weights, const float *ws,
                uint16_t *out, hipStream_t s, SharedTerm sh)
 {
-    const int bpt = (K / 4 + 255) / 256;
-    return launch(reduce_kernel, dim3((unsigned)((int64_t)M * bpt)), dim3(256), 0, s, pv.pos_of_pair, topk_weights,
-                  ws, topk, K, bpt, sh, reinterpret_cast<f16 *>(out));
+    // Each CU's load throughput bounds this pass, so a small batch runs 64-thread blocks: its rows
+    // spread over four times as many CUs (at 16 tokens and K = 2048: 128 blocks instead of 32).
+    const int threads = (int64_t)M * ((K / 4 + 255) / 256) < 2 * (int64_t)device_cus() ? 64 : 256;
+    const int bpt = (K / 4 + threads - 1) / threads;
+    return launch(reduce_kernel, dim3((unsigned)((int64_t)M * bpt)), dim3((unsigned)threads), 0, s, pv.pos_of_pair,
+                  topk_weights, ws, topk, K, bpt, sh, reinterpret_cast<f16 *>(out));
 }
 
 }  // namespace nvfp4

@@ -122,6 +122,15 @@ static double dot_half_row(const uint16_t *x, const double *w, int64_t K)
     return s;
 }
 
+/* The same sum with the activation row already decoded to double (xd[k] = orc_half(x[k])): the
+ * terms and their order are those of dot_half_row, so the result is bitwise the same. */
+static double dot_row(const double *xd, const double *w, int64_t K)
+{
+    double s = 0.0;
+    for (int64_t k = 0; k < K; ++k) s += xd[k] * w[k];
+    return s;
+}
+
 /* SiLU(g) = g * sigmoid(g) = g / (1 + e^-g). */
 double orc_silu(double g) { return g / (1.0 + exp(-g)); }
 static double silu(double g) { return orc_silu(g); }
@@ -402,6 +411,7 @@ void orc_moe_grouped(const uint16_t *x, const float *tw, int64_t M, int64_t topk
     {
         double *w13 = (double *)malloc(sizeof(double) * (size_t)(2 * I * K));
         double *w2 = (double *)malloc(sizeof(double) * (size_t)(K * I));
+        double *xd = (double *)malloc(sizeof(double) * (size_t)K);
 #pragma omp for schedule(dynamic, 1)
         for (int64_t e = 0; e < E; ++e) {
             if (offsets[e + 1] == offsets[e]) continue;
@@ -411,9 +421,10 @@ void orc_moe_grouped(const uint16_t *x, const float *tw, int64_t M, int64_t topk
                 int64_t t = sorted_pair[j] / topk;
                 const uint16_t *xt = x + t * K;
                 double *hj = h + j * I;
+                for (int64_t k = 0; k < K; ++k) xd[k] = orc_half(xt[k]);  /* decoded once per pair */
                 for (int64_t i = 0; i < I; ++i) {
-                    double g = dot_half_row(xt, w13 + gate_row(&w, i) * K, K);
-                    double u = dot_half_row(xt, w13 + up_row(&w, i) * K, K);
+                    double g = dot_row(xd, w13 + gate_row(&w, i) * K, K);
+                    double u = dot_row(xd, w13 + up_row(&w, i) * K, K);
                     hj[i] = silu(g) * u;
                 }
                 for (int64_t n = 0; n < K; ++n) {
@@ -425,6 +436,7 @@ void orc_moe_grouped(const uint16_t *x, const float *tw, int64_t M, int64_t topk
         }
         free(w13);
         free(w2);
+        free(xd);
     }
 #pragma omp parallel for num_threads(nthreads) schedule(static)
     for (int64_t t = 0; t < M; ++t) {

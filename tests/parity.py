@@ -45,6 +45,27 @@ def assert_rows_close(gpu: np.ndarray, ref: np.ndarray, what: str = "", rel_l2: 
         assert mab <= max_abs_rms * rms, f"{what} row {r}: max-abs {mab:.3e} > {max_abs_rms}*RMS {rms:.3e}"
 
 
+def assert_rows_close_all(gpu: np.ndarray, ref: np.ndarray, what: str = "", rel_l2: float = REL_L2,
+                          max_abs_rms: float = MAX_ABS_RMS):
+    """assert_rows_close for many rows at once (the same rule, vectorised over rows). Rows with a
+    non-finite or all-zero reference go through the per-row form."""
+    gpu = np.asarray(gpu, dtype=np.float64).reshape(ref.shape[0], -1)
+    ref = np.asarray(ref, dtype=np.float64).reshape(ref.shape[0], -1)
+    special = ~np.isfinite(ref).all(axis=1) | ~np.any(ref, axis=1)
+    for r in np.nonzero(special)[0]:
+        assert_rows_close(gpu[r][None], ref[r][None], f"{what} row {r}", rel_l2, max_abs_rms)
+    g, f = gpu[~special], ref[~special]
+    rows = np.nonzero(~special)[0]
+    assert np.isfinite(g).all(), f"{what}: unexpected non-finite output in row {rows[~np.isfinite(g).all(axis=1)][0]}"
+    err = g - f
+    rl2 = np.linalg.norm(err, axis=1) / np.linalg.norm(f, axis=1)
+    mab = np.abs(err).max(axis=1) / np.sqrt(np.mean(f * f, axis=1))
+    bad = np.nonzero((rl2 > rel_l2) | (mab > max_abs_rms))[0]
+    assert bad.size == 0, (f"{what}: {bad.size} rows fail, first row {rows[bad[0]]}: rel-L2 {rl2[bad[0]]:.3e}, "
+                           f"max-abs/RMS {mab[bad[0]]:.3e}")
+    return float(rl2.max()), float(mab.max())
+
+
 def half_bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
