@@ -11,8 +11,8 @@
 //   * Work unit: (row tile of the plan, a group of 16-row weight tiles). A row tile has at most
 //     16 bucket rows (pairs) of one expert. Units are numbered tile-major and cut into contiguous
 //     ranges, one per persistent block (W13: two 256-thread blocks per CU; W2: one), weighted so
-//     that blocks that start late get fewer units (unit_range). Blocks past the device-side unit
-//     count leave at once, so no device-to-host read is ever needed.
+//     that blocks that start late get fewer units (stream_schedule.hpp). Blocks past the
+//     device-side unit count leave at once, so no device-to-host read is ever needed.
 //   * Block start: the block stages its range's tile descriptors from the plan (expert, rows, first
 //     bucket row, activation row of each row) in LDS: one load after the tile count.
 //   * Inside a block the four waves split the reduction axis into its 512-element chunks
@@ -30,12 +30,13 @@
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 #include "plan_device.hpp"
+#include "stream_schedule.hpp"
 
 namespace nvfp4 {
 namespace {
 
 constexpr int LDS_ROW = 20;  // padded row of 16 floats: rows 4 apart land on different banks
-constexpr int MAX_RANGE_TILES = 16;
+using sched::MAX_RANGE_TILES;
 
 // Per-block staging of the row tiles its unit range touches: expert id, row count, first bucket
 // row, the activation row index of each row (token for W13, bucket row for W2) and, for W2, each
@@ -48,44 +49,10 @@ struct TileStage {
     int pair[MAX_RANGE_TILES][16];
 };
 
-__device__ __forceinline__ int t_lo_of(int64_t u0, int upt) { return (int)(u0 / upt); }
-
-// Contiguous unit range of this block out of U units; returns false if empty.
-//
-// The first `first` blocks are the first resident block of each CU. With two blocks per CU, the
-// second block's first loads queue behind the first block's first unit and its prefetch, so it
-// runs about 1.7 units behind for the whole kernel (measured on MI355X at 16 tokens: first units
-// done at 7.5 vs 12.2 us, ends at 27.7 vs 34.0 us). First blocks therefore take weight FIRST_W and
-// second ones SECOND_W (13 : 7 was the fastest of 11 : 9 to 14 : 6 for W13 at 16 tokens: 36.8 vs
-// 38.1 us with an equal split). Only while there are at most two blocks per CU and more units than
-// blocks; otherwise the split is equal (with U <= G every block has at most one unit anyway).
-//
-// The hardware deals block ids to the 8 XCDs round-robin. Within each group of blocks the ranges
-// are laid out XCD-major (the blocks of one XCD get consecutive ranges), so that the rounding of
-// U / G to whole units does not fall on the same XCDs every time (an equal split at U/G = 8.5 gave
-// every odd XCD 9 units per block and every even one 8).
-#ifndef NVFP4_FIRST_W
-#define NVFP4_FIRST_W 13
-#endif
-#ifndef NVFP4_SECOND_W
-#define NVFP4_SECOND_W 7
-#endif
-constexpr int FIRST_W = NVFP4_FIRST_W, SECOND_W = NVFP4_SECOND_W;
-
+// This block's contiguous unit range out of U units (sched::unit_range); false if empty.
 __device__ __forceinline__ bool unit_range(int64_t U, int first, int64_t &u0, int64_t &u1)
 {
-    const int G = (int)gridDim.x, b = (int)blockIdx.x;
-    const int nA = min(first, G), nB = G - nA;
-    const bool weighted = nB > 0 && nB <= nA && U > G;
-    const int wa = weighted ? FIRST_W : 1, wb = weighted ? SECOND_W : 1;
-    const bool in_a = b < nA;
-    const int n = in_a ? nA : nB, i = in_a ? b : b - nA, w = in_a ? wa : wb;
-    const int L = (n & 7) == 0 ? (i & 7) * (n >> 3) + (i >> 3) : i;
-    const int64_t W0 = (in_a ? 0 : (int64_t)nA * wa) + (int64_t)L * w;
-    const int64_t Wt = (int64_t)nA * wa + (int64_t)nB * wb;
-    u0 = U * W0 / Wt;
-    u1 = U * (W0 + w) / Wt;
-    return u0 < u1;
+    return sched::unit_range(U, first, (int)gridDim.x, (int)blockIdx.x, u0, u1);
 }
 
 // Stage tiles [t_lo, t_lo + ntl) from the plan's tile descriptors: expert id, row count, first
@@ -353,7 +320,7 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
         WaveDotRegs gr;
         if (gate0) wave_dot_load(gr, x + (size_t)blockIdx.x * K, gv, K);
         if (has_units) {
-            const int tl = t_lo_of(u0, upt), nl = (int)((u1 - 1) / upt) - tl + 1;
+            const int tl = sched::range_first_tile(u0, upt), nl = sched::range_tiles(u0, u1, upt);
             if constexpr (FP) stage_tiles_fused(pl, st, tl, nl, topk, fid, frank, Ts, shx.M);
             else stage_tiles<SH>(pv, st, tl, nl, topk, Ts, shx.M);
         }
@@ -367,12 +334,12 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
         }
     }
     if (!has_units) return;  // block-uniform
-    const int t_lo = (int)(u0 / upt);
+    const int t_lo = sched::range_first_tile(u0, upt);
     const G g(K);
     const size_t crow = (size_t)K >> 1, srow = (size_t)K >> 4;
     if constexpr (!SH) {
-        if constexpr (FP) stage_tiles_fused(pl, st, t_lo, (int)((u1 - 1) / upt) - t_lo + 1, topk, fid, frank);
-        else stage_tiles<SH>(pv, st, t_lo, (int)((u1 - 1) / upt) - t_lo + 1, topk);
+        if constexpr (FP) stage_tiles_fused(pl, st, t_lo, sched::range_tiles(u0, u1, upt), topk, fid, frank);
+        else stage_tiles<SH>(pv, st, t_lo, sched::range_tiles(u0, u1, upt), topk);
     }
 
     int cur = -1;
@@ -477,10 +444,10 @@ __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, con
     const int Ts = SH ? (shw.M + 15) >> 4 : 0;  // shared expert tiles, before the plan's
     int64_t u0, u1;
     if (!unit_range((int64_t)(Ts + pv.hdr[3]) * upt, first, u0, u1)) return;
-    const int t_lo = (int)(u0 / upt);
+    const int t_lo = sched::range_first_tile(u0, upt);
     const G g(I);
     const size_t crow = (size_t)I >> 1, srow = (size_t)I >> 4;
-    stage_tiles<SH>(pv, st, t_lo, (int)((u1 - 1) / upt) - t_lo + 1, 0, Ts, SH ? shw.M : 0);
+    stage_tiles<SH>(pv, st, t_lo, sched::range_tiles(u0, u1, upt), 0, Ts, SH ? shw.M : 0);
 
     int cur = -1;
     f16x8 af[4][4];
@@ -889,22 +856,12 @@ int split_for(int k)
     return s <= 1 ? 1 : (s <= 2 ? 2 : 4);
 }
 
-// Persistent grid: `occ` 256-thread blocks per CU, never more blocks than units, and enough
-// blocks that no block's unit range spans more than MAX_RANGE_TILES row tiles. With the weighted
-// split of unit_range (only while G <= 2 * first) a block gets at most 2*13/20 U/G + 1 units, i.e.
-// at most 1.3 t_max/G + 3 row tiles, so G >= t_max / 10 keeps that within 16 (checked by brute
-// force over t_max up to 60000, 1..32 units per tile and 1..304 CUs: at most 14 tiles).
-// *cus_out: the device's CU count.
+// Persistent grid (sched::grid_blocks). *cus_out: the device's CU count.
 unsigned stream_grid(int occ, int64_t units_max, int64_t t_max, int *cus_out)
 {
     const int cus = device_cus();
     *cus_out = cus;
-    static_assert(MAX_RANGE_TILES == 16, "the bound below assumes 16 staged row tiles");
-    int64_t g = occ * (int64_t)cus;
-    const int64_t g_min = (t_max + 9) / 10;
-    if (g < g_min) g = g_min;
-    if (g > units_max) g = units_max;
-    return (unsigned)(g > 0 ? g : 1);
+    return (unsigned)sched::grid_blocks(occ, cus, units_max, t_max);
 }
 
 }  // namespace
@@ -919,7 +876,7 @@ int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, 
     t_max += (shx.M + 15) / 16;  // the shared expert's tiles
     int cus = 0;
     const dim3 grid(stream_grid(W13_OCC, t_max * upt, t_max, &cus)), block(256);
-    const int first = W13_OCC > 1 ? cus : (int)grid.x;  // one block per CU resident first
+    const int first = sched::first_blocks(W13_OCC, cus, (int)grid.x);
     const f16 *xp = reinterpret_cast<const f16 *>(x);
     f16 *hp = reinterpret_cast<f16 *>(h);
     if (fp.ids) {  // the plan built in the launch
@@ -960,7 +917,7 @@ int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uin
     t_max += (shw.M + 15) / 16;
     int cus = 0;
     const dim3 grid(stream_grid(W2_OCC, t_max * upt, t_max, &cus)), block(256);
-    const int first = W2_OCC > 1 ? cus : (int)grid.x;
+    const int first = sched::first_blocks(W2_OCC, cus, (int)grid.x);
     const f16 *hp = reinterpret_cast<const f16 *>(h);
     int st;
     switch (split) {

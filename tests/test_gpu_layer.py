@@ -80,3 +80,18 @@ def test_layer_object_reuses_its_workspace():
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
         f = G.plan_fields(layer.plan, 16, 10, 512)
         assert f["n_valid"] == int(((c2["ids"] >= 0) & (c2["ids"] < 512)).sum())
+
+
+def test_layer_workspace_reused_across_shapes():
+    """One workspace sized for the largest call serves calls of other token counts in turn, in every
+    regime of the decode layer (token-major W2 at 1 token, expert-major at 16 to 64): each output
+    equals that of a fresh workspace."""
+    sizes = (40, 16, 64, 1, 24)
+    need = max(G.nvfp4_moe_layer_workspace_bytes(m, 10, 512, 2048, 512) for m in sizes)
+    ws = torch.full((need,), 0xEE, dtype=torch.uint8, device="cuda")
+    for m in sizes:
+        case, d = _case(m, pattern=7)
+        got = G.nvfp4_moe_layer(d["ids"], 512, d["x"], d["w13"], d["w2"], d["tw"], ws=ws).clone()
+        ref = G.nvfp4_moe_layer(d["ids"], 512, d["x"], d["w13"], d["w2"], d["tw"])
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"m={m}"
