@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     NVFP4Tensor,
     header_functions,
     layer_workspace_parts,
+    layer_h_pair_order,
     lib,
     nvfp4_abi_version,
     nvfp4_linear,

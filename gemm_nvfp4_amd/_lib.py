@@ -373,6 +373,13 @@ def nvfp4_moe_layer_workspace_bytes(M: int, topk: int, E: int, K: int, I: int) -
     return int(lib().nvfp4_moe_layer_workspace_bytes(M, topk, E, K, I))
 
 
+def layer_h_pair_order(M: int, topk: int, E: int) -> bool:
+    """Whether nvfp4_moe_layer leaves h in pair order (row p = t*topk + k) instead of bucket order:
+    the pair-major small-batch path of nvfp4moe.h (4*M*topk <= E, M*topk <= 256, E <= 1024)."""
+    P = M * topk
+    return 4 * P <= E and P <= 256 and E <= 1024
+
+
 def layer_workspace_parts(M: int, topk: int, E: int, I: int) -> tuple[int, int]:
     """Byte offsets of h and of the W2 workspace inside the layer workspace (the plan is at 0)."""
     h_off = nvfp4_moe_plan_bytes(M, topk, E)
@@ -426,7 +433,8 @@ def nvfp4_moe_layer_noalloc(topk_ids: torch.Tensor, E: int, x: torch.Tensor, w13
 class MoELayer:
     """One MoE layer call (nvfp4_moe_layer: plan + W13+SwiGLU, then W2+reduce) with its buffers
     allocated once, so the call can be replayed (or captured in a HIP graph) without allocation.
-    plan, h and ws are views into the one layer workspace."""
+    plan, h and ws are views into the one layer workspace (h in pair order where layer_h_pair_order
+    holds, else in bucket order)."""
 
     def __init__(self, M: int, topk: int, w13: NVFP4Tensor, w2: NVFP4Tensor, layout: int = 0, device="cuda"):
         self.M, self.topk, self.E = M, topk, w13.groups

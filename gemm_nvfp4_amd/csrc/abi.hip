@@ -107,8 +107,9 @@ namespace {
 
 // The plan and W13 after every check passed: one launch (the plan built in the W13 launch) for
 // small decode batches, else the plan's launches and then the regime's W13 kernel.
+// pair_major (the layer call, only where use_pair_major holds): h in pair order, see FusedPlan.
 int enqueue_plan_w13(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E, int32_t *pl, const uint16_t *x,
-                     const nvfp4_weights &w13, int32_t layout, uint16_t *h, hipStream_t s)
+                     const nvfp4_weights &w13, int32_t layout, uint16_t *h, hipStream_t s, bool pair_major = false)
 {
     const int K = w13.k, I = w13.rows / 2;
     const PlanLayout L = nvfp4::plan_layout(M, topk, E);
@@ -120,6 +121,7 @@ int enqueue_plan_w13(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E
         fp.L = L;
         fp.M = M;
         fp.E = E;
+        fp.pair_major = pair_major;
         return nvfp4::run_w13(nvfp4::plan_view(pl, L), L.T, topk, x, w13, layout, h, s, {}, fp);
     }
     int st = nvfp4::run_plan(topk_ids, M, topk, E, pl, L, s);
@@ -129,8 +131,11 @@ int enqueue_plan_w13(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E
 }
 
 // W2 and the reduction after every check passed.
+// pair_ids (the layer call's pair-major path): h is in pair order; the token-major kernel reads
+// each slot's expert from these ids.
 int enqueue_w2(const void *plan, int32_t M, int32_t topk, int32_t E, const uint16_t *h, const nvfp4_weights &w2,
-               const float *topk_weights, uint16_t *out, void *ws, hipStream_t s, nvfp4::SharedTerm sh)
+               const float *topk_weights, uint16_t *out, void *ws, hipStream_t s, nvfp4::SharedTerm sh,
+               const int32_t *pair_ids = nullptr)
 {
     const int K = w2.rows, I = w2.k;
     const PlanLayout L = nvfp4::plan_layout(M, topk, E);
@@ -140,7 +145,7 @@ int enqueue_w2(const void *plan, int32_t M, int32_t topk, int32_t E, const uint1
         if (st != NVFP4_OK) return st;
         return nvfp4::run_reduce(pv, M, topk, K, topk_weights, static_cast<const float *>(ws), out, s, sh);
     }
-    return nvfp4::run_w2(pv, L.T, M, topk, h, w2, topk_weights, out, static_cast<float *>(ws), s, sh);
+    return nvfp4::run_w2(pv, L.T, M, topk, h, w2, topk_weights, out, static_cast<float *>(ws), s, sh, {}, pair_ids);
 }
 
 }  // namespace
@@ -271,9 +276,12 @@ int enqueue_layer(const int32_t *topk_ids, int32_t M, int32_t topk, int32_t E, c
     const LayerParts parts = layer_parts(M, topk, E, w13.k, w13.rows / 2);
     int32_t *plan = reinterpret_cast<int32_t *>(ws);
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + parts.h);
-    const int st = enqueue_plan_w13(topk_ids, M, topk, E, plan, x, w13, layout, h, s);
+    // Small batches take the pair-major path: W13 reads its rows straight from the ids, h in pair
+    // order, and the token-major W2 reads the ids and that h, so no load waits for the plan.
+    const bool pm = nvfp4::use_pair_major((int64_t)M * topk, E);
+    const int st = enqueue_plan_w13(topk_ids, M, topk, E, plan, x, w13, layout, h, s, pm);
     if (st != NVFP4_OK) return st;
-    return enqueue_w2(plan, M, topk, E, h, w2, topk_weights, out, ws + parts.w2, s, {});
+    return enqueue_w2(plan, M, topk, E, h, w2, topk_weights, out, ws + parts.w2, s, {}, pm ? topk_ids : nullptr);
 }
 
 }  // namespace

@@ -137,11 +137,15 @@ struct SharedW13 {
 // The plan built inside the W13 launch (ids == nullptr: read pv): block 0 writes it to `plan`.
 constexpr int FUSED_PLAN_PAIRS = 256;     // one pair per thread of a W13 block
 constexpr int FUSED_PLAN_EXPERTS = 1024;  // four experts per thread in the scans
+// pair_major: W13 takes its rows straight from the ids, one pair per row tile (the pair-major
+// small-batch path of the layer call); h is then written in pair order (row p = t*topk + k) and
+// block 0 only builds and writes the plan.
 struct FusedPlan {
     const int32_t *ids = nullptr;  // [M*topk]
     int32_t *plan = nullptr;
     PlanLayout L{};
     int32_t M = 0, E = 0;
+    bool pair_major = false;
 };
 inline bool use_fused_plan(int64_t P, int32_t E) { return P <= FUSED_PLAN_PAIRS && E <= FUSED_PLAN_EXPERTS; }
 int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, const nvfp4_weights &w,
@@ -166,7 +170,7 @@ struct SharedW2 {
 
 int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uint16_t *h, const nvfp4_weights &w,
            const float *topk_weights, uint16_t *out, float *ws, hipStream_t s, SharedTerm sh = {},
-           SharedW2 shw = {});
+           SharedW2 shw = {}, const int32_t *pair_ids = nullptr);
 // Lets the dense kernels use the CU's whole LDS; idempotent, cheap after the first call on a device.
 // Entry points that enqueue several launches call it before the first one.
 int linear_prepare();
@@ -198,6 +202,10 @@ int run_shared_gate(const uint16_t *x, int32_t M, int32_t K, const uint16_t *g, 
 #define NVFP4_TOKEN_W2_DIV 4
 #endif
 inline bool use_token_w2(int64_t P, int32_t E) { return NVFP4_TOKEN_W2_DIV * P <= (int64_t)E; }
+// The layer call's pair-major path: W13 one pair per row tile straight from the ids, h in pair
+// order, token-major W2 reading the ids and that h (no plan lookup on the critical path). Needs the
+// token-major regime and a plan that one W13 block can build.
+inline bool use_pair_major(int64_t P, int32_t E) { return use_token_w2(P, E) && use_fused_plan(P, E); }
 
 inline bool use_prefill(int64_t M, int64_t P, int32_t E, int32_t K, int32_t I)
 {

@@ -110,7 +110,7 @@ struct PlanLds {
 __device__ int fused_plan(const FusedPlan &fp, PlanLds &pl, int topk, int &id, int &rank)
 {
     const int tid = threadIdx.x, P = (int)fp.L.P, E = fp.E;
-    const bool writer = blockIdx.x == 0;
+    const bool writer = blockIdx.x == 0;  // (in the pair-major launch, block 0 does nothing else)
     const int raw = tid < P ? fp.ids[tid] : -1;
     for (int e = tid; e < E; e += 256) pl.cnt[e] = 0;
     if (tid == 0) pl.bad = 0;
@@ -208,6 +208,27 @@ __device__ void stage_tiles_fused(const PlanLds &pl, TileStage &st, int t_lo, in
     __syncthreads();
 }
 
+// Stage tiles [t_lo, t_lo + ntl) of the pair-major W13 launch: tile p is pair p alone (expert
+// ids[p], or -1 when the id is outside [0, E): the pair is skipped), activation row p / topk, h row
+// p (pair order).
+__device__ __forceinline__ void stage_tiles_pairs(const int32_t *__restrict__ ids, int E, TileStage &st, int t_lo,
+                                                  int ntl, int topk)
+{
+    if ((int)threadIdx.x < ntl) {
+        const int p = t_lo + threadIdx.x, id = ids[p];
+        const bool ok = id >= 0 && id < E;
+        st.e[threadIdx.x] = ok ? id : -1;
+        st.cnt[threadIdx.x] = ok ? 1 : 0;
+        st.base[threadIdx.x] = p;
+    }
+    if ((int)threadIdx.x < ntl * 16) {
+        const int i = threadIdx.x >> 4, r = threadIdx.x & 15;
+        st.arow[i][r] = (t_lo + i) / topk;  // rows past the first are padding, never loaded
+        st.pair[i][r] = t_lo + i;
+    }
+    __syncthreads();
+}
+
 // Tuning of the streaming kernels: TP 16-row weight-tile pairs per wave per unit, *_OCC resident
 // 256-thread blocks per CU.
 #ifndef NVFP4_W13_TP
@@ -290,7 +311,11 @@ __device__ __forceinline__ void mma_chunk(const RawChunk (&w)[NW], const f16x8 a
 // SH: the shared expert's tiles come first (SharedW13); without it the kernel has none of their code.
 //
 // FP: the launch builds the plan itself from fp.ids (fused_plan) instead of reading pv.
-template <int SPLIT, int TP, bool SH, bool FP = false>
+//
+// PM (pair-major, small batches of the layer call): row tile p is pair p alone, taken straight
+// from fp.ids, and h is written in pair order; block 0 builds and writes the plan (for the caller)
+// and computes nothing, blocks 1.. share the units. No unit waits for the plan.
+template <int SPLIT, int TP, bool SH, bool FP = false, bool PM = false>
 __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanView pv, int topk, const f16 *__restrict__ x,
                                                                              const uint8_t *__restrict__ codes,
                                                                              const uint8_t *__restrict__ scales,
@@ -298,6 +323,7 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
                                                                              int layout, f16 *__restrict__ h, int first,
                                                                              SharedW13 shx, FusedPlan fp)
 {
+    static_assert(!PM || (!SH && !FP), "the pair-major launch has neither shared tiles nor staged plan rows");
     using G = Geo<SPLIT>;
     constexpr int SL = G::GROUPS * TP;  // i slices per unit
     __shared__ float part[4][2 * TP][16][LDS_ROW];
@@ -306,14 +332,24 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
     const int upt = (itiles + SL - 1) / SL;  // units per row tile
     const int Ts = SH ? (shx.M + 15) >> 4 : 0;  // shared expert tiles, before the plan's
     int64_t u0, u1;
-    __shared__ std::conditional_t<FP, PlanLds, int> pl;
+    __shared__ std::conditional_t<FP || PM, PlanLds, int> pl;
     int fid = -1, frank = 0;
     int T;
-    if constexpr (FP) T = fused_plan(fp, pl, topk, fid, frank);
-    else T = pv.hdr[3];
+    bool has_units;
+    if constexpr (PM) {
+        if (blockIdx.x == 0) {  // the plan, for the caller; nothing downstream waits for it
+            fused_plan(fp, pl, topk, fid, frank);
+            return;
+        }
+        T = (int)fp.L.P;
+        has_units = sched::unit_range((int64_t)T * upt, first, (int)gridDim.x - 1, (int)blockIdx.x - 1, u0, u1);
+    } else {
+        if constexpr (FP) T = fused_plan(fp, pl, topk, fid, frank);
+        else T = pv.hdr[3];
+        has_units = unit_range((int64_t)(Ts + T) * upt, first, u0, u1);
+    }
     // Shared expert: block b computes the gates of tokens b, b + G, ... (wave 0). The first one's
     // loads are issued before the tile staging, which hides their latency.
-    const bool has_units = unit_range((int64_t)(Ts + T) * upt, first, u0, u1);
     if constexpr (SH) {
         const f16 *gv = reinterpret_cast<const f16 *>(shx.gate);
         const bool gate0 = (int)blockIdx.x < shx.M && threadIdx.x < 64;
@@ -337,7 +373,9 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
     const int t_lo = sched::range_first_tile(u0, upt);
     const G g(K);
     const size_t crow = (size_t)K >> 1, srow = (size_t)K >> 4;
-    if constexpr (!SH) {
+    if constexpr (PM) {
+        stage_tiles_pairs(fp.ids, fp.E, st, t_lo, sched::range_tiles(u0, u1, upt), topk);
+    } else if constexpr (!SH) {
         if constexpr (FP) stage_tiles_fused(pl, st, t_lo, sched::range_tiles(u0, u1, upt), topk, fid, frank);
         else stage_tiles<SH>(pv, st, t_lo, sched::range_tiles(u0, u1, upt), topk);
     }
@@ -353,6 +391,7 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
         const int ti = (int)(u / upt) - t_lo;
         const int it0 = (int)(u % upt) * SL + g.sub * TP;
         const int e = st.e[ti];
+        if constexpr (PM) dummy = dummy || e < 0;  // a skipped pair: nothing of it is read
         const uint8_t *cb = !SH || e >= 0 ? codes : shx.codes, *sb = !SH || e >= 0 ? scales : shx.scales;
         const size_t eb = !SH || e >= 0 ? (size_t)e * 2 * I : 0;
         const int q_ld = dummy ? 0 : g.q_ld;
@@ -378,8 +417,9 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
         load_unit(u + 1 < u1 ? u + 1 : u, wn, u + 1 >= u1);  // next unit's weights (after the last: a dummy)
         // The global scale (a scalar load) is read here, after the LDS reads that address the loads
         // above: scalar loads and LDS share one wait counter, so an earlier read would hold those
-        // loads back, and here its latency overlaps the MFMA chain.
-        const float gs = SH ? (e >= 0 ? gscale[e] : shx.gscale[0]) : gscale[e];
+        // loads back, and here its latency overlaps the MFMA chain. (A skipped pair of the
+        // pair-major launch has no scale and stores nothing: its tile has no rows.)
+        const float gs = SH ? (e >= 0 ? gscale[e] : shx.gscale[0]) : gscale[PM && e < 0 ? 0 : e];
         __builtin_amdgcn_sched_barrier(0);      // keep those loads ahead of this unit's math
         f32x4 acc[2 * TP];
 #pragma unroll
@@ -588,6 +628,15 @@ __global__ __launch_bounds__(256) void reduce_kernel(const int32_t *__restrict__
     *reinterpret_cast<f16x4 *>(out + (size_t)t * K + n) = f16x4{f16_of_f32(s0), f16_of_f32(s1), f16_of_f32(s2), f16_of_f32(s3)};
 }
 
+// One float read on the vector memory path (a buffer load over n floats; an index past them reads
+// 0). A scalar load would share its wait counter with LDS accesses, so every LDS wait after it
+// would also wait for this often cold read; a vector load can be issued beside the weight loads.
+__device__ __forceinline__ float vector_load_f32(const float *base, int index, int n)
+{
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, n * 4, 0x00020000);
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, index * 4, 0, 0));
+}
+
 // Stage the valid slots' h rows (pieces of 8 fp16, 16 bytes) into LDS for the token-major W2
 // kernels: in rounds of up to four pieces per thread, each thread first issues the round's loads,
 // then stores them, so their latencies overlap instead of one round trip per piece. (Four per
@@ -623,12 +672,16 @@ __device__ __forceinline__ void stage_slot_rows(f16 (*s_h)[KCHUNK], int nslot, i
 // are read once per pair instead of once per expert, which costs little when pairs rarely share
 // an expert (P << E); blocks of one n-tile are numbered consecutively per XCD so that shared rows
 // meet in its L2.
+//
+// Pair mode (ids != NULL: the layer call's pair-major path): h is in pair order and each slot's
+// expert is its id (skipped when outside [0, E)), so no load waits for the plan.
 __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int M, int topk, const f16 *__restrict__ hin,
                                                           const uint8_t *__restrict__ codes,
                                                           const uint8_t *__restrict__ scales,
                                                           const float *__restrict__ gscale, int K, int I,
                                                           const float *__restrict__ tw, SharedTerm sh,
-                                                          f16 *__restrict__ out)
+                                                          f16 *__restrict__ out, const int32_t *__restrict__ ids,
+                                                          int E)
 {
     __shared__ float yk[MAX_TOPK][16];
     __shared__ int s_row[MAX_TOPK], s_e[MAX_TOPK];
@@ -640,16 +693,33 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
     const int item = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);  // XCD-aware numbering
     if (item >= G) return;
     const int nt = item / M, t = item - nt * M;
-    if ((int)threadIdx.x < topk) {
+    const int S = num_chunks(I);
+    const bool slot_thread = (int)threadIdx.x < topk;
+    int row_r = 0, e_r = -1;
+    float w_r = 0.f;
+    if (slot_thread) {  // the loads first; the LDS writes wait for them after the h staging below
         const int p = t * topk + threadIdx.x;
-        const int j = pv.pos_of_pair[p];
-        s_row[threadIdx.x] = j;
-        s_e[threadIdx.x] = pv.pair_expert[p];  // -1 for a skipped pair: loaded beside pos_of_pair, not after it
-        s_w[threadIdx.x] = tw[p];
+        w_r = tw[p];
+        if (ids) {
+            row_r = p;
+            e_r = ids[p];
+        } else {
+            row_r = pv.pos_of_pair[p];
+            e_r = pv.pair_expert[p];  // -1 for a skipped pair: loaded beside pos_of_pair, not after it
+        }
+    }
+    // Pair mode with one chunk: h rows are in pair order, so every slot's row is staged now, beside
+    // the id loads (a skipped pair's row holds no result and is never used).
+    if (ids && S == 1)
+        stage_slot_rows(s_h, topk, I >> 3, [&](int k) { return hin + ((size_t)t * topk + k) * I; },
+                        [&](int) { return true; });
+    if (slot_thread) {
+        s_row[threadIdx.x] = row_r;
+        s_e[threadIdx.x] = ids ? (e_r >= 0 && e_r < E ? e_r : -1) : e_r;
+        s_w[threadIdx.x] = w_r;
     }
     __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, q = lane >> 4;
-    const int S = num_chunks(I);
     const size_t crow = (size_t)I >> 1, srow = (size_t)I >> 4;
     if (S == 1) {
         // One chunk (I <= 512). Each wave issues the packed rows and global scales of up to three
@@ -673,14 +743,11 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
                 // An idle slot's registers are never used: all its lanes read one line of row 0.
                 const size_t wr = live ? (size_t)eg[g] * K + nt * 16 + n : 0;
                 w[g] = load_chunk(codes + wr * crow, scales + wr * srow, 0, live ? q_ld : 0);
+                gsk[g] = vector_load_f32(gscale, eg[g], E);  // beside the weights: one round trip
             }
-            if (gi == 0)
+            if (gi == 0 && !ids)  // plan mode: the rows come from the plan, loaded above
                 stage_slot_rows(s_h, topk, pieces, [&](int k) { return hin + (size_t)s_row[k] * I; },
                                 [&](int k) { return s_e[k] >= 0; });
-            // The global scales are scalar loads, and scalar loads share a wait counter with LDS:
-            // issued after the staging's LDS reads, they never hold back the h loads.
-#pragma unroll
-            for (int g = 0; g < 3; ++g) gsk[g] = gscale[eg[g]];
             if (gi == 0) __syncthreads();  // s_h staged; it is not written again
 #pragma unroll
             for (int g = 0; g < 3; ++g) {
@@ -879,6 +946,22 @@ int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, 
     const int first = sched::first_blocks(W13_OCC, cus, (int)grid.x);
     const f16 *xp = reinterpret_cast<const f16 *>(x);
     f16 *hp = reinterpret_cast<f16 *>(h);
+    if (fp.ids && fp.pair_major) {  // block 0: the plan; blocks 1..: one pair per row tile
+        // Unit blocks as for any streaming launch (at least P / 10, so a range stays within the
+        // staging), less one when that keeps block 0 and every unit block resident at once.
+        const int64_t U = fp.L.P * upt;
+        int ub = sched::grid_blocks(W13_OCC, cus, U, fp.L.P);
+        if (ub == W13_OCC * cus && ub > 1 && ub - 1 >= (fp.L.P + 9) / 10) --ub;
+        const dim3 gp((unsigned)(ub + 1));
+        // Block 0 takes a first slot but finishes early, so the unit block that shares its CU counts
+        // as a first block: the weighted split stays on (cus first against cus - 1 second blocks).
+        const int fpm = sched::first_blocks(W13_OCC, cus, ub + 1);
+        switch (split) {
+        case 1: return launch(w13_swiglu_stream_kernel<1, W13_TP, false, false, true>, gp, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, fpm, shx, fp);
+        case 2: return launch(w13_swiglu_stream_kernel<2, W13_TP, false, false, true>, gp, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, fpm, shx, fp);
+        default: return launch(w13_swiglu_stream_kernel<4, W13_TP, false, false, true>, gp, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, fpm, shx, fp);
+        }
+    }
     if (fp.ids) {  // the plan built in the launch
         switch (split) {
         case 1: return launch(shx.M > 0 ? w13_swiglu_stream_kernel<1, W13_TP, true, true> : w13_swiglu_stream_kernel<1, W13_TP, false, true>, grid, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, first, shx, fp);
@@ -894,9 +977,11 @@ int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, 
 }
 
 int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uint16_t *h, const nvfp4_weights &w,
-           const float *topk_weights, uint16_t *out, float *ws, hipStream_t s, SharedTerm sh, SharedW2 shw)
+           const float *topk_weights, uint16_t *out, float *ws, hipStream_t s, SharedTerm sh, SharedW2 shw,
+           const int32_t *pair_ids)
 {
     const int K = w.rows, I = w.k;
+    if (pair_ids && (!use_token_w2((int64_t)M * topk, w.groups) || shw.M > 0)) return NVFP4_ERR_UNSUPPORTED;
     if (use_token_w2((int64_t)M * topk, w.groups)) {
         const int64_t G = (int64_t)M * (K / 16);
         if (shw.M > 0)
@@ -905,7 +990,7 @@ int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uin
                           shw, reinterpret_cast<f16 *>(out));
         return launch(w2_token_kernel, dim3((unsigned)((G + 7) / 8 * 8)), dim3(256), 0, s, pv, M, topk,
                       reinterpret_cast<const f16 *>(h), w.codes, w.scales, w.global_scale, K, I, topk_weights, sh,
-                      reinterpret_cast<f16 *>(out));
+                      reinterpret_cast<f16 *>(out), pair_ids, w.groups);
     }
     if (shw.M > 0) {  // the shared tiles write y; the reduction adds sigma * y after the routed slots
         sh.y = shw.y;

@@ -205,8 +205,12 @@ int nvfp4_moe_w2_reduce(const void *plan, int32_t M, int32_t topk, int32_t E,
  *   ws                     device workspace, at least nvfp4_moe_layer_workspace_bytes(M, topk, E, K,
  *                          I) bytes, 16-byte aligned, contents ignored on entry. On return it holds
  *                          the plan at byte 0 (nvfp4_moe_plan_bytes(M, topk, E) bytes, the layout of
- *                          nvfp4_moe_plan), h (fp16 [M*topk][I], bucket order) at the next multiple of
- *                          256 bytes, and the W2 workspace after that, also at a multiple of 256.
+ *                          nvfp4_moe_plan), h (fp16 [M*topk][I]) at the next multiple of 256 bytes,
+ *                          and the W2 workspace after that, also at a multiple of 256. h is in bucket
+ *                          order, except on the pair-major path for small batches (4*M*topk <= E,
+ *                          M*topk <= 256 and E <= 1024): there row p = t*topk + k holds pair p's h
+ *                          (rows of skipped pairs are unspecified), W13 takes its rows straight from
+ *                          topk_ids and W2 reads the ids and that h, so no load waits for the plan.
  * Requirements: K % 128 == 0, K <= 2048, I % 128 == 0, I <= 2048, 1 <= topk <= 32, E <= 4096;
  * topk_ids and topk_weights 4-byte aligned; x, out and codes 16-byte aligned. Errors: those of
  * the calls it replaces, all checked before anything is enqueued; M = 0 is an OK no-op.

@@ -2,7 +2,7 @@
 // built with g++ and run by test_stream_schedule.py. The kernels include the same header. Over a
 // sweep of CU counts (8..304), blocks per CU (1, 2), units per row tile (1..32), row-tile counts
 // up to 60000, and tile counts below what the grid was sized for (the device-side count is only
-// bounded on the host), it checks:
+// bounded on the host), and for the pair-major W13 launch's unit blocks as well, it checks:
 //   * the grid has at least one block and never more blocks than units;
 //   * the blocks' ranges are disjoint and cover every unit of [0, U) exactly once;
 //   * every range touches at most MAX_RANGE_TILES row tiles, so each unit's staged slot
@@ -67,6 +67,11 @@ int main()
                     const int first = first_blocks(occ, cus, G);
                     const bool cover = t_max * upt <= 20000;
                     check_launch(t_max, upt, G, first, cover);
+                    // the pair-major W13 launch: block 0 builds the plan, one unit block fewer
+                    // when that keeps every block resident
+                    int Gp = G;
+                    if (Gp == occ * cus && Gp > 1 && Gp - 1 >= (t_max + 9) / 10) --Gp;
+                    check_launch(t_max, upt, Gp, first_blocks(occ, cus, Gp + 1), cover);
                     // the device-side tile count below the bound the grid was sized for
                     if (t_max > 1) check_launch((t_max * 3) / 4, upt, G, first, cover);
                     if (t_max > 2) check_launch(1, upt, G, first, cover);

@@ -3,8 +3,9 @@ grouped W13 + SwiGLU and grouped W2 + the slot-order reduction (the grouped-MoE 
 the "[Kernel][SM70] Improve Qwen3.8 no-MTP concurrency" page, "Latest grouped-MoE screen").
 
 Its output, and the plan and h it leaves in the workspace, must be bitwise those of the separate
-calls (nvfp4_moe_plan_w13_swiglu, then nvfp4_moe_w2_reduce) in every regime: the plan built inside
-W13 with token-major W2 (1 token), expert-major W2 with the reduction launch (16 and 40 tokens), the
+calls (nvfp4_moe_plan_w13_swiglu, then nvfp4_moe_w2_reduce) in every regime: the pair-major path
+(1, 4 and 12 tokens: W13 straight from the ids with h in pair order, token-major W2 on that h),
+the plan built inside W13 with expert-major W2 and the reduction launch (16 and 40 tokens), the
 separate plan launch (30 tokens: 300 pairs), and the MFMA-tiled prefill kernels (1024 tokens). The
 16-token case is also compared with the fp64 oracle.
 """
@@ -37,8 +38,8 @@ def _case(m, routing="uniform", pattern=0):
     return case, d
 
 
-@pytest.mark.parametrize("m,routing", [(1, "uniform"), (16, "uniform"), (30, "zipf"), (40, "repeat_invalid"),
-                                       (1024, "uniform")])
+@pytest.mark.parametrize("m,routing", [(1, "uniform"), (4, "repeat_invalid"), (12, "zipf"), (16, "uniform"),
+                                       (30, "zipf"), (40, "repeat_invalid"), (1024, "uniform")])
 def test_layer_call_equals_separate_calls(m, routing):
     case, d = _case(m, routing)
     sep = run_moe(case, 0, dev=d, fused=True)
@@ -55,11 +56,18 @@ def test_layer_call_equals_separate_calls(m, routing):
         assert np.array_equal(got[name], ref[name]), f"plan {name}, m={m}"
     nv = ref["n_valid"]
     h = ws[h_off:h_off + m * 10 * 512 * 2].view(torch.float16).view(m * 10, 512)
-    assert torch.equal(h[:nv].view(torch.int16), sep["h"][:nv].view(torch.int16)), f"h, m={m}"
+    if G.layer_h_pair_order(m, 10, 512):  # pair-major path: row p is pair p's h
+        pos = torch.from_numpy(ref["pos_of_pair"].astype(np.int64)).cuda()
+        valid = pos >= 0
+        assert int(valid.sum()) == nv
+        assert torch.equal(h[valid].view(torch.int16), sep["h"][pos[valid]].view(torch.int16)), f"h, m={m}"
+    else:
+        assert torch.equal(h[:nv].view(torch.int16), sep["h"][:nv].view(torch.int16)), f"h, m={m}"
 
 
-def test_layer_call_against_oracle(orc):
-    case, d = _case(16)
+@pytest.mark.parametrize("m,routing", [(4, "repeat_invalid"), (16, "uniform")])
+def test_layer_call_against_oracle(orc, m, routing):
+    case, d = _case(m, routing)
     out = G.nvfp4_moe_layer(d["ids"], 512, d["x"], d["w13"], d["w2"], d["tw"])
     torch.cuda.synchronize()
     pl = orc.plan(case["ids"], 512, 16)
