@@ -39,15 +39,39 @@ constexpr int PF_R = 5;                 // row tiles per wave (and per pass)
 constexpr int PF_ROWS = 16 * PF_R;      // bucket rows per pass
 constexpr int PF_T = 4;                 // weight tiles per wave
 constexpr int AQ = 32;                  // elements of one lane group per quarter chunk (one step group)
-constexpr int A_ROW = 4 * AQ + 8;       // staged quarter per row: 4 lane groups + 16 bytes of bank padding
 constexpr int NBUF = 3;                 // ring of quarter buffers
+
+// Staged activation quarters: [buffer][lane group q][row][AQ elements], each row's four 16-byte
+// units swizzled. Measured on MI355X (LDS bank-conflict counters over address patterns), a
+// ds_read_b128 is served 32 lanes at a time from 128 four-byte banks, so it is conflict-free when
+// each half-wave's 32 addresses fall in 32 different 16-byte slots modulo 512 bytes. The MFMA A
+// read of lane (n, q) takes unit s of row 16r + n in plane q: half a wave is rows 0..15 of two
+// planes, which no row padding can spread over 32 slots (the old 272-byte pitch left 50% of the
+// LDS cycles to conflicts). XOR-ing the unit with bit 3 of the row and bit 0 of q puts rows n and
+// n + 8, and planes q and q + 1, on different slots. A row is 64 bytes and every plane's row count
+// is a multiple of 16, so planes start at multiples of 512 bytes and a slot depends only on the
+// row within its 8-row group, the plane's parity and the unit.
+__device__ __forceinline__ int a_unit(int row, int q, int u) { return u ^ ((row >> 3) & 1) ^ ((q & 1) << 1); }
+
+// The 16-byte piece of a staged quarter that thread t loads and stores for each 16-row group:
+// unit ps of lane group qs of row srow. Each half-wave stores eight rows of one plane (32
+// distinct slots, conflict-free by a_unit), and four consecutive threads read one 64-byte
+// segment of a row from global memory.
+struct StagePiece {
+    int qs, ps, srow;
+};
+__device__ __forceinline__ StagePiece stage_piece()
+{
+    const int t = threadIdx.x, hw = (t >> 5) & 7;
+    return {hw & 3, t & 3, 8 * (hw >> 2) + ((t >> 2) & 7)};
+}
 #ifndef NVFP4_W2S1_R
 #define NVFP4_W2S1_R 3
 #endif
 constexpr int W2S1_R = NVFP4_W2S1_R;   // row tiles per pass of the one-chunk W2 kernel (two blocks per CU)
 
 struct __attribute__((aligned(16))) PrefillShared {
-    f16 a[NBUF][PF_ROWS][A_ROW];  // activation quarters: [buffer][row][lane group q: 32 elements]
+    f16 a[NBUF][4][PF_ROWS][AQ];  // activation quarters: [buffer][lane group q][row][32 elements, swizzled]
     int arow[PF_ROWS];            // activation row (token or bucket row) of each pass row
     int pair[PF_ROWS];            // pair index of each pass row (W2: where its result goes)
 };
@@ -162,7 +186,8 @@ __device__ __forceinline__ void pass_chunks(PrefillShared &sh, const PassSrc &sr
                                             bool working, int n, int q, Epi &&epi)
 {
     const int red = src.red, S = num_chunks(red), G = 4 * S;
-    const int qs = (threadIdx.x >> 2) & 3, ps = threadIdx.x & 3, srow = threadIdx.x >> 4;  // staged piece
+    const StagePiece sp = stage_piece();
+    const int qs = sp.qs, ps = sp.ps, srow = sp.srow;  // staged piece
     uint32_t vo[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -181,7 +206,7 @@ __device__ __forceinline__ void pass_chunks(PrefillShared &sh, const PassSrc &sr
     };
     auto stage_store = [&](const StageRegs<NR> &st, int buf) {
 #pragma unroll
-        for (int i = 0; i < NR; ++i) *reinterpret_cast<u32x4 *>(&sh.a[buf][srow + 16 * i][AQ * qs + 8 * ps]) = st.v[i];
+        for (int i = 0; i < NR; ++i) *reinterpret_cast<u32x4 *>(&sh.a[buf][qs][srow + 16 * i][8 * a_unit(srow, qs, ps)]) = st.v[i];
     };
     RawChunk w[PF_T];
     auto load_quarter = [&](int c, int b) {
@@ -227,7 +252,7 @@ __device__ __forceinline__ void pass_chunks(PrefillShared &sh, const PassSrc &sr
         for (int t = 0; t < PF_T; ++t) bf[slot][t] = scale8(raw[t], sc[t][s >> 1]);
     };
     auto a_read = [&](int r, int s, int buf) {
-        return *reinterpret_cast<const f16x8 *>(&sh.a[buf][16 * r + n][AQ * q + 8 * s]);
+        return *reinterpret_cast<const f16x8 *>(&sh.a[buf][q][16 * r + n][8 * a_unit(n, q, s)]);
     };
     // The chunk sum starts from -0, the exact identity of addition (-0 + x is x for every x,
     // zeros of both signs included), so no chunk needs a special case.
@@ -314,7 +339,7 @@ __device__ __forceinline__ void pass_dispatch(PrefillShared &sh, const PassSrc &
 constexpr int W13_R = NVFP4_W13_R;  // row tiles per W13 pass
 constexpr int W13_ROWS = 16 * W13_R;
 struct __attribute__((aligned(16))) W13Shared {
-    f16 a[NBUF][W13_ROWS][A_ROW];  // activation quarters, as in PrefillShared
+    f16 a[NBUF][4][W13_ROWS][AQ];  // activation quarters, as in PrefillShared
     int arow[2][W13_ROWS];         // token of each row of pass p, in arow[p & 1]
 };
 
@@ -353,7 +378,8 @@ __global__ __launch_bounds__(256, 1) void w13_swiglu_prefill_kernel(PlanView pv,
     const float gs = gscale[e];
     const int S = num_chunks(K), GQ = 4 * S;  // chunks and quarters per pass
     const int npass = (cnt + W13_ROWS - 1) / W13_ROWS;
-    const int qs = (threadIdx.x >> 2) & 3, ps = threadIdx.x & 3, srow = threadIdx.x >> 4;  // staged piece
+    const StagePiece sp = stage_piece();
+    const int qs = sp.qs, ps = sp.ps, srow = sp.srow;  // staged piece
     auto groups_of = [&](int c) { return min(KCHUNK, K - c * KCHUNK) >> 7; };
     // Token of row threadIdx.x of pass p (rows past the expert's end and passes past the last read
     // token 0: computed, never stored).
@@ -375,7 +401,7 @@ __global__ __launch_bounds__(256, 1) void w13_swiglu_prefill_kernel(PlanView pv,
     };
     auto stage_store = [&](const StageRegs<NR> &st, int buf) {
 #pragma unroll
-        for (int i = 0; i < NR; ++i) *reinterpret_cast<u32x4 *>(&sh.a[buf][srow + 16 * i][AQ * qs + 8 * ps]) = st.v[i];
+        for (int i = 0; i < NR; ++i) *reinterpret_cast<u32x4 *>(&sh.a[buf][qs][srow + 16 * i][8 * a_unit(srow, qs, ps)]) = st.v[i];
     };
     RawChunk w[PF_T];
     auto load_quarter = [&](int c, int b) {
@@ -423,7 +449,7 @@ __global__ __launch_bounds__(256, 1) void w13_swiglu_prefill_kernel(PlanView pv,
         for (int t = 0; t < PF_T; ++t) bf[slot][t] = scale8(raw[t], sc[t][s >> 1]);
     };
     auto a_read = [&](int r, int s, int buf) {
-        return *reinterpret_cast<const f16x8 *>(&sh.a[buf][16 * r + n][AQ * q + 8 * s]);
+        return *reinterpret_cast<const f16x8 *>(&sh.a[buf][q][16 * r + n][8 * a_unit(n, q, s)]);
     };
     cvt_step(0, 0);
     mul_step(0, 0, 0, 0);
@@ -573,7 +599,7 @@ __global__ __launch_bounds__(256, 1) void w2_prefill_kernel(PlanView pv, const f
 // Rows past the expert's end re-read its last row and are never stored.
 template <int NR>
 struct S1Shared {
-    f16 a[NBUF][16 * NR][A_ROW];
+    f16 a[NBUF][4][16 * NR][AQ];  // as in PrefillShared
     int pair[2][16 * NR];  // pair index of each row of pass p, in pair[p & 1]
 };
 
@@ -617,7 +643,8 @@ __global__ __launch_bounds__(256, 2) void w2_prefill_s1_kernel(PlanView pv, cons
         w[t].scales[1] = bload4(rs, (wo >> 3) + 4, 0);
     }
 
-    const int qs = (threadIdx.x >> 2) & 3, ps = threadIdx.x & 3, srow = threadIdx.x >> 4;
+    const StagePiece sp = stage_piece();
+    const int qs = sp.qs, ps = sp.ps, srow = sp.srow;
     // Lane groups past the end of a short chunk (I < 512) stage zeros: an offset of at least 2^31
     // is out of range of every buffer here (all are smaller than 2^31 bytes) and reads as zero.
     const uint32_t oob = qs < groups ? 0u : 0x80000000u;
@@ -635,7 +662,7 @@ __global__ __launch_bounds__(256, 2) void w2_prefill_s1_kernel(PlanView pv, cons
     };
     auto stage_store = [&](const Stage &st, int buf) {
 #pragma unroll
-        for (int i = 0; i < PIECES; ++i) *reinterpret_cast<u32x4 *>(&sh.a[buf][srow + 16 * i][AQ * qs + 8 * ps]) = st.v[i];
+        for (int i = 0; i < PIECES; ++i) *reinterpret_cast<u32x4 *>(&sh.a[buf][qs][srow + 16 * i][8 * a_unit(srow, qs, ps)]) = st.v[i];
     };
     auto pairs_load = [&](int p) {  // pair indices of pass p's rows, one per thread
         const int r = p * ROWS + (int)threadIdx.x;
@@ -672,7 +699,7 @@ __global__ __launch_bounds__(256, 2) void w2_prefill_s1_kernel(PlanView pv, cons
         for (int t = 0; t < PF_T; ++t) bf[slot][t] = scale8(raw[t], sc[t][b][s >> 1]);
     };
     auto a_read = [&](int r, int s, int buf) {
-        return *reinterpret_cast<const f16x8 *>(&sh.a[buf][16 * r + n][AQ * q + 8 * s]);
+        return *reinterpret_cast<const f16x8 *>(&sh.a[buf][q][16 * r + n][8 * a_unit(n, q, s)]);
     };
     int cur = 0;
     cvt_step(0, 0);
