@@ -111,9 +111,18 @@ def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> int:
     return t.data_ptr()
 
 
-def _stream(stream) -> int:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, device_index: int | None = None) -> int:
+    """The HIP stream handle: the given torch stream's, else the current stream of the device
+    (device_index, or the current device), read without building a stream object when torch
+    offers that."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _RAW_STREAM is not None:
+        return _RAW_STREAM(torch.cuda.current_device() if device_index is None else device_index)
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _shape(t: torch.Tensor, name: str, shape: tuple):
@@ -157,9 +166,15 @@ class NVFP4Tensor:
                    torch.from_numpy(gs).to(device))
 
     def desc(self) -> nvfp4_weights:
-        return nvfp4_weights(_dev(self.codes, "codes", torch.uint8), _dev(self.scales, "scales", torch.uint8),
-                             _dev(self.global_scale, "global_scale", torch.float32),
-                             self.groups, self.rows, self.k)
+        """The C descriptor; built once and reused while codes, scales and global_scale are the same
+        tensor objects (their storage must not be reallocated in place)."""
+        c = self.__dict__.get("_desc")
+        if c is not None and c[0] is self.codes and c[1] is self.scales and c[2] is self.global_scale:
+            return c[3]
+        d = nvfp4_weights(_dev(self.codes, "codes", torch.uint8), _dev(self.scales, "scales", torch.uint8),
+                          _dev(self.global_scale, "global_scale", torch.float32), self.groups, self.rows, self.k)
+        self._desc = (self.codes, self.scales, self.global_scale, d)
+        return d
 
 
 def nvfp4_abi_version() -> int:
@@ -449,6 +464,7 @@ class MoELayer:
         self.h = self.workspace[h_off:h_off + M * topk * self.I * 2].view(torch.float16).view(M * topk, self.I)
         self.ws = self.workspace[w2_off:]
         self.out = torch.empty((M, self.K), dtype=torch.float16, device=device)
+        self._fast = None
 
     def _same(self, w: NVFP4Tensor, ref: NVFP4Tensor, name: str):
         if (w.groups, w.rows, w.k) != (ref.groups, ref.rows, ref.k):
@@ -456,13 +472,29 @@ class MoELayer:
 
     def __call__(self, x, topk_ids, topk_weights, w13: NVFP4Tensor | None = None, w2: NVFP4Tensor | None = None,
                  stream=None):
-        if w13 is not None:
+        # The same checks as nvfp4_moe_layer, with the fixed arguments (descriptors of the layer's
+        # weights, workspace and output pointers, the C function) resolved once: an eager call
+        # spends little host time before its first launch.
+        if w13 is not None and w13 is not self.w13:
             self._same(w13, self.w13, "w13")
-        if w2 is not None:
+        if w2 is not None and w2 is not self.w2:
             self._same(w2, self.w2, "w2")
-        _shape(topk_ids, "topk_ids", (self.M, self.topk))
-        nvfp4_moe_layer(topk_ids, self.E, x, w13 or self.w13, w2 or self.w2, topk_weights, self.layout, out=self.out,
-                        ws=self.workspace, stream=stream)
+        f = self._fast
+        if f is None:
+            f = self._fast = (lib().nvfp4_moe_layer, self.out.data_ptr(), self.workspace.data_ptr(),
+                              self.workspace.numel(), self.out.device.index)
+        args = ((topk_ids, "topk_ids", (self.M, self.topk), torch.int32), (x, "x", (self.M, self.K), torch.float16),
+                (topk_weights, "topk_weights", (self.M, self.topk), torch.float32))
+        for t, name, shape, _ in args:  # every shape before any device check, as nvfp4_moe_layer
+            if t.shape != shape:
+                _shape(t, name, shape)
+        for t, name, _, dtype in args:
+            _dev(t, name, dtype)
+        d13 = (w13 or self.w13).desc()
+        d2 = (w2 or self.w2).desc()
+        _check("nvfp4_moe_layer", f[0](topk_ids.data_ptr(), self.M, self.topk, self.E, x.data_ptr(), C.byref(d13),
+                                       self.layout, C.byref(d2), topk_weights.data_ptr(), f[1], f[2], f[3],
+                                       _stream(stream, f[4])))
         return self.out
 
 
