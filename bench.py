@@ -274,7 +274,7 @@ def w13_kernel_timing(M, launches, W13, routes):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w13_swiglu_stream_decode16_traffic.txt")
-ROOFLINE_KERNEL = "w13_swiglu_stream_kernel<4, 1, false, true> (routing plan built in the launch)"
+ROOFLINE_KERNEL = "w13_swiglu_stream_kernel<4, 1, false, true, false> (routing plan built in the launch)"
 KERNEL_SOURCES = ("gemm_nvfp4_amd/csrc/moe_gemm.hip", "gemm_nvfp4_amd/csrc/nvfp4_device.hpp",
                   "gemm_nvfp4_amd/csrc/internal.hpp", "gemm_nvfp4_amd/csrc/plan_device.hpp",
                   "gemm_nvfp4_amd/csrc/stream_schedule.hpp")
