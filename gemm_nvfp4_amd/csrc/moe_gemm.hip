@@ -663,6 +663,30 @@ __device__ __forceinline__ void stage_slot_rows(f16 (*s_h)[KCHUNK], int nslot, i
     }
 }
 
+// The slot-order fold of one output column of the token-major kernels: acc = fmaf(w_k, y_k, acc)
+// over the valid slots k < nslot in order, from +0 (the reduce kernel's chain). The slot data are
+// read from LDS eight slots at a time, all reads before the fmafs, so the chain does not wait for
+// one LDS round trip per slot.
+__device__ __forceinline__ float slot_fold(const int *s_e, const float *s_w, const float *yk, int nslot, int col)
+{
+    float acc = 0.f;
+    for (int k0 = 0; k0 < nslot; k0 += 8) {
+        int e[8];
+        float w[8], y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int k = k0 + i < nslot ? k0 + i : k0;
+            e[i] = s_e[k];
+            w[i] = s_w[k];
+            y[i] = yk[k * 16 + col];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (k0 + i < nslot && e[i] >= 0) acc = fmaf(w[i], y[i], acc);
+    }
+    return acc;
+}
+
 // ---- W2 + reduction, token-major (small batches) -----------------------------------------------------
 // One block per (token t, 16 output rows n-tile); its four waves take the token's slots k = w,
 // w+4, ... For each valid slot the wave runs the same MFMA chain as w2_stream_kernel on a
@@ -733,13 +757,15 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
         for (int gi = 0; gi < ngroups; ++gi) {
             const int k0 = wave + 12 * gi;
             RawChunk w[3];
-            int eg[3];
+            int eg[3], se[3];
             float gsk[3];
+#pragma unroll
+            for (int g = 0; g < 3; ++g) se[g] = k0 + 4 * g < topk ? s_e[k0 + 4 * g] : -1;  // LDS reads together
 #pragma unroll
             for (int g = 0; g < 3; ++g) {
                 const int k = k0 + 4 * g;
-                const bool live = k < topk && s_e[k] >= 0;
-                eg[g] = __builtin_amdgcn_readfirstlane(live ? s_e[k] : 0);
+                const bool live = se[g] >= 0;
+                eg[g] = __builtin_amdgcn_readfirstlane(live ? se[g] : 0);
                 // An idle slot's registers are never used: all its lanes read one line of row 0.
                 const size_t wr = live ? (size_t)eg[g] * K + nt * 16 + n : 0;
                 w[g] = load_chunk(codes + wr * crow, scales + wr * srow, 0, live ? q_ld : 0);
@@ -752,7 +778,7 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
 #pragma unroll
             for (int g = 0; g < 3; ++g) {
                 const int k = k0 + 4 * g;
-                if (k >= topk || s_e[k] < 0) continue;  // wave-uniform
+                if (se[g] < 0) continue;  // wave-uniform (also past topk)
                 f16x8 af[4][4];
 #pragma unroll
                 for (int bb = 0; bb < 4; ++bb)
@@ -789,9 +815,7 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
     }
     __syncthreads();
     if ((int)threadIdx.x < 16) {
-        float acc = 0.f;
-        for (int k = 0; k < topk; ++k)
-            if (s_e[k] >= 0) acc = fmaf(s_w[k], yk[k][threadIdx.x], acc);
+        float acc = slot_fold(s_e, s_w, &yk[0][0], topk, threadIdx.x);
         if (sh.y) acc = fmaf(sh.sigma[t], sh.y[(size_t)t * K + nt * 16 + threadIdx.x], acc);  // shared expert last
         out[(size_t)t * K + nt * 16 + threadIdx.x] = f16_of_f32(acc);
     }
@@ -909,9 +933,7 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_shared_kernel(PlanView 
     }
     __syncthreads();
     if ((int)threadIdx.x < 16) {
-        float acc = 0.f;
-        for (int k = 0; k < topk; ++k)
-            if (s_e[k] >= 0) acc = fmaf(s_w[k], yk[k][threadIdx.x], acc);
+        float acc = slot_fold(s_e, s_w, &yk[0][0], topk, threadIdx.x);
         acc = fmaf(s_w[topk], yk[topk][threadIdx.x], acc);  // the shared expert last
         out[(size_t)t * K + nt * 16 + threadIdx.x] = f16_of_f32(acc);
     }
