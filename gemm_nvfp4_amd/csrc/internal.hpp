@@ -33,21 +33,12 @@ constexpr int MAX_MOE_RED = 2048;
 // K = 32768; the plain projection takes one tile per wave beyond 16384.
 constexpr int MAX_LINEAR_K = 32768;
 constexpr int MAX_LINEAR_SWIGLU_K = 16384;  // always two weight tiles per wave (gate and up)
-constexpr int MAX_LINEAR_FP8_K = 16384;     // two weight tiles per wave when N % 32 == 0
+constexpr int MAX_LINEAR_FP8_K = 16384;     // two weight tiles per wave always fit
 constexpr size_t MAX_LDS_BYTES = 160 * 1024;
 constexpr size_t linear_lds_bytes(int k, int nw) { return (size_t)((k + 511) / 512) * 2 * nw * 16 * 20 * 4; }
-// Weight tiles per wave of the plain dense projection: two when the rows pair up and the partial
-// tiles fit in LDS, else one.
-// Weight tiles per wave of the dense kernels (a tuning switch). One tile per wave doubles the
-// grid to 272 blocks at 4352 rows but was slower at every batch size on MI355X (4352x5120: 10.6
-// vs 8.8 us at M=1, 26.5 vs 17.8 us at M=32), so two tiles per wave are used wherever they fit.
-#ifndef NVFP4_LINEAR_MAX_TILES
-#define NVFP4_LINEAR_MAX_TILES 2
-#endif
-constexpr int linear_tiles(int rows, int k)
-{
-    return NVFP4_LINEAR_MAX_TILES >= 2 && rows % 32 == 0 && linear_lds_bytes(k, 2) <= MAX_LDS_BYTES ? 2 : 1;
-}
+// Most weight tiles per wave of the plain dense kernels: two wherever their partial tiles fit in
+// LDS, else one. A block then owns up to 16 output columns per tile.
+constexpr int linear_max_tiles(int k) { return linear_lds_bytes(k, 2) <= MAX_LDS_BYTES ? 2 : 1; }
 
 // CU count of the current device, queried from the runtime once per device and cached.
 inline int device_cus()

@@ -6,10 +6,13 @@
 // projections of the packed MLP weights): h = fp16(silu(g) * u) with g and u the projections on
 // the gate and up rows.
 //
-// gfx950 design: one block per 16 output columns (weight rows; gate and up rows of 16 h columns in
-// the gated form). Its waves share the reduction axis, one 512-element chunk each (intra-block
-// split-K). A wave decodes its chunk once into MFMA B fragments in registers and applies them to
-// every 16-row tile of x, so at small M the weight bytes are read from HBM exactly once. Chunk
+// gfx950 design: one block per R consecutive output columns (weight rows; gate and up rows of R h
+// columns in the gated form), R chosen so that the blocks cover every CU with an equal share of the
+// weight bytes (each CU's load path, not HBM, limits a small launch: at 4352 rows, 17 columns on
+// 256 blocks instead of 32 on 136 took the one-token projection from 8.9 to 8.5 us). Its waves share
+// the reduction axis, one 512-element chunk each (intra-block split-K). A wave decodes its chunk into
+// MFMA B fragments in registers and applies them to every 16-row tile of x, so at small M the weight
+// bytes are read from HBM exactly once. Chunk
 // partials meet in LDS and are added in chunk order, which is the same reduction order as every
 // other GEMM here; the gated epilogue is the MoE W13 epilogue (global scale, then SwiGLU). A batch
 // of any size is therefore bitwise equal to single-row calls, and the gated form equals the
@@ -29,66 +32,155 @@ constexpr int MAX_WAVES = 10;
 
 constexpr int ROW_GROUP = 2;    // 16-row tiles of x handled per pass over the weights
 
-// Each wave holds NW 16-row weight tiles. Plain (GATED false): tile t covers output columns
-// (nt*NW + t)*16 .. +15. Gated: tile 0 holds the gate rows and tile 1 the up rows of h columns
-// nt*16 .. +15 (layout 0: rows i and I + i; layout 1: rows 2i and 2i + 1).
+// Small batches stage each wave's activation chunk in LDS: one 16-byte direct-to-LDS load per lane
+// and row (gfx950 global_load_lds_dwordx4: lane i's bytes land at the row's base + 16 i) brings a
+// whole 1 KB chunk row in with one instruction, where the fragment loads take sixteen per row tile
+// whatever the number of rows (at one token, 60% of a CU's load instructions, with 4 of 64 lanes
+// active each; a CU's load issue, not HBM, bounds these launches). Row pitch 1040 bytes: the
+// fragment reads of 16 rows and two lane groups hit distinct 16-byte bank slots.
+constexpr int XS_ROWS = 8;       // batches up to this many rows stage (M * 1040 bytes per wave)
+constexpr int XS_PITCH = 1040;
+
+// Rows [0, M) of the activation chunk starting at element kb into this wave's LDS rows. Lanes past
+// K load the row's first 16 bytes into the tail of the row's slot, which no fragment reads (lane
+// groups past the chunk end feed zeros).
+__device__ __forceinline__ void stage_x_chunk(const f16 *x, int M, int K, int kb, unsigned char *xw, int lane)
+{
+    const int k = kb + 8 * lane;
+    for (int r = 0; r < M; ++r) {
+        const f16 *src = x + (size_t)r * K + (k < K ? k : 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                         (__attribute__((address_space(3))) void *)(xw + r * XS_PITCH), 16, 0, 0);
+    }
+}
+
+// An empty asm that the compiler must treat as changing the weight registers: placed inside the
+// row-tile loop, it keeps the decode there. Hoisted out of the loop, the decoded fragments would hold
+// 128 registers across it (spills) and the decode would wait for the weights before the A loads of
+// the first row tile are issued. No instruction is emitted.
+__device__ __forceinline__ void keep_in_loop(RawChunk &w)
+{
+#pragma unroll
+    for (int b = 0; b < 4; ++b) asm volatile("" : "+v"(w.codes[b]));
+    asm volatile("" : "+v"(w.scales[0]), "+v"(w.scales[1]));
+}
+
+// Where a kernel's A fragments come from.
+enum AFrom { A_GLOBAL, A_BUFFER, A_STAGED };
+
+// The A fragments of one 16-row tile, row m of the pass's M rows (xg: the pass's first row): from
+// this wave's staged LDS rows (A_STAGED: the pass is rows 0..M-1 of x), or from x by loads that only
+// valid lanes issue (A_GLOBAL) or by buffer loads that all lanes issue, at an out-of-range offset for
+// the others (A_BUFFER: no branch, so no wait for the earlier loads at the merge; measured faster
+// for the channel-FP8 kernel, slower for the NVFP4 one). Rows at or past M, and lane groups past the
+// chunk end, are zeros.
+template <AFrom AF>
+__device__ __forceinline__ void load_a_tile(f16x8 (&af)[4][4], const f16 *xg, rsrc_t xr, const unsigned char *xw,
+                                            int m, int M, int K, int kb, int q, bool qv)
+{
+    const bool v = m < M && qv;
+    if constexpr (AF == A_STAGED) {
+        // The compiler does not order LDS reads after the direct-to-LDS loads that fill them: wait
+        // for every load of this wave (vmcnt(0); expcnt and lgkmcnt left at their maxima).
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        // an LDS-typed pointer, so that the reads are ds_read_b128 and not flat loads
+        typedef const __attribute__((address_space(3))) f16x8 lds_f16x8;
+        lds_f16x8 *p = (lds_f16x8 *)(xw + (v ? m : 0) * XS_PITCH + 256 * q);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) af[b][s] = v ? p[4 * b + s] : zero8();
+    } else if constexpr (AF == A_BUFFER) {
+        const uint32_t o = v ? (uint32_t)(m * K + kb + 128 * q) * 2u : BUF_OOB;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) af[b][s] = __builtin_bit_cast(f16x8, bload16(xr, o + 64 * b + 16 * s, 0));
+    } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) af[b][s] = zero8();
+        if (v) {
+            const f16 *xp = xg + (size_t)m * K;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) af[b][s] = a_frag(xp, kb, q, b, s);
+        }
+    }
+}
+
+// Each wave holds NW 16-row weight tiles. Block nt owns output columns nt*R .. nt*R + R - 1 (R at
+// most 16*NW plain, 16 gated). Plain (GATED false): lane n of tile t takes column nt*R + 16t + n.
+// Gated: tile 0 holds the gate rows and tile 1 the up rows of h columns nt*R + n (layout 0: rows i
+// and I + i; layout 1: rows 2i and 2i + 1). Lanes of columns outside the block's range read zero
+// weights; an MFMA column depends only on its own operands, so a column's result is the same
+// whatever R is.
 // OUT is the output type: fp16 (rounded once), or FP32 for a result that is summed further (the
 // shared expert's down projection, added into the MoE output before its one rounding).
-template <int NW, bool GATED, typename OUT = f16>
+template <int NW, bool GATED, typename OUT, bool XS>
 __global__ __launch_bounds__(MAX_WAVES * 64) void linear_kernel(const f16 *__restrict__ x, int M,
                                                                  const uint8_t *__restrict__ codes,
                                                                  const uint8_t *__restrict__ scales,
                                                                  const float *__restrict__ gscale, int N, int K,
-                                                                 int layout, OUT *__restrict__ y)
+                                                                 int layout, OUT *__restrict__ y, int R)
 {
-    extern __shared__ float part[];  // [S][ROW_GROUP][NW][16][LDS_ROW]
+    extern __shared__ float part[];  // [S][ROW_GROUP][NW][16][LDS_ROW], then with XS the staged rows
     const int nt = blockIdx.x;
+    const int col0 = nt * R;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
     const int n = lane & 15, q = lane >> 4;
     const int S = num_chunks(K);
     const int row_tiles = (M + 15) >> 4;
-    const int col = nt * 16 + n;  // gated: h column of this lane's weight rows
     const uint8_t *cr[NW], *sr[NW];
+    bool cv[NW];  // this lane's column of tile t lies in the block's range
 #pragma unroll
     for (int t = 0; t < NW; ++t) {
-        const size_t wrow = GATED ? (size_t)(layout ? 2 * col + t : t * N + col) : (size_t)((nt * NW + t) * 16 + n);
+        const int lc = GATED ? n : 16 * t + n;  // column within the block
+        cv[t] = lc < R && col0 + lc < N;
+        const int col = cv[t] ? col0 + lc : 0;
+        const size_t wrow = GATED ? (size_t)(layout ? 2 * col + t : t * N + col) : (size_t)col;
         cr[t] = codes + wrow * ((size_t)K >> 1);
         sr[t] = scales + wrow * ((size_t)K >> 4);
     }
     const float gs = gscale[0];
+    unsigned char *xw = reinterpret_cast<unsigned char *>(part + (size_t)S * ROW_GROUP * NW * 16 * LDS_ROW) +
+                        (size_t)wave * M * XS_PITCH;
 
     for (int rt0 = 0; rt0 < row_tiles; rt0 += ROW_GROUP) {
+        // x rows of this pass (offsets relative to its first row stay within 32 bits)
+        const int gm = min(M - 16 * rt0, 16 * ROW_GROUP);
+        const f16 *xg = x + (size_t)16 * rt0 * K;
+        const rsrc_t xr = make_rsrc(xg, (uint32_t)gm * (uint32_t)K * 2u);
         for (int c = wave; c < S; c += nwaves) {
             const int kb = c * KCHUNK;
             const int groups = min(KCHUNK, K - kb) >> 7;  // 128-element lane groups with data
             const bool qv = q < groups;
+            // Lanes outside the block's columns or past the chunk end load nothing (masked lanes cost
+            // the address unit nothing; a buffer load at an out-of-range offset would) and keep the
+            // zero codes and scales, which decode to exact zeros.
             RawChunk w[NW];
 #pragma unroll
-            for (int t = 0; t < NW; ++t) w[t] = load_chunk(cr[t], sr[t], kb, qv ? q : groups - 1);
+            for (int t = 0; t < NW; ++t) {
+                w[t] = RawChunk{};
+                if (cv[t] && qv) w[t] = load_chunk(cr[t], sr[t], kb, q);
+            }
+            if constexpr (XS) stage_x_chunk(x, M, K, kb, xw, lane);
 #pragma unroll 1
             for (int r = 0; r < ROW_GROUP; ++r) {
                 const int rt = rt0 + r;
                 if (rt >= row_tiles) break;
-                const int m = rt * 16 + n;
-                const bool rv = m < M && qv;
-                // All 16 A fragments are loaded before the chain, back to back, so their latencies
-                // overlap. Only lanes of rows below M (and lane groups inside K) load: padding rows
-                // are zeros without a load, so a small batch does not pull duplicate activation
-                // bytes through the CU (each CU's load throughput is the limit here).
-                const f16 *xr = x + (size_t)(rv ? m : 0) * K;
+                // All 16 A fragments are read before the chain, back to back, so their latencies
+                // overlap.
                 f16x8 af[4][4];
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) af[b][s] = zero8();
-                if (rv) {
-#pragma unroll
-                    for (int b = 0; b < 4; ++b)
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) af[b][s] = a_frag(xr, kb, q, b, s);
-                }
+                load_a_tile<XS ? A_STAGED : A_GLOBAL>(af, xg, xr, xw, r * 16 + n, gm, K, kb, q, qv);
                 __builtin_amdgcn_sched_barrier(0);  // every load (weights, then A) is issued before the math
+#pragma unroll
+                for (int t = 0; t < NW; ++t) keep_in_loop(w[t]);
                 f32x4 acc[NW];
 #pragma unroll
                 for (int t = 0; t < NW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -100,7 +192,7 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void linear_kernel(const f16 *__res
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
 #pragma unroll
-                        for (int t = 0; t < NW; ++t) acc[t] = mfma_step(af[b][s], b_frag(w[t], sc[t], b, s, qv), acc[t]);
+                        for (int t = 0; t < NW; ++t) acc[t] = mfma_step(af[b][s], decode8(w[t].codes[b][s], sc[t][s >> 1]), acc[t]);
                 }
 #pragma unroll
                 for (int t = 0; t < NW; ++t) {
@@ -123,10 +215,13 @@ __global__ __launch_bounds__(MAX_WAVES * 64) void linear_kernel(const f16 *__res
                         tot[t] += part[(((size_t)c * ROW_GROUP + r) * NW + t) * 16 * LDS_ROW + row * LDS_ROW + cl];
                 }
                 if constexpr (GATED) {
-                    y[(size_t)m * N + nt * 16 + cl] = f16_of_f32(swiglu(tot[0] * gs, tot[1] * gs));
+                    if (cl < R && col0 + cl < N) y[(size_t)m * N + col0 + cl] = f16_of_f32(swiglu(tot[0] * gs, tot[1] * gs));
                 } else {
 #pragma unroll
-                    for (int t = 0; t < NW; ++t) y[(size_t)m * N + (nt * NW + t) * 16 + cl] = to_out<OUT>(tot[t] * gs);
+                    for (int t = 0; t < NW; ++t) {
+                        const int lc = 16 * t + cl;
+                        if (lc < R && col0 + lc < N) y[(size_t)m * N + col0 + lc] = to_out<OUT>(tot[t] * gs);
+                    }
                 }
             }
         }
@@ -146,73 +241,70 @@ struct Fp8Chunk {
     u32x4 codes[8];  // codes[j] = elements [kb + 128q + 16j, +16)
 };
 
-__device__ __forceinline__ Fp8Chunk load_chunk8(const uint8_t *row, int kb, int q_ld)
-{
-    Fp8Chunk r;
-    const uint8_t *c = row + kb + 128 * q_ld;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r.codes[j] = *reinterpret_cast<const u32x4 *>(c + 16 * j);
-    return r;
-}
-
 // B fragment of step (b, s): elements [128q + 32b + 8s, +8), i.e. half of load 2b + s/2.
-__device__ __forceinline__ f16x8 b_frag8(const Fp8Chunk &r, int b, int s, bool qv)
+__device__ __forceinline__ f16x8 b_frag8(const Fp8Chunk &r, int b, int s)
 {
     const u32x4 v = r.codes[2 * b + (s >> 1)];
     const uint32_t d0 = v[2 * (s & 1)], d1 = v[2 * (s & 1) + 1];
     const f16x2 p0 = e4m3_pair<false>(d0), p1 = e4m3_pair<true>(d0), p2 = e4m3_pair<false>(d1), p3 = e4m3_pair<true>(d1);
-    const f16x8 w = f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-    return qv ? w : zero8();
+    return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// Two 16-row weight tiles per wave (output columns (nt*2 + t)*16 .. +15), as the NVFP4 kernel.
+// Up to two 16-row weight tiles per wave, block nt owning output columns nt*R .. +R-1, as the
+// NVFP4 kernel.
 // Eight waves: the channel-FP8 chunk holds twice the packed bytes of an NVFP4 one (two weight tiles
 // take 64 registers), so ten waves would spill; at K = 5120 two waves take a second chunk.
 constexpr int FP8_WAVES = 8;
-template <int NW>
+template <int NW, bool XS>
 __global__ __launch_bounds__(FP8_WAVES * 64) void linear_fp8_kernel(const f16 *__restrict__ x, int M,
                                                           const uint8_t *__restrict__ codes,
                                                           const float *__restrict__ chscale, int N, int K,
-                                                          f16 *__restrict__ y)
+                                                          f16 *__restrict__ y, int R)
 {
-    extern __shared__ float part[];  // [S][ROW_GROUP][NW][16][LDS_ROW]
+    extern __shared__ float part[];  // [S][ROW_GROUP][NW][16][LDS_ROW], then with XS the staged rows
     const int nt = blockIdx.x;
+    const int col0 = nt * R;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
     const int n = lane & 15, q = lane >> 4;
     const int S = num_chunks(K);
     const int row_tiles = (M + 15) >> 4;
     const uint8_t *cr[NW];
+    bool cv[NW];
 #pragma unroll
-    for (int t = 0; t < NW; ++t) cr[t] = codes + (size_t)((nt * NW + t) * 16 + n) * K;
+    for (int t = 0; t < NW; ++t) {
+        cv[t] = 16 * t + n < R && col0 + 16 * t + n < N;
+        cr[t] = codes + (size_t)(cv[t] ? col0 + 16 * t + n : 0) * K;
+    }
+    unsigned char *xw = reinterpret_cast<unsigned char *>(part + (size_t)S * ROW_GROUP * NW * 16 * LDS_ROW) +
+                        (size_t)wave * M * XS_PITCH;
 
     for (int rt0 = 0; rt0 < row_tiles; rt0 += ROW_GROUP) {
+        // x rows of this pass (offsets relative to its first row stay within 32 bits)
+        const int gm = min(M - 16 * rt0, 16 * ROW_GROUP);
+        const f16 *xg = x + (size_t)16 * rt0 * K;
+        const rsrc_t xr = make_rsrc(xg, (uint32_t)gm * (uint32_t)K * 2u);
         for (int c = wave; c < S; c += nwaves) {
             const int kb = c * KCHUNK;
             const int groups = min(KCHUNK, K - kb) >> 7;
             const bool qv = q < groups;
-            Fp8Chunk w[NW];
+            Fp8Chunk w[NW];  // as in linear_kernel: masked lanes keep zero bytes, exact zero weights
 #pragma unroll
-            for (int t = 0; t < NW; ++t) w[t] = load_chunk8(cr[t], kb, qv ? q : groups - 1);
+            for (int t = 0; t < NW; ++t) {
+                w[t] = Fp8Chunk{};
+                if (cv[t] && qv) {
+                    const uint8_t *c = cr[t] + kb + 128 * q;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) w[t].codes[j] = *reinterpret_cast<const u32x4 *>(c + 16 * j);
+                }
+            }
+            if constexpr (XS) stage_x_chunk(x, M, K, kb, xw, lane);
 #pragma unroll
             for (int r = 0; r < ROW_GROUP; ++r) {
                 const int rt = rt0 + r;
                 if (rt >= row_tiles) break;
-                const int m = rt * 16 + n;
-                const bool rv = m < M && qv;
-                // As in linear_kernel: only valid rows load their A fragments.
-                const f16 *xr = x + (size_t)(rv ? m : 0) * K;
                 f16x8 af[4][4];
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) af[b][s] = zero8();
-                if (rv) {
-#pragma unroll
-                    for (int b = 0; b < 4; ++b)
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) af[b][s] = a_frag(xr, kb, q, b, s);
-                }
+                load_a_tile<XS ? A_STAGED : A_BUFFER>(af, xg, xr, xw, r * 16 + n, gm, K, kb, q, qv);
                 __builtin_amdgcn_sched_barrier(0);  // every load (weights, then A) is issued before the math
                 f32x4 acc[NW];
 #pragma unroll
@@ -222,7 +314,7 @@ __global__ __launch_bounds__(FP8_WAVES * 64) void linear_fp8_kernel(const f16 *_
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
 #pragma unroll
-                        for (int t = 0; t < NW; ++t) acc[t] = mfma_step(af[b][s], b_frag8(w[t], b, s, qv), acc[t]);
+                        for (int t = 0; t < NW; ++t) acc[t] = mfma_step(af[b][s], b_frag8(w[t], b, s), acc[t]);
 #pragma unroll
                 for (int t = 0; t < NW; ++t) {
                     float *pc = part + (((size_t)c * ROW_GROUP + r) * NW + t) * 16 * LDS_ROW;
@@ -241,8 +333,8 @@ __global__ __launch_bounds__(FP8_WAVES * 64) void linear_fp8_kernel(const f16 *_
                     float tot = part[(((size_t)0 * ROW_GROUP + r) * NW + t) * 16 * LDS_ROW + row * LDS_ROW + cl];
                     for (int c = 1; c < S; ++c)
                         tot += part[(((size_t)c * ROW_GROUP + r) * NW + t) * 16 * LDS_ROW + row * LDS_ROW + cl];
-                    const int colx = (nt * NW + t) * 16 + cl;
-                    y[(size_t)m * N + colx] = f16_of_f32(tot * chscale[colx]);
+                    const int colx = col0 + 16 * t + cl;
+                    if (16 * t + cl < R && colx < N) y[(size_t)m * N + colx] = f16_of_f32(tot * chscale[colx]);
                 }
             }
         }
@@ -266,13 +358,18 @@ int linear_prepare()
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return NVFP4_ERR_LAUNCH;
     if (dev < 64 && done[dev].load(std::memory_order_acquire)) return NVFP4_OK;
-    hipError_t e = allow_lds(linear_kernel<1, false, f16>);
-    if (e == hipSuccess) e = allow_lds(linear_kernel<2, false, f16>);
-    if (e == hipSuccess) e = allow_lds(linear_kernel<1, false, float>);
-    if (e == hipSuccess) e = allow_lds(linear_kernel<2, false, float>);
-    if (e == hipSuccess) e = allow_lds(linear_kernel<2, true, f16>);
-    if (e == hipSuccess) e = allow_lds(linear_fp8_kernel<1>);
-    if (e == hipSuccess) e = allow_lds(linear_fp8_kernel<2>);
+    hipError_t e = hipSuccess;
+    for (int xs = 0; xs < 2 && e == hipSuccess; ++xs) {
+        e = allow_lds(xs ? linear_kernel<1, false, f16, true> : linear_kernel<1, false, f16, false>);
+        if (e == hipSuccess) e = allow_lds(xs ? linear_kernel<2, false, f16, true> : linear_kernel<2, false, f16, false>);
+        if (e == hipSuccess)
+            e = allow_lds(xs ? linear_kernel<1, false, float, true> : linear_kernel<1, false, float, false>);
+        if (e == hipSuccess)
+            e = allow_lds(xs ? linear_kernel<2, false, float, true> : linear_kernel<2, false, float, false>);
+        if (e == hipSuccess) e = allow_lds(xs ? linear_kernel<2, true, f16, true> : linear_kernel<2, true, f16, false>);
+        if (e == hipSuccess) e = allow_lds(xs ? linear_fp8_kernel<1, true> : linear_fp8_kernel<1, false>);
+        if (e == hipSuccess) e = allow_lds(xs ? linear_fp8_kernel<2, true> : linear_fp8_kernel<2, false>);
+    }
     if (e != hipSuccess) return NVFP4_ERR_LAUNCH;
     if (dev < 64) done[dev].store(1, std::memory_order_release);
     return NVFP4_OK;
@@ -280,22 +377,39 @@ int linear_prepare()
 
 namespace {
 
+// Whether the activations stage in LDS: small batches whose staged rows fit beside the partial tiles.
+bool stage_rows(int M, int waves, size_t part_bytes)
+{
+    return M >= 1 && M <= XS_ROWS && part_bytes + (size_t)waves * M * XS_PITCH <= MAX_LDS_BYTES;
+}
+
+// Output columns per block: the N columns spread over every CU of the device, at most max_cols.
+int cols_per_block(int n, int max_cols)
+{
+    const int cus = device_cus();
+    const int r = (n + cus - 1) / cus;
+    return r < 1 ? 1 : (r > max_cols ? max_cols : r);
+}
+
 template <int NW>
-int launch_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights &w, uint16_t *y, hipStream_t s)
+int launch_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights &w, int R, uint16_t *y, hipStream_t s)
 {
     const int N = w.rows, K = w.k;
     const int S = num_chunks(K);
     const int waves = S < FP8_WAVES ? S : FP8_WAVES;
     const size_t shmem = (size_t)S * ROW_GROUP * NW * 16 * LDS_ROW * sizeof(float);
     if (shmem > MAX_LDS_BYTES) return NVFP4_ERR_UNSUPPORTED;  // the entry point admits no such K
+    const bool xs = stage_rows(M, waves, shmem);
     const int st = linear_prepare();
     if (st != NVFP4_OK) return st;
-    return launch(linear_fp8_kernel<NW>, dim3((unsigned)(N / (16 * NW))), dim3((unsigned)(waves * 64)), shmem, s,
-                  reinterpret_cast<const f16 *>(x), M, w.codes, w.channel_scale, N, K, reinterpret_cast<f16 *>(y));
+    return launch(xs ? linear_fp8_kernel<NW, true> : linear_fp8_kernel<NW, false>, dim3((unsigned)((N + R - 1) / R)),
+                  dim3((unsigned)(waves * 64)), shmem + (xs ? (size_t)waves * M * XS_PITCH : 0), s,
+                  reinterpret_cast<const f16 *>(x), M, w.codes, w.channel_scale, N, K, reinterpret_cast<f16 *>(y), R);
 }
 
 template <int NW, bool GATED, typename OUT = f16>
-int launch_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, int N, int layout, void *y, hipStream_t s)
+int launch_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, int N, int layout, int R, void *y,
+                  hipStream_t s)
 {
     const int K = w.k;
     const int S = num_chunks(K);
@@ -303,26 +417,30 @@ int launch_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, int N, i
     const size_t shmem = (size_t)S * ROW_GROUP * NW * 16 * LDS_ROW * sizeof(float);
     static_assert(ROW_GROUP == 2 && LDS_ROW == 20, "linear_lds_bytes assumes this partial-tile layout");
     if (shmem != linear_lds_bytes(K, NW) || shmem > MAX_LDS_BYTES) return NVFP4_ERR_UNSUPPORTED;
+    const bool xs = stage_rows(M, waves, shmem);
     const int st = linear_prepare();
     if (st != NVFP4_OK) return st;
-    const int blocks = GATED ? N / 16 : N / (16 * NW);
-    return launch(linear_kernel<NW, GATED, OUT>, dim3((unsigned)blocks), dim3((unsigned)(waves * 64)), shmem, s,
+    const int blocks = (N + R - 1) / R;
+    return launch(xs ? linear_kernel<NW, GATED, OUT, true> : linear_kernel<NW, GATED, OUT, false>, dim3((unsigned)blocks),
+                  dim3((unsigned)(waves * 64)), shmem + (xs ? (size_t)waves * M * XS_PITCH : 0), s,
                   reinterpret_cast<const f16 *>(x), M, w.codes, w.scales, w.global_scale, N, K, layout,
-                  static_cast<OUT *>(y));
+                  static_cast<OUT *>(y), R);
 }
 
 }  // namespace
 
 int run_linear(const uint16_t *x, int32_t M, const nvfp4_weights &w, uint16_t *y, hipStream_t s)
 {
-    if (linear_tiles(w.rows, w.k) == 2) return launch_linear<2, false>(x, M, w, w.rows, 0, y, s);
-    return launch_linear<1, false>(x, M, w, w.rows, 0, y, s);
+    const int R = cols_per_block(w.rows, 16 * linear_max_tiles(w.k));
+    if (R > 16) return launch_linear<2, false>(x, M, w, w.rows, 0, R, y, s);
+    return launch_linear<1, false>(x, M, w, w.rows, 0, R, y, s);
 }
 
 int run_linear_f32(const uint16_t *x, int32_t M, const nvfp4_weights &w, float *y, hipStream_t s)
 {
-    if (linear_tiles(w.rows, w.k) == 2) return launch_linear<2, false, float>(x, M, w, w.rows, 0, y, s);
-    return launch_linear<1, false, float>(x, M, w, w.rows, 0, y, s);
+    const int R = cols_per_block(w.rows, 16 * linear_max_tiles(w.k));
+    if (R > 16) return launch_linear<2, false, float>(x, M, w, w.rows, 0, R, y, s);
+    return launch_linear<1, false, float>(x, M, w, w.rows, 0, R, y, s);
 }
 
 // ---- shared-expert gate ---------------------------------------------------------------------------
@@ -364,14 +482,15 @@ int run_shared_gate(const uint16_t *x, int32_t M, int32_t K, const uint16_t *g, 
 
 int run_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights &w, uint16_t *y, hipStream_t s)
 {
-    if (w.rows % 32 == 0) return launch_linear_fp8<2>(x, M, w, y, s);
-    return launch_linear_fp8<1>(x, M, w, y, s);
+    const int R = cols_per_block(w.rows, 16 * linear_max_tiles(w.k));
+    if (R > 16) return launch_linear_fp8<2>(x, M, w, R, y, s);
+    return launch_linear_fp8<1>(x, M, w, R, y, s);
 }
 
 int run_linear_swiglu(const uint16_t *x, int32_t M, const nvfp4_weights &w, int32_t layout, uint16_t *h,
                       hipStream_t s)
 {
-    return launch_linear<2, true>(x, M, w, w.rows / 2, layout, h, s);
+    return launch_linear<2, true>(x, M, w, w.rows / 2, layout, cols_per_block(w.rows / 2, 16), h, s);
 }
 
 }  // namespace nvfp4

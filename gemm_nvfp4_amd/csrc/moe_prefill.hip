@@ -76,25 +76,6 @@ struct __attribute__((aligned(16))) PrefillShared {
     int pair[PF_ROWS];            // pair index of each pass row (W2: where its result goes)
 };
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Raw buffer resource over [base, base + bytes). Dword 3 = 0x00020000 selects the 32-bit data
-// format that gfx9 untyped buffer loads require. Reads at offsets >= bytes return zero.
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff)
-{
-    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-}
-
-__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff)
-{
-    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-}
-
 // Logical block index with blocks of one expert kept on one XCD: the hardware deals block ids to
 // the 8 XCDs round-robin, so logical = xcd * ceil(G/8) + slot puts consecutive logical blocks on the
 // same XCD. Returns -1 for the padding ids of the last XCD.

@@ -120,6 +120,35 @@ __device__ __forceinline__ f16x8 zero8()
     return f16x8{0, 0, 0, 0, 0, 0, 0, 0};
 }
 
+// ---- buffer loads ----------------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over [base, base + bytes). Dword 3 = 0x00020000 selects the 32-bit data
+// format that gfx9 untyped buffer loads require. Reads at offsets >= bytes return zero, so a lane
+// that must feed zeros can load at BUF_OOB instead of branching around its load (a branch around a
+// load makes the compiler wait for every earlier load before any later one issues).
+constexpr uint32_t BUF_OOB = 0x40000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
+__device__ __forceinline__ uint2 bload8(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
 // Block barrier that orders LDS only. __syncthreads() also fences global memory, and on gfx9 that
 // means s_waitcnt vmcnt(0): it would wait for loads still in flight (a prefetch). Kernels that pass
 // no global data between the waves of a block use this instead.
