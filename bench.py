@@ -369,8 +369,15 @@ def dense_timing(copies=64, launches=256):
         y = torch.empty((M, N), dtype=torch.float16, device="cuda")
         ms = med(time_graph(lambda: [G.nvfp4_linear(x, ws[i % copies], y=y) for i in range(launches)], launches))
         us = ms * 1e3 / launches
+        # the split-K form (nvfp4_linear_ws: same results, per-chunk partials in a workspace, then
+        # their ordered sum; up to 8 rows it runs the one-launch kernel)
+        wsb = torch.empty(max(G.nvfp4_linear_ws_bytes(M, N, Kd), 16), dtype=torch.uint8, device="cuda")
+        ms_ws = med(time_graph(lambda: [G.nvfp4_linear_ws(x, ws[i % copies], y=y, ws=wsb) for i in range(launches)],
+                               launches))
+        us_ws = ms_ws * 1e3 / launches
         res.append({"M": M, "us": round(us, 3), "weight_GBps": round(wbytes / (us * 1e-6) / 1e9, 1),
-                    "hbm_frac": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+                    "hbm_frac": round(wbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "split_k_us": round(us_ws, 3),
+                    "split_k_hbm_frac": round(wbytes / (us_ws * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
     return res
 
 
@@ -472,8 +479,17 @@ def mlp_timing(copies=48, launches=192):
                               launches))
         d_ms = med(time_graph(lambda: [G.nvfp4_linear(h, w2[i % copies], y=y) for i in range(launches)], launches))
         g_us, d_us = g_ms * 1e3 / launches, d_ms * 1e3 / launches
+        # the split-K forms of both projections, one workspace sized for the larger
+        wsb = torch.empty(max(G.nvfp4_linear_ws_bytes(M, 2 * Id, Kd), G.nvfp4_linear_ws_bytes(M, Kd, Id), 16),
+                          dtype=torch.uint8, device="cuda")
+        gs_ms = med(time_graph(lambda: [G.nvfp4_linear_swiglu_ws(x, w13[i % copies], h=h, ws=wsb)
+                                        for i in range(launches)], launches))
+        ds_ms = med(time_graph(lambda: [G.nvfp4_linear_ws(h, w2[i % copies], y=y, ws=wsb) for i in range(launches)],
+                               launches))
+        gs_us, ds_us = gs_ms * 1e3 / launches, ds_ms * 1e3 / launches
         res.append({"M": M, "gate_up_swiglu_us": round(g_us, 3), "down_us": round(d_us, 3),
-                    "weight_GBps": round((b13 + b2) / ((g_us + d_us) * 1e-6) / 1e9, 1)})
+                    "weight_GBps": round((b13 + b2) / ((g_us + d_us) * 1e-6) / 1e9, 1),
+                    "split_k_gate_up_swiglu_us": round(gs_us, 3), "split_k_down_us": round(ds_us, 3)})
     return res
 
 

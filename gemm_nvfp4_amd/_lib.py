@@ -60,6 +60,9 @@ _SIGS = {
     "nvfp4_moe_w2_reduce_with_shared": (C.c_int, [_vp, _i32, _i32, _i32, _vp, C.POINTER(nvfp4_weights), _vp, _vp,
                                                   C.POINTER(nvfp4_weights), _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_linear_swiglu": (C.c_int, [_vp, _i32, C.POINTER(nvfp4_weights), _i32, _vp, _vp]),
+    "nvfp4_linear_ws_bytes": (C.c_size_t, [_i32, _i32, _i32]),
+    "nvfp4_linear_ws": (C.c_int, [_vp, _i32, C.POINTER(nvfp4_weights), _vp, _vp, C.c_size_t, _vp]),
+    "nvfp4_linear_swiglu_ws": (C.c_int, [_vp, _i32, C.POINTER(nvfp4_weights), _i32, _vp, _vp, C.c_size_t, _vp]),
     "nvfp4_moe_plan_w13_swiglu": (C.c_int, [_vp, _i32, _i32, _i32, _vp, _sz, _vp, C.POINTER(nvfp4_weights), _i32, _vp,
                                             _vp]),
     "nvfp4_linear_fp8": (C.c_int, [_vp, _i32, C.POINTER(fp8_channel_weights), _vp, _vp]),
@@ -381,6 +384,52 @@ def nvfp4_linear_swiglu(x: torch.Tensor, w13: NVFP4Tensor, layout: int = 0, h: t
     d = w13.desc()
     _check("nvfp4_linear_swiglu", lib().nvfp4_linear_swiglu(_dev(x, "x", torch.float16), M, C.byref(d), layout,
                                                             _dev(h, "h", torch.float16), _stream(stream)))
+    return h
+
+
+def nvfp4_linear_ws_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().nvfp4_linear_ws_bytes(M, N, K))
+
+
+def _split_ws(ws, M, w, dev):
+    need = nvfp4_linear_ws_bytes(M, w.rows, w.k)
+    if ws is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"ws holds {ws.numel() * ws.element_size()} bytes, the call needs {need}")
+    return ws
+
+
+def nvfp4_linear_ws(x: torch.Tensor, w: NVFP4Tensor, y: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """Split-K form of nvfp4_linear (bitwise the same y); ws: nvfp4_linear_ws_bytes(M, N, K) bytes."""
+    M = x.shape[0]
+    _shape(x, "x", (M, w.k))
+    if y is None:
+        y = torch.empty((M, w.rows), dtype=torch.float16, device=x.device)
+    _shape(y, "y", (M, w.rows))
+    ws = _split_ws(ws, M, w, x.device)
+    d = w.desc()
+    _check("nvfp4_linear_ws", lib().nvfp4_linear_ws(_dev(x, "x", torch.float16), M, C.byref(d),
+                                                    _dev(y, "y", torch.float16), ws.data_ptr(),
+                                                    ws.numel() * ws.element_size(), _stream(stream)))
+    return y
+
+
+def nvfp4_linear_swiglu_ws(x: torch.Tensor, w13: NVFP4Tensor, layout: int = 0, h: torch.Tensor | None = None,
+                           ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Split-K form of nvfp4_linear_swiglu (bitwise the same h); ws: nvfp4_linear_ws_bytes(M, 2I, K) bytes."""
+    M = x.shape[0]
+    I = w13.rows // 2
+    _shape(x, "x", (M, w13.k))
+    if h is None:
+        h = torch.empty((M, I), dtype=torch.float16, device=x.device)
+    _shape(h, "h", (M, I))
+    ws = _split_ws(ws, M, w13, x.device)
+    d = w13.desc()
+    _check("nvfp4_linear_swiglu_ws", lib().nvfp4_linear_swiglu_ws(
+        _dev(x, "x", torch.float16), M, C.byref(d), layout, _dev(h, "h", torch.float16), ws.data_ptr(),
+        ws.numel() * ws.element_size(), _stream(stream)))
     return h
 
 

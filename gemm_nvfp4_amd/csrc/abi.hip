@@ -551,6 +551,54 @@ NVFP4_API int nvfp4_linear_swiglu(const uint16_t *x, int32_t M, const nvfp4_weig
     return nvfp4::run_linear_swiglu(x, M, *w13, layout, h, static_cast<hipStream_t>(stream));
 }
 
+NVFP4_API size_t nvfp4_linear_ws_bytes(int32_t M, int32_t N, int32_t K)
+{
+    if (M < 0 || N < 1 || K < 1) return 0;
+    return nvfp4::linear_ws_bytes(M, N, K);
+}
+
+// The split-K calls: the same checks as the one-launch calls, then the workspace's.
+static int split_ws_ok(int32_t M, const nvfp4_weights *w, const void *ws, size_t ws_bytes)
+{
+    if (!ws) return NVFP4_ERR_NULL;
+    if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
+    if (ws_bytes < nvfp4::linear_ws_bytes(M, w->rows, w->k)) return NVFP4_ERR_WORKSPACE;
+    // the fold launch takes four outputs per thread, 64 threads per block
+    if ((int64_t)M * w->rows / 256 >= (int64_t)INT32_MAX) return NVFP4_ERR_UNSUPPORTED;
+    return NVFP4_OK;
+}
+
+NVFP4_API int nvfp4_linear_ws(const uint16_t *x, int32_t M, const nvfp4_weights *w, uint16_t *y, void *ws,
+                              size_t ws_bytes, void *stream)
+{
+    if (M < 0) return NVFP4_ERR_SHAPE;
+    int st = check_weights(w);
+    if (st != NVFP4_OK) return st;
+    if (w->groups != 1) return NVFP4_ERR_SHAPE;
+    if (w->k % 128 != 0 || w->k > nvfp4::MAX_LINEAR_K || w->rows % 16 != 0) return NVFP4_ERR_UNSUPPORTED;
+    if (M == 0) return NVFP4_OK;
+    if (!x || !y) return NVFP4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(y, 16)) return NVFP4_ERR_ALIGN;
+    if ((st = split_ws_ok(M, w, ws, ws_bytes)) != NVFP4_OK) return st;
+    return nvfp4::run_linear_split(x, M, *w, y, ws, static_cast<hipStream_t>(stream));
+}
+
+NVFP4_API int nvfp4_linear_swiglu_ws(const uint16_t *x, int32_t M, const nvfp4_weights *w13, int32_t layout,
+                                     uint16_t *h, void *ws, size_t ws_bytes, void *stream)
+{
+    if (M < 0 || (layout != 0 && layout != 1)) return NVFP4_ERR_SHAPE;
+    int st = check_weights(w13);
+    if (st != NVFP4_OK) return st;
+    if (w13->groups != 1 || w13->rows % 2 != 0) return NVFP4_ERR_SHAPE;
+    if (w13->k % 128 != 0 || w13->k > nvfp4::MAX_LINEAR_SWIGLU_K || (w13->rows / 2) % 16 != 0)
+        return NVFP4_ERR_UNSUPPORTED;
+    if (M == 0) return NVFP4_OK;
+    if (!x || !h) return NVFP4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(h, 16)) return NVFP4_ERR_ALIGN;
+    if ((st = split_ws_ok(M, w13, ws, ws_bytes)) != NVFP4_OK) return st;
+    return nvfp4::run_linear_swiglu_split(x, M, *w13, layout, h, ws, static_cast<hipStream_t>(stream));
+}
+
 NVFP4_API int nvfp4_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights *w, uint16_t *y, void *stream)
 {
     if (M < 0) return NVFP4_ERR_SHAPE;

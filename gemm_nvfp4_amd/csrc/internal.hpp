@@ -187,6 +187,11 @@ bool prefill_offsets_fit(int64_t M, int64_t P, int32_t K, int32_t I);
 int run_reduce(const PlanView &pv, int32_t M, int32_t topk, int32_t K, const float *topk_weights, const float *ws,
                uint16_t *out, hipStream_t s, SharedTerm sh = {});
 int run_linear_f32(const uint16_t *x, int32_t M, const nvfp4_weights &w, float *y, hipStream_t s);
+// Split-K forms with a workspace of linear_ws_bytes(M, w.rows, w.k) bytes (16-byte aligned).
+size_t linear_ws_bytes(int32_t M, int32_t N, int32_t K);
+int run_linear_split(const uint16_t *x, int32_t M, const nvfp4_weights &w, uint16_t *y, void *ws, hipStream_t s);
+int run_linear_swiglu_split(const uint16_t *x, int32_t M, const nvfp4_weights &w, int32_t layout, uint16_t *h,
+                            void *ws, hipStream_t s);
 int run_shared_gate(const uint16_t *x, int32_t M, int32_t K, const uint16_t *g, float *sigma, hipStream_t s);
 
 // Regime switch (performance only: every kernel uses the same reduction order, so results are

@@ -342,6 +342,141 @@ __global__ __launch_bounds__(FP8_WAVES * 64) void linear_fp8_kernel(const f16 *_
     }
 }
 
+// ---- split-K form (workspace) ---------------------------------------------------------------------
+// The same products with the reduction split across blocks and a second launch that adds the chunk
+// partials. In the one-launch kernel every block reads all of x (M * K * 2 bytes; 327 KB per CU at
+// 32 rows of 5120), which bounds it once M grows. Here block b takes chunk c = b % S and T
+// consecutive 16-row weight tiles, one per wave, so a CU reads one chunk of x (M KB) and T tiles of
+// that chunk's weights. Each wave's FP32 chain result for (chunk c, rows, its 16 weight rows) is
+// stored to part[c][m][n]; the fold launch adds part[0..S-1] in chunk order and applies the same
+// epilogue as the one-launch kernel, so the outputs are bitwise those of nvfp4_linear and
+// nvfp4_linear_swiglu.
+constexpr int SPLIT_ROWS = 32;  // activation rows staged in LDS per pass
+constexpr int SPLIT_WAVES = 12;  // three waves per SIMD: room for the decoded fragments (168 registers)
+
+__global__ __launch_bounds__(SPLIT_WAVES * 64) void linear_partials_kernel(const f16 *__restrict__ x, int M,
+                                                                           const uint8_t *__restrict__ codes,
+                                                                           const uint8_t *__restrict__ scales, int N,
+                                                                           int K, float *__restrict__ part)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char xs[SPLIT_ROWS * XS_PITCH];
+    const int S = num_chunks(K);
+    const int c = blockIdx.x % S;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const int n = lane & 15, q = lane >> 4;
+    const int t = (blockIdx.x / S) * nwaves + wave;  // this wave's weight tile
+    const bool tv = t < (N >> 4);                    // wave-uniform
+    const int kb = c * KCHUNK;
+    const bool qv = q < (min(KCHUNK, K - kb) >> 7);
+    // The weights first, so that they are in flight while the activations are staged.
+    RawChunk w = RawChunk{};
+    if (tv && qv) {
+        const size_t row = (size_t)t * 16 + n;
+        w = load_chunk(codes + row * ((size_t)K >> 1), scales + row * ((size_t)K >> 4), kb, q);
+    }
+    const int k = kb + 8 * lane;
+    for (int m0 = 0; m0 < M; m0 += SPLIT_ROWS) {
+        const int gm = min(M - m0, SPLIT_ROWS);
+        if (m0 > 0) lds_barrier();  // the previous pass's fragment reads are done
+        for (int r = wave; r < gm; r += nwaves) {
+            const f16 *src = x + (size_t)(m0 + r) * K + (k < K ? k : 0);
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                             (__attribute__((address_space(3))) void *)(xs + r * XS_PITCH), 16, 0, 0);
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's direct-to-LDS loads (and weights) are done
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        lds_barrier();                       // and every other wave's
+        if (!tv) continue;
+        // One tile per wave leaves room to keep the decoded B fragments for every row tile.
+        f16x8 bf[4][4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const f16x2 sc = chunk_scales(w, b);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) bf[b][s] = decode8(w.codes[b][s], sc[s >> 1]);
+        }
+#pragma unroll 1
+        for (int rt = 0; rt * 16 < gm; ++rt) {
+            f16x8 af[4][4];
+            load_a_tile<A_STAGED>(af, x, make_rsrc(x, 0), xs, rt * 16 + n, gm, K, kb, q, qv);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mfma_step(af[b][s], bf[b][s], acc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m = m0 + rt * 16 + 4 * q + j;
+                if (m < M) part[((size_t)c * M + m) * N + (size_t)t * 16 + n] = acc[j];
+            }
+        }
+    }
+}
+
+// y = epilogue(sum over c of part[c]) for 4 consecutive output columns per thread. Plain: the N
+// weight rows are the N columns of y (fp16, or FP32 for OUT = float). Gated: y has N/2 columns, h
+// column i from weight rows g(i) and u(i) of the layout, as the one-launch kernel.
+constexpr int FOLD_THREADS = 64;  // small blocks: the fold's few threads spread over many CUs
+
+template <bool GATED, typename OUT>
+__global__ __launch_bounds__(FOLD_THREADS) void linear_fold_kernel(const float *__restrict__ part, int S, int M, int N,
+                                                          const float *__restrict__ gscale, int layout,
+                                                          OUT *__restrict__ y)
+{
+    const int Ny = GATED ? N >> 1 : N;
+    const size_t i = ((size_t)blockIdx.x * FOLD_THREADS + threadIdx.x) * 4;
+    if (i >= (size_t)M * Ny) return;
+    const int m = (int)(i / Ny), col = (int)(i % Ny);
+    const size_t plane = (size_t)M * N;
+    const float *p = part + (size_t)m * N;
+    const float gs = gscale[0];
+    // Sums of the chunk partials of weight rows ra .. ra + 3 and (GATED) rb .. rb + 3, each in chunk
+    // order, with the loads of up to FB chunks of both issued before their adds.
+    constexpr int FB = GATED ? 8 : 16;
+    auto chunk_sums = [&](int ra, int rb, float4 &ta, float4 &tb) {
+        ta = *reinterpret_cast<const float4 *>(p + ra);
+        if (GATED) tb = *reinterpret_cast<const float4 *>(p + rb);
+        for (int c0 = 1; c0 < S; c0 += FB) {
+            float4 va[FB], vb[FB];
+#pragma unroll
+            for (int e = 0; e < FB; ++e)
+                if (c0 + e < S) {
+                    va[e] = *reinterpret_cast<const float4 *>(p + (size_t)(c0 + e) * plane + ra);
+                    if (GATED) vb[e] = *reinterpret_cast<const float4 *>(p + (size_t)(c0 + e) * plane + rb);
+                }
+#pragma unroll
+            for (int e = 0; e < FB; ++e)
+                if (c0 + e < S) {
+                    ta.x += va[e].x, ta.y += va[e].y, ta.z += va[e].z, ta.w += va[e].w;
+                    if (GATED) tb.x += vb[e].x, tb.y += vb[e].y, tb.z += vb[e].z, tb.w += vb[e].w;
+                }
+        }
+    };
+    OUT *yo = y + (size_t)m * Ny + col;
+    if constexpr (GATED) {
+        float g[4], u[4];
+        float4 a, b;
+        if (layout) {  // gate and up rows interleaved: rows 2i, 2i + 1
+            chunk_sums(2 * col, 2 * col + 4, a, b);
+            g[0] = a.x, u[0] = a.y, g[1] = a.z, u[1] = a.w, g[2] = b.x, u[2] = b.y, g[3] = b.z, u[3] = b.w;
+        } else {
+            chunk_sums(col, Ny + col, a, b);
+            g[0] = a.x, g[1] = a.y, g[2] = a.z, g[3] = a.w, u[0] = b.x, u[1] = b.y, u[2] = b.z, u[3] = b.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yo[e] = f16_of_f32(swiglu(g[e] * gs, u[e] * gs));
+    } else {
+        float4 a, b;
+        chunk_sums(col, col, a, b);
+        yo[0] = to_out<OUT>(a.x * gs);
+        yo[1] = to_out<OUT>(a.y * gs);
+        yo[2] = to_out<OUT>(a.z * gs);
+        yo[3] = to_out<OUT>(a.w * gs);
+    }
+}
+
 template <typename KernelT>
 hipError_t allow_lds(KernelT *kernel)
 {
@@ -441,6 +576,58 @@ int run_linear_f32(const uint16_t *x, int32_t M, const nvfp4_weights &w, float *
     const int R = cols_per_block(w.rows, 16 * linear_max_tiles(w.k));
     if (R > 16) return launch_linear<2, false, float>(x, M, w, w.rows, 0, R, y, s);
     return launch_linear<1, false, float>(x, M, w, w.rows, 0, R, y, s);
+}
+
+size_t linear_ws_bytes(int32_t M, int32_t N, int32_t K)
+{
+    return (size_t)num_chunks(K) * (size_t)M * (size_t)N * sizeof(float);
+}
+
+// Split-K form: the partials launch, then the fold. N = weight rows (2I for the gated form).
+namespace {
+int launch_split(const uint16_t *x, int32_t M, const nvfp4_weights &w, float *part, hipStream_t s)
+{
+    const int N = w.rows, K = w.k, S = num_chunks(K), NT = N / 16;
+    const int cus = device_cus();
+    int T = (int)(((int64_t)NT * S + cus - 1) / cus);  // tiles per block: about one block per CU
+    T = T < 1 ? 1 : (T > SPLIT_WAVES ? SPLIT_WAVES : T);
+    const int64_t blocks = (int64_t)S * ((NT + T - 1) / T);
+    return launch(linear_partials_kernel, dim3((unsigned)blocks), dim3((unsigned)(T * 64)), 0, s,
+                  reinterpret_cast<const f16 *>(x), M, w.codes, w.scales, N, K, part);
+}
+
+template <bool GATED>
+int launch_fold(const float *part, int32_t M, const nvfp4_weights &w, int layout, uint16_t *y, hipStream_t s)
+{
+    const int N = w.rows, S = num_chunks(w.k);
+    const int64_t quads = (int64_t)M * (GATED ? N / 2 : N) / 4;
+    return launch(linear_fold_kernel<GATED, f16>, dim3((unsigned)((quads + FOLD_THREADS - 1) / FOLD_THREADS)),
+                  dim3(FOLD_THREADS), 0, s, part, S, M, N, w.global_scale, layout, reinterpret_cast<f16 *>(y));
+}
+}  // namespace
+
+// The split form pays once the copy of x that every one-launch block reads (M * K * 2 bytes) is
+// large: past 8 rows and 96 KiB. Measured on MI355X, 4352x5120: 7.3 vs 8.6 us at one row, 8.2 vs
+// 9.2 at eight (one-launch faster), 9.3 vs 10.7 at twelve, 12.1 vs 16.1 at 32; the 5120x2176 down
+// projection of the gated MLP: 7.5 vs 8.0 at 16 rows (70 KB of x), 9.6 vs 10.7 at 32. Below that the
+// split-K calls run the one-launch kernel (the same results bitwise; ws is then not touched).
+bool split_pays(int32_t M, int32_t K) { return M > 8 && (int64_t)M * K * 2 > 96 * 1024; }
+
+int run_linear_split(const uint16_t *x, int32_t M, const nvfp4_weights &w, uint16_t *y, void *ws, hipStream_t s)
+{
+    if (!split_pays(M, w.k)) return run_linear(x, M, w, y, s);
+    float *part = static_cast<float *>(ws);
+    const int st = launch_split(x, M, w, part, s);
+    return st != NVFP4_OK ? st : launch_fold<false>(part, M, w, 0, y, s);
+}
+
+int run_linear_swiglu_split(const uint16_t *x, int32_t M, const nvfp4_weights &w, int32_t layout, uint16_t *h,
+                            void *ws, hipStream_t s)
+{
+    if (!split_pays(M, w.k)) return run_linear_swiglu(x, M, w, layout, h, s);
+    float *part = static_cast<float *>(ws);
+    const int st = launch_split(x, M, w, part, s);
+    return st != NVFP4_OK ? st : launch_fold<true>(part, M, w, layout, h, s);
 }
 
 // ---- shared-expert gate ---------------------------------------------------------------------------

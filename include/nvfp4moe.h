@@ -336,6 +336,28 @@ int nvfp4_linear_fp8(const uint16_t *x, int32_t M, const fp8_channel_weights *w,
 int nvfp4_linear_swiglu(const uint16_t *x, int32_t M, const nvfp4_weights *w13, int32_t layout, uint16_t *h,
                         void *stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * Split-K forms of nvfp4_linear and nvfp4_linear_swiglu (same page and sections: the split-K /
+ * FP32 reduction order the verifier keeps). Results are bitwise those of the one-launch calls: the
+ * same 512-element chunk products, added in the same chunk order, the same epilogue. The
+ * reduction is split across blocks instead of inside one, so each CU reads one chunk of x instead
+ * of all of it, which pays once M grows (x is read by every block of the one-launch kernel).
+ * Two launches: per-chunk FP32 partial products into ws, then their ordered sum.
+ *   ws     device memory of at least nvfp4_linear_ws_bytes(M, rows, k) bytes (rows = N, or 2I for
+ *          the gated form), 16-byte aligned, owned by the caller; its contents on entry do not
+ *          matter and are overwritten (num_chunks(K) * M * rows FP32 values, num_chunks(K) =
+ *          ceil(K / 512)). Calls that share a ws must not run concurrently.
+ * Arguments, requirements and the other errors are those of nvfp4_linear / nvfp4_linear_swiglu;
+ * in addition NVFP4_ERR_NULL for ws == NULL, NVFP4_ERR_ALIGN for a misaligned ws and
+ * NVFP4_ERR_WORKSPACE for ws_bytes below the size above, all before anything is enqueued.
+ * nvfp4_linear_ws_bytes returns 0 for M < 0, N < 1 or K < 1.
+ * --------------------------------------------------------------------------------------------- */
+size_t nvfp4_linear_ws_bytes(int32_t M, int32_t N, int32_t K);
+int nvfp4_linear_ws(const uint16_t *x, int32_t M, const nvfp4_weights *w, uint16_t *y, void *ws, size_t ws_bytes,
+                    void *stream);
+int nvfp4_linear_swiglu_ws(const uint16_t *x, int32_t M, const nvfp4_weights *w13, int32_t layout, uint16_t *h,
+                           void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

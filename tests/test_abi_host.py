@@ -42,7 +42,7 @@ def test_header_declares_the_expected_entry_points():
         "nvfp4_linear_swiglu", "nvfp4_linear_fp8", "nvfp4_moe_shared_expert", "nvfp4_moe_w2_reduce_shared",
         "nvfp4_moe_w13_swiglu_with_shared", "nvfp4_moe_w2_reduce_with_shared", "nvfp4_moe_plan_w13_swiglu",
         "nvfp4_moe_plan_w13_swiglu_with_shared", "nvfp4_moe_layer_workspace_bytes", "nvfp4_moe_layer",
-        "nvfp4_moe_layer_noalloc"])
+        "nvfp4_moe_layer_noalloc", "nvfp4_linear_ws_bytes", "nvfp4_linear_ws", "nvfp4_linear_swiglu_ws"])
 
 
 def test_library_exports_every_declared_function():
@@ -210,3 +210,26 @@ def test_layer_call_checks(L):
     assert args(odd, 4, 2, E, fake, w13, 0, w2, fake, fake, fake, need) == 3              # ids unaligned
     assert args(fake, 4, 2, E, fake, w13, 0, w2, fake, fake, odd, need) == 3              # ws unaligned
     assert args(fake, 4, 2, E, fake, w13, 0, w2, fake, fake, fake, need - 1) == 4         # ws too small
+
+
+def test_split_k_dense_workspace_and_errors(L):
+    """The split-K dense calls need ceil(K/512) * M * rows FP32 partials; a missing, misaligned or
+    short workspace is reported before anything is enqueued (fake device pointers are never read)."""
+    from gemm_nvfp4_amd._lib import nvfp4_weights
+    L.nvfp4_linear_ws_bytes.restype = C.c_size_t
+    for M, N, K in ((1, 4352, 5120), (32, 4352, 5120), (45, 256, 2176), (7, 64, 128)):
+        assert L.nvfp4_linear_ws_bytes(M, N, K) == -(-K // 512) * M * N * 4
+    assert L.nvfp4_linear_ws_bytes(-1, 64, 128) == 0 and L.nvfp4_linear_ws_bytes(4, 0, 128) == 0
+    fake, odd, null = C.c_void_p(0x1000), C.c_void_p(0x1008), None
+    w = nvfp4_weights(fake, fake, fake, 1, 64, 640)
+    need = L.nvfp4_linear_ws_bytes(20, 64, 640)
+    assert L.nvfp4_linear_ws(fake, 20, C.byref(w), fake, null, need, null) == 1          # ERR_NULL
+    assert L.nvfp4_linear_ws(fake, 20, C.byref(w), fake, odd, need, null) == 3           # ERR_ALIGN
+    assert L.nvfp4_linear_ws(fake, 20, C.byref(w), fake, fake, need - 1, null) == 4      # ERR_WORKSPACE
+    assert L.nvfp4_linear_ws(fake, 20, C.byref(nvfp4_weights(fake, fake, fake, 1, 64, 96)), fake, fake, need,
+                             null) == 5                                                  # K % 128
+    assert L.nvfp4_linear_ws(null, 0, C.byref(w), null, null, 0, null) == 0              # M = 0
+    w13 = nvfp4_weights(fake, fake, fake, 1, 64, 640)
+    assert L.nvfp4_linear_swiglu_ws(fake, 20, C.byref(w13), 0, fake, fake, need - 4, null) == 4
+    assert L.nvfp4_linear_swiglu_ws(fake, 20, C.byref(w13), 2, fake, fake, need, null) == 2   # layout
+    assert L.nvfp4_linear_swiglu_ws(fake, 20, C.byref(w13), 0, fake, null, need, null) == 1

@@ -58,6 +58,8 @@ def test_dense_and_shared_checks():
     _raises_shape(lambda: G.nvfp4_linear(_f16(3, 384), w), "x must have shape")
     _raises_shape(lambda: G.nvfp4_linear(_f16(3, 256), w, y=_f16(3, 48)), "y must have shape")
     _raises_shape(lambda: G.nvfp4_linear_swiglu(_f16(3, 256), w, h=_f16(3, 64)), "h must have shape")
+    _raises_shape(lambda: G.nvfp4_linear_ws(_f16(3, 256), w, ws=torch.zeros(64, dtype=torch.uint8)), "ws holds")
+    _raises_shape(lambda: G.nvfp4_linear_swiglu_ws(_f16(3, 256), w, ws=torch.zeros(64, dtype=torch.uint8)), "ws holds")
     s13, s2 = _w(1, 2 * I, K), _w(1, K, I)
     _raises_shape(lambda: G.nvfp4_moe_shared_expert(_f16(M, K), s13, s2, _f16(K + 8)), "gate must have shape")
     _raises_shape(lambda: G.nvfp4_moe_shared_expert(_f16(M, K), s13, s2, _f16(K), h=_f16(M, I + 16)),

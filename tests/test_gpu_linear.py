@@ -1,7 +1,7 @@
 """GPU parity of the dense NVFP4 projection against the fp64 oracle.
 
-Covers the 4352 x 5120 projection at M = 1..32, an integer-exact case (bitwise), and batch
-invariance. A batch must be bitwise equal to single-row calls and to concatenated 8-row calls
+Covers the 4352 x 5120 projection at M = 1..32, an integer-exact case (bitwise), batch
+invariance, and the split-K form (nvfp4_linear_ws) bitwise against the one-launch form. A batch must be bitwise equal to single-row calls and to concatenated 8-row calls
 (the verifier check on the "[SM70][Draft] Extend Qwen3.8 DFlash2 concurrency paths" page). It
 also covers ragged K and M, a non-unit global scale, NaN propagation and M = 0.
 """
@@ -89,9 +89,42 @@ def test_linear_m0_is_noop():
 
 @pytest.mark.parametrize("K", [16896, 32768])
 def test_linear_long_reduction(orc, K):
-    """Past K = 16384 the projection takes one weight tile per wave, so the chunk partials fit in
-    the CU's 160 KiB of LDS (with two tiles, 33 or more chunks would need more). 64 rows pair up, so
-    below that length the two-tile kernel runs; both give the same reduction order."""
+    """Past K = 16384 the projection takes at most one weight tile per wave, so the chunk partials
+    fit in the CU's 160 KiB of LDS (with two tiles, 33 or more chunks would need more); the reduction
+    order is the same either way."""
     case = S.dense_case(3, n=64, k=K, weight_set=K)
     y = _run(case["x"], case["w"])
     assert_rows_close(to_np64(y), orc.linear(case["x"], case["w"]), f"linear K={K}")
+
+
+def _poisoned_ws(M, N, K):
+    """A split-K workspace filled with NaN bytes: the call must overwrite every partial it reads."""
+    return torch.full((max(G.nvfp4_linear_ws_bytes(M, N, K), 16),), 0xFF, dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("N,K,M", [(4352, 5120, 10), (4352, 5120, 16), (4352, 5120, 32), (256, 2176, 45),
+                                   (64, 640, 80), (96, 1152, 70), (4352, 5120, 4), (64, 640, 33)])
+def test_linear_split_k_bitwise_equals_one_launch(N, K, M):
+    """nvfp4_linear_ws (per-chunk partials in a workspace, then their sum in chunk order) equals
+    nvfp4_linear bitwise: past 32 rows it stages x in passes (45, 70, 80), 2176, 1152 and 640 end
+    in a short chunk. Where each block's copy of x is small (M = 4, and 33 rows of 640) the call runs
+    the one-launch kernel instead."""
+    case = S.dense_case(M, n=N, k=K, weight_set=N + K)
+    w = G.NVFP4Tensor.from_numpy(case["w"])
+    x = torch.from_numpy(case["x"]).cuda()
+    one = G.nvfp4_linear(x, w)
+    split = G.nvfp4_linear_ws(x, w, ws=_poisoned_ws(M, N, K))
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), split.view(torch.int16))
+
+
+def test_linear_split_k_matches_oracle_and_batch_invariance(orc):
+    case = S.dense_case(32, weight_set=5)
+    w = G.NVFP4Tensor.from_numpy(case["w"])
+    x = torch.from_numpy(case["x"]).cuda()
+    ws = _poisoned_ws(32, S.DENSE_N, S.DENSE_K)
+    full = G.nvfp4_linear_ws(x, w, ws=ws)
+    halves = torch.cat([G.nvfp4_linear_ws(x[m:m + 16].contiguous(), w, ws=ws) for m in (0, 16)])
+    torch.cuda.synchronize()
+    assert torch.equal(full.view(torch.int16), halves.view(torch.int16))
+    assert_rows_close(to_np64(full), orc.linear(case["x"], case["w"]), "linear split-K M=32")

@@ -79,3 +79,17 @@ def test_gated_zero_rows():
     w13, _ = _weights(3, k=256, i=32, n=64)
     h = G.nvfp4_linear_swiglu(torch.zeros((0, 256), dtype=torch.float16, device="cuda"), G.NVFP4Tensor.from_numpy(w13))
     assert h.shape == (0, 32)
+
+
+@pytest.mark.parametrize("M,layout", [(16, 0), (33, 1), (12, 1)])
+def test_gated_split_k_bitwise_equals_one_launch(M, layout):
+    """nvfp4_linear_swiglu_ws folds the gate and up partials with the one-launch epilogue: h is
+    bitwise the same, in both layouts (33 rows take two staging passes)."""
+    w13, _ = _weights(3)
+    x = torch.from_numpy(S.activations(S.rng_for(S.WORKLOAD_IDS["dense"], 64, M), M, K)).cuda()
+    wt = G.NVFP4Tensor.from_numpy(w13)
+    ws = torch.full((G.nvfp4_linear_ws_bytes(M, 2 * I, K),), 0xFF, dtype=torch.uint8, device="cuda")
+    one = G.nvfp4_linear_swiglu(x, wt, layout)
+    split = G.nvfp4_linear_swiglu_ws(x, wt, layout, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), split.view(torch.int16))
