@@ -287,7 +287,9 @@ __device__ __forceinline__ void load_a_chunk(f16x8 af[4][4], const f16 *row, boo
         for (int s = 0; s < 4; ++s) af[b][s] = valid ? a_frag(row, kb, q, b, s) : zero8();
 }
 
-// One chunk of NW weight rows (tiles) against the resident A fragments.
+// One chunk of NW weight rows (tiles) against the resident A fragments. A lane group past the
+// chunk end (qv false) takes zero block scales: its finite E2M1 codes then decode to zeros, one
+// select per scale pair instead of one per fragment.
 template <int NW>
 __device__ __forceinline__ void mma_chunk(const RawChunk (&w)[NW], const f16x8 af[4][4], bool qv, f32x4 (&acc)[NW])
 {
@@ -295,11 +297,11 @@ __device__ __forceinline__ void mma_chunk(const RawChunk (&w)[NW], const f16x8 a
     for (int b = 0; b < 4; ++b) {
         f16x2 sc[NW];
 #pragma unroll
-        for (int t = 0; t < NW; ++t) sc[t] = chunk_scales(w[t], b);
+        for (int t = 0; t < NW; ++t) sc[t] = qv ? chunk_scales(w[t], b) : f16x2{0, 0};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int t = 0; t < NW; ++t) acc[t] = mfma_step(af[b][s], b_frag(w[t], sc[t], b, s, qv), acc[t]);
+            for (int t = 0; t < NW; ++t) acc[t] = mfma_step(af[b][s], decode8(w[t].codes[b][s], sc[t][s >> 1]), acc[t]);
     }
 }
 

@@ -101,14 +101,6 @@ __device__ __forceinline__ f16x2 chunk_scales(const RawChunk &r, int b)
     return (b & 1) ? e4m3_pair<true>(w) : e4m3_pair<false>(w);
 }
 
-// B fragment of step (b, s); `sc` = chunk_scales(r, b); lanes of a lane group past the chunk end
-// (qv false) give exact zeros.
-__device__ __forceinline__ f16x8 b_frag(const RawChunk &r, f16x2 sc, int b, int s, bool qv)
-{
-    const f16x8 w = decode8(r.codes[b][s], sc[s >> 1]);
-    return qv ? w : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-}
-
 // A fragment of step (b, s) of an activation row, chunk starting at kb.
 __device__ __forceinline__ f16x8 a_frag(const f16 *row, int kb, int q, int b, int s)
 {
