@@ -457,10 +457,16 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
     };
     RawChunk wa[2 * TP], wb[2 * TP];
     load_unit(u0, wa, false);
-    for (int64_t u = u0; u < u1; u += 2) {
+    // Pairs of units with the trip count fixed on entry, then an odd unit after the loop. An exit
+    // between the two steps becomes (after the compiler makes the loop single-exit) a path from the
+    // first step back to the top, on which that step's prefetch into wb looks still in flight when
+    // wb is next written: the compiler then waits for every load before issuing the next unit's.
+    int64_t u = u0;
+    for (int64_t k = (u1 - u0) >> 1; k > 0; --k, u += 2) {
         step(u, wa, wb);
-        if (u + 1 < u1) step(u + 1, wb, wa);
+        step(u + 1, wb, wa);
     }
+    if (u < u1) step(u, wa, wb);
 }
 
 // ---- W2: per-pair FP32 results y[p][n] = global * sum_i dq(W2)[n][i] * h[j][i], stored in pair order -----
@@ -572,10 +578,12 @@ __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, con
     };
     RawChunk wa[NT], wb[NT];
     load_unit(u0, wa, false);
-    for (int64_t u = u0; u < u1; u += 2) {
+    int64_t u = u0;  // pairs with a fixed trip count, then the odd unit (as in the W13 kernel)
+    for (int64_t k = (u1 - u0) >> 1; k > 0; --k, u += 2) {
         step(u, wa, wb);
-        if (u + 1 < u1) step(u + 1, wb, wa);
+        step(u + 1, wb, wa);
     }
+    if (u < u1) step(u, wa, wb);
 }
 
 // ---- slot-order weighted reduction: out[t][n] = fp16( fmaf chain over valid slots ) -----------------
