@@ -252,6 +252,36 @@ constexpr int W2_TP = NVFP4_W2_TP;
 constexpr int W13_OCC = NVFP4_W13_OCC;
 constexpr int W2_OCC = NVFP4_W2_OCC;
 
+// A unit's place in a block's range: index among the block's staged row tiles, unit within the
+// tile. The stream kernels step it by one per unit instead of dividing a 64-bit unit index.
+struct UnitPos {
+    int ti, j;
+};
+__device__ __forceinline__ UnitPos next_pos(UnitPos p, int upt)
+{
+    return p.j + 1 < upt ? UnitPos{p.ti, p.j + 1} : UnitPos{p.ti + 1, 0};
+}
+
+// A block's n units (from position pa) with two weight buffers: step(pos, next, last, w, wn)
+// computes the unit at pos from w and loads the next unit (next) into wn, or a dummy when last.
+// The loop runs pairs of steps with the trip count fixed on entry, then the odd unit: an exit
+// between the two steps would become (after the compiler makes the loop single-exit) a path back
+// to the top on which the first step's prefetch looks still in flight when its buffer is next
+// written, and the compiler would then wait for every load before issuing the next unit's.
+template <typename Buf, typename Load, typename Step>
+__device__ __forceinline__ void run_units(UnitPos pa, int n, int upt, Buf &wa, Buf &wb, Load load_unit, Step step)
+{
+    load_unit(pa, wa, false);
+    int left = n;
+    for (; left >= 2; left -= 2) {
+        const UnitPos pb = next_pos(pa, upt), pc = next_pos(pb, upt);
+        step(pa, pb, false, wa, wb);
+        step(pb, pc, left == 2, wb, wa);
+        pa = pc;
+    }
+    if (left) step(pa, pa, true, wa, wb);
+}
+
 // Geometry shared by both kernels: SPLIT waves per wave group (parallel chunks), 4/SPLIT wave
 // groups per unit; `red` is the reduction length.
 template <int SPLIT>
@@ -262,7 +292,7 @@ struct Geo {
     __device__ Geo(int red)
     {
         lane = threadIdx.x & 63;
-        wave = threadIdx.x >> 6;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: unit bases stay scalar
         n = lane & 15;
         q = lane >> 4;
         sub = wave / SPLIT;
@@ -389,34 +419,40 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
     // dummy (block-uniform): the "next unit" of the last unit, whose registers are never used; every
     // lane then reads the same 64 bytes of row 0 (one cache line per load), so the block's last
     // unit costs no second copy of its bytes through the CU's memory path.
-    auto load_unit = [&](int64_t u, RawChunk (&w)[2 * TP], bool dummy) {
-        const int ti = (int)(u / upt) - t_lo;
-        const int it0 = (int)(u % upt) * SL + g.sub * TP;
-        const int e = st.e[ti];
+    // A unit's rows are a wave-uniform base (expert, slice; scalar arithmetic) plus this lane's
+    // fixed offsets (its row among the slice's 16 and its lane group's bytes in the chunk, at most
+    // 31 rows of at most 1 KiB of codes).
+    const int rstep = layout ? 2 : 1;  // row distance between consecutive i
+    const size_t up_rows = layout ? 1 : (size_t)I;  // an up row relative to its gate row
+    const uint32_t lane_c = (uint32_t)(rstep * g.n) * (uint32_t)crow + (uint32_t)(g.kb_ld >> 1) + 64u * (uint32_t)g.q_ld;
+    const uint32_t lane_s = (uint32_t)(rstep * g.n) * (uint32_t)srow + (uint32_t)(g.kb_ld >> 4) + 8u * (uint32_t)g.q_ld;
+    auto load_unit = [&](UnitPos pu, RawChunk (&w)[2 * TP], bool dummy) {
+        const int it0 = pu.j * SL + g.sub * TP;
+        const int e = __builtin_amdgcn_readfirstlane(st.e[pu.ti]);
         if constexpr (PM) dummy = dummy || e < 0;  // a skipped pair: nothing of it is read
-        const uint8_t *cb = !SH || e >= 0 ? codes : shx.codes, *sb = !SH || e >= 0 ? scales : shx.scales;
-        const size_t eb = !SH || e >= 0 ? (size_t)e * 2 * I : 0;
-        const int q_ld = dummy ? 0 : g.q_ld;
+        const bool own = !SH || e >= 0;
+        const uint8_t *cb = own ? codes : shx.codes, *sb = own ? scales : shx.scales;
+        const size_t eb = own ? (size_t)e * 2 * I : 0;
+        const uint32_t lc = dummy ? 0u : lane_c, ls = dummy ? 0u : lane_s;
 #pragma unroll
         for (int p = 0; p < TP; ++p) {
-            const int i_row = min(it0 + p, itiles - 1) * 16 + g.n;
-            const size_t rg = dummy ? 0 : eb + (layout ? 2 * i_row : i_row);
-            const size_t ru = dummy ? 0 : eb + (layout ? 2 * i_row + 1 : I + i_row);
-            w[2 * p] = load_chunk(cb + rg * crow, sb + rg * srow, g.kb_ld, q_ld);
-            w[2 * p + 1] = load_chunk(cb + ru * crow, sb + ru * srow, g.kb_ld, q_ld);
+            const size_t rg = dummy ? 0 : eb + (size_t)rstep * (size_t)(min(it0 + p, itiles - 1) * 16);
+            const size_t ru = dummy ? 0 : rg + up_rows;
+            w[2 * p] = load_chunk_at(cb + rg * crow, lc, sb + rg * srow, ls);
+            w[2 * p + 1] = load_chunk_at(cb + ru * crow, lc, sb + ru * srow, ls);
         }
     };
-    // One unit: math on `w` (already loading), next unit's weights into `wn`. Called with the two
-    // buffers alternating, so no register copy ever waits on a load in flight.
-    auto step = [&](int64_t u, RawChunk (&w)[2 * TP], RawChunk (&wn)[2 * TP]) {
-        const int ti = (int)(u / upt) - t_lo;
-        const int it0 = (int)(u % upt) * SL + g.sub * TP;
-        const int e = SH ? __builtin_amdgcn_readfirstlane(st.e[ti]) : st.e[ti], cnt = st.cnt[ti], base = st.base[ti];
+    // One unit: math on `w` (already loading) and the next unit's weights into `wn`, or the dummy
+    // when last. The two buffers alternate, so no register copy ever waits on a load in flight.
+    auto step = [&](UnitPos pu, UnitPos pn, bool last, RawChunk (&w)[2 * TP], RawChunk (&wn)[2 * TP]) {
+        const int ti = pu.ti;
+        const int it0 = pu.j * SL + g.sub * TP;
+        const int e = __builtin_amdgcn_readfirstlane(st.e[ti]), cnt = st.cnt[ti], base = st.base[ti];
         if (ti != cur) {  // A of this tile's rows, reused by every unit of the tile
             cur = ti;
             load_a_chunk(af, x + (size_t)st.arow[ti][g.n] * K, g.qv && g.n < cnt, g.kb, g.q);
         }
-        load_unit(u + 1 < u1 ? u + 1 : u, wn, u + 1 >= u1);  // next unit's weights (after the last: a dummy)
+        load_unit(last ? pu : pn, wn, last);  // next unit's weights (after the last: a dummy)
         // The global scale (a scalar load) is read here, after the LDS reads that address the loads
         // above: scalar loads and LDS share one wait counter, so an earlier read would hold those
         // loads back, and here its latency overlaps the MFMA chain. (A skipped pair of the
@@ -442,7 +478,7 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
         for (int gp = 0; gp < G::GROUPS; ++gp)
 #pragma unroll
             for (int p = 0; p < TP; ++p) {
-                const int itx = (int)(u % upt) * SL + gp * TP + p;
+                const int itx = pu.j * SL + gp * TP + p;
                 if (itx < itiles && row < cnt) {
                     float Gs = part[gp * SPLIT][2 * p][row][col];
                     float Us = part[gp * SPLIT][2 * p + 1][row][col];
@@ -456,17 +492,8 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
         lds_barrier();
     };
     RawChunk wa[2 * TP], wb[2 * TP];
-    load_unit(u0, wa, false);
-    // Pairs of units with the trip count fixed on entry, then an odd unit after the loop. An exit
-    // between the two steps becomes (after the compiler makes the loop single-exit) a path from the
-    // first step back to the top, on which that step's prefetch into wb looks still in flight when
-    // wb is next written: the compiler then waits for every load before issuing the next unit's.
-    int64_t u = u0;
-    for (int64_t k = (u1 - u0) >> 1; k > 0; --k, u += 2) {
-        step(u, wa, wb);
-        step(u + 1, wb, wa);
-    }
-    if (u < u1) step(u, wa, wb);
+    // The range starts in staged tile 0.
+    run_units(UnitPos{0, (int)(u0 - (int64_t)t_lo * upt)}, (int)(u1 - u0), upt, wa, wb, load_unit, step);
 }
 
 // ---- W2: per-pair FP32 results y[p][n] = global * sum_i dq(W2)[n][i] * h[j][i], stored in pair order -----
@@ -501,24 +528,27 @@ __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, con
     f16x8 af[4][4];
     // Packed weights of unit u into w; unconditional (idle waves re-read valid rows).
     // dummy: as in the W13 kernel, the never-used "next unit" of the last unit reads one line.
-    auto load_unit = [&](int64_t u, RawChunk (&w)[NT], bool dummy) {
-        const int ti = (int)(u / upt) - t_lo;
-        const int nt0 = (int)(u % upt) * UT + g.sub * NT;
-        const int e = st.e[ti];
-        const uint8_t *cb = !SH || e >= 0 ? codes : shw.codes, *sb = !SH || e >= 0 ? scales : shw.scales;
-        const size_t eb = !SH || e >= 0 ? (size_t)e * K : 0;
-        const int q_ld = dummy ? 0 : g.q_ld;
+    // Wave-uniform row base plus this lane's fixed offsets, as in the W13 kernel.
+    const uint32_t lane_c = (uint32_t)g.n * (uint32_t)crow + (uint32_t)(g.kb_ld >> 1) + 64u * (uint32_t)g.q_ld;
+    const uint32_t lane_s = (uint32_t)g.n * (uint32_t)srow + (uint32_t)(g.kb_ld >> 4) + 8u * (uint32_t)g.q_ld;
+    auto load_unit = [&](UnitPos pu, RawChunk (&w)[NT], bool dummy) {
+        const int nt0 = pu.j * UT + g.sub * NT;
+        const int e = __builtin_amdgcn_readfirstlane(st.e[pu.ti]);
+        const bool own = !SH || e >= 0;
+        const uint8_t *cb = own ? codes : shw.codes, *sb = own ? scales : shw.scales;
+        const size_t eb = own ? (size_t)e * K : 0;
+        const uint32_t lc = dummy ? 0u : lane_c, ls = dummy ? 0u : lane_s;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const size_t r = dummy ? 0 : eb + min(nt0 + t, ntiles - 1) * 16 + g.n;
-            w[t] = load_chunk(cb + r * crow, sb + r * srow, g.kb_ld, q_ld);
+            const size_t r = dummy ? 0 : eb + (size_t)(min(nt0 + t, ntiles - 1) * 16);
+            w[t] = load_chunk_at(cb + r * crow, lc, sb + r * srow, ls);
         }
     };
     // One unit: math on `w`, next unit's weights into `wn` (the buffers alternate).
-    auto step = [&](int64_t u, RawChunk (&w)[NT], RawChunk (&wn)[NT]) {
-        const int ti = (int)(u / upt) - t_lo;
-        const int nt0 = (int)(u % upt) * UT + g.sub * NT;
-        const int e = SH ? __builtin_amdgcn_readfirstlane(st.e[ti]) : st.e[ti], cnt = st.cnt[ti], base = st.base[ti];
+    auto step = [&](UnitPos pu, UnitPos pn, bool last, RawChunk (&w)[NT], RawChunk (&wn)[NT]) {
+        const int ti = pu.ti;
+        const int nt0 = pu.j * UT + g.sub * NT;
+        const int e = __builtin_amdgcn_readfirstlane(st.e[ti]), cnt = st.cnt[ti], base = st.base[ti];
         const bool working = g.chunk && nt0 < ntiles;
         if (ti != cur) {
             cur = ti;
@@ -529,7 +559,7 @@ __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, con
         auto out_row = [&](int row) {
             return !SH || e >= 0 ? ws + (size_t)st.pair[ti][row] * K : shw.y + (size_t)(base + row) * K;
         };
-        load_unit(u + 1 < u1 ? u + 1 : u, wn, u + 1 >= u1);  // after the last unit: a dummy
+        load_unit(last ? pu : pn, wn, last);  // after the last unit: a dummy
         // The global scale: a scalar load, read after the LDS reads that address the loads above
         // (scalar loads and LDS share one wait counter), so its latency overlaps the MFMA chain.
         const float gs = SH ? (e >= 0 ? gscale[e] : shw.gscale[0]) : gscale[e];
@@ -566,7 +596,7 @@ __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, con
             for (int gp = 0; gp < G::GROUPS; ++gp)
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    const int ntx = (int)(u % upt) * UT + gp * NT + t;
+                    const int ntx = pu.j * UT + gp * NT + t;
                     if (ntx < ntiles && row < cnt) {
                         float Y = part[gp * SPLIT][t][row][col];
                         for (int cc = 1; cc < g.S; ++cc) Y += part[gp * SPLIT + cc][t][row][col];
@@ -577,13 +607,7 @@ __global__ __launch_bounds__(256, W2_OCC) void w2_stream_kernel(PlanView pv, con
         }
     };
     RawChunk wa[NT], wb[NT];
-    load_unit(u0, wa, false);
-    int64_t u = u0;  // pairs with a fixed trip count, then the odd unit (as in the W13 kernel)
-    for (int64_t k = (u1 - u0) >> 1; k > 0; --k, u += 2) {
-        step(u, wa, wb);
-        step(u + 1, wb, wa);
-    }
-    if (u < u1) step(u, wa, wb);
+    run_units(UnitPos{0, (int)(u0 - (int64_t)t_lo * upt)}, (int)(u1 - u0), upt, wa, wb, load_unit, step);
 }
 
 // ---- slot-order weighted reduction: out[t][n] = fp16( fmaf chain over valid slots ) -----------------

@@ -94,6 +94,21 @@ __device__ __forceinline__ RawChunk load_chunk(const uint8_t *row_codes, const u
     return r;
 }
 
+// load_chunk with the row split into a wave-uniform base and this lane's byte offsets from it
+// (codes: its row and lane group within the chunk; scales likewise). Offsets below 2^32 let the
+// loads take the base in scalar registers and one 32-bit offset per lane.
+__device__ __forceinline__ RawChunk load_chunk_at(const uint8_t *cbase, uint32_t coff, const uint8_t *sbase, uint32_t soff)
+{
+    RawChunk r;
+    const uint8_t *c = cbase + coff;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) r.codes[b] = *reinterpret_cast<const u32x4 *>(c + 16 * b);
+    const uint2 sc = *reinterpret_cast<const uint2 *>(sbase + soff);
+    r.scales[0] = sc.x;
+    r.scales[1] = sc.y;
+    return r;
+}
+
 // The two block scales of load b (steps s = 0,1 and s = 2,3), as fp16.
 __device__ __forceinline__ f16x2 chunk_scales(const RawChunk &r, int b)
 {
