@@ -328,6 +328,26 @@ def counters_mode(kind, W13, W2):
         f"FLOP per layer {np.mean(routes.valid) * FLOP_PER_PAIR:.4g}")
 
 
+def eager_launch_floor(calls=50):
+    """Median µs of one eager launch of a one-element kernel (torch's in-place add) bracketed by HIP
+    events and a synchronize, as eager_latency brackets a layer call: the runtime's own latency of
+    a single launch, which an eager layer call pays once more than its graph replay."""
+    import torch
+    t = torch.zeros(1, device="cuda")
+    for _ in range(5):
+        t.add_(1.0)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    us = []
+    for _ in range(calls):
+        t0.record()
+        t.add_(1.0)
+        t1.record()
+        torch.cuda.synchronize()
+        us.append(t0.elapsed_time(t1) * 1e3)
+    return round(float(np.median(us)), 3)
+
+
 def launch_floor(launches=480):
     import torch
     t = torch.zeros(1, device="cuda")
@@ -583,7 +603,8 @@ def main():
     routes16 = Routes(16, args.patterns, 1000)
     head = moe_layer_timing(16, args.steps, args.warmup, W13, W2, routes16, trials=max(20, args.trials))
     log(f"headline M=16: {head}")
-    eager = {"M1_us": eager_latency(1, W13, W2, Routes(1, 8, 4000)), "M16_us": eager_latency(16, W13, W2, routes16)}
+    eager = {"M1_us": eager_latency(1, W13, W2, Routes(1, 8, 4000)), "M16_us": eager_latency(16, W13, W2, routes16),
+             "one_kernel_us": eager_launch_floor()}
     log(f"eager single-call latency: {eager}")
     k_us, k_bytes = w13_kernel_timing(16, args.steps, W13, routes16)
     achieved = k_bytes / (k_us * 1e-6) / 1e9
