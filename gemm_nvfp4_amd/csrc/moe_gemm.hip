@@ -675,22 +675,22 @@ __device__ __forceinline__ float vector_load_f32(const float *base, int index, i
 // kernels: in rounds of up to four pieces per thread, each thread first issues the round's loads,
 // then stores them, so their latencies overlap instead of one round trip per piece. (Four per
 // round: batching eight makes the kernels spill.) One round covers 16 slots of 512 columns.
-template <typename RowOf, typename ValidOf>
+template <int NT = 256, typename RowOf, typename ValidOf>
 __device__ __forceinline__ void stage_slot_rows(f16 (*s_h)[KCHUNK], int nslot, int pieces, RowOf row_of, ValidOf valid)
 {
     constexpr int MAXP = 4;
     const int total = nslot * pieces;
-    for (int base = 0; base < total; base += MAXP * 256) {
+    for (int base = 0; base < total; base += MAXP * NT) {
         u32x4 v[MAXP];
 #pragma unroll
         for (int i = 0; i < MAXP; ++i) {
-            const int idx = base + (int)threadIdx.x + 256 * i;
+            const int idx = base + (int)threadIdx.x + NT * i;
             const int k = idx / pieces, pc = idx - k * pieces;
             if (idx < total && valid(k)) v[i] = *reinterpret_cast<const u32x4 *>(row_of(k) + 8 * pc);
         }
 #pragma unroll
         for (int i = 0; i < MAXP; ++i) {
-            const int idx = base + (int)threadIdx.x + 256 * i;
+            const int idx = base + (int)threadIdx.x + NT * i;
             const int k = idx / pieces, pc = idx - k * pieces;
             if (idx < total && valid(k)) *reinterpret_cast<u32x4 *>(&s_h[k][8 * pc]) = v[i];
         }
@@ -733,7 +733,8 @@ __device__ __forceinline__ float slot_fold(const int *s_e, const float *s_w, con
 //
 // Pair mode (ids != NULL: the layer call's pair-major path): h is in pair order and each slot's
 // expert is its id (skipped when outside [0, E)), so no load waits for the plan.
-__global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int M, int topk, const f16 *__restrict__ hin,
+template <int NW>  // waves per block: 4 (three slots per wave) or 12 (one)
+__global__ __launch_bounds__(64 * NW, NW == 4 ? W2T_OCC : 1) void w2_token_kernel(PlanView pv, int M, int topk, const f16 *__restrict__ hin,
                                                           const uint8_t *__restrict__ codes,
                                                           const uint8_t *__restrict__ scales,
                                                           const float *__restrict__ gscale, int K, int I,
@@ -769,7 +770,7 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
     // Pair mode with one chunk: h rows are in pair order, so every slot's row is staged now, beside
     // the id loads (a skipped pair's row holds no result and is never used).
     if (ids && S == 1)
-        stage_slot_rows(s_h, topk, I >> 3, [&](int k) { return hin + ((size_t)t * topk + k) * I; },
+        stage_slot_rows<64 * NW>(s_h, topk, I >> 3, [&](int k) { return hin + ((size_t)t * topk + k) * I; },
                         [&](int) { return true; });
     if (slot_thread) {
         s_row[threadIdx.x] = row_r;
@@ -780,24 +781,25 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, q = lane >> 4;
     const size_t crow = (size_t)I >> 1, srow = (size_t)I >> 4;
     if (S == 1) {
-        // One chunk (I <= 512). Each wave issues the packed rows and global scales of up to three
-        // slots at once; then the block stages the valid slots' h rows in LDS while those loads are
+        // One chunk (I <= 512). Each wave issues the packed rows and global scales of its SPW slots
+        // (12 / NW: three or one) at once; then the block stages the valid slots' h rows in LDS while those loads are
         // in flight, so the weight round trip never waits for the h round trip.
         const int pieces = I >> 3;
         const int groups = I >> 7;
         const bool qv = q < groups;
         const int q_ld = qv ? q : groups - 1;
+        constexpr int SPW = 12 / NW;
         const int ngroups = (topk + 11) / 12;  // block-uniform trip count (the loop holds a barrier)
         for (int gi = 0; gi < ngroups; ++gi) {
             const int k0 = wave + 12 * gi;
-            RawChunk w[3];
-            int eg[3], se[3];
-            float gsk[3];
+            RawChunk w[SPW];
+            int eg[SPW], se[SPW];
+            float gsk[SPW];
 #pragma unroll
-            for (int g = 0; g < 3; ++g) se[g] = k0 + 4 * g < topk ? s_e[k0 + 4 * g] : -1;  // LDS reads together
+            for (int g = 0; g < SPW; ++g) se[g] = k0 + NW * g < topk ? s_e[k0 + NW * g] : -1;  // LDS reads together
 #pragma unroll
-            for (int g = 0; g < 3; ++g) {
-                const int k = k0 + 4 * g;
+            for (int g = 0; g < SPW; ++g) {
+                const int k = k0 + NW * g;
                 const bool live = se[g] >= 0;
                 eg[g] = __builtin_amdgcn_readfirstlane(live ? se[g] : 0);
                 // An idle slot's registers are never used: all its lanes read one line of row 0.
@@ -806,12 +808,12 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
                 gsk[g] = vector_load_f32(gscale, eg[g], E);  // beside the weights: one round trip
             }
             if (gi == 0 && !ids)  // plan mode: the rows come from the plan, loaded above
-                stage_slot_rows(s_h, topk, pieces, [&](int k) { return hin + (size_t)s_row[k] * I; },
+                stage_slot_rows<64 * NW>(s_h, topk, pieces, [&](int k) { return hin + (size_t)s_row[k] * I; },
                                 [&](int k) { return s_e[k] >= 0; });
             if (gi == 0) __syncthreads();  // s_h staged; it is not written again
 #pragma unroll
-            for (int g = 0; g < 3; ++g) {
-                const int k = k0 + 4 * g;
+            for (int g = 0; g < SPW; ++g) {
+                const int k = k0 + NW * g;
                 if (se[g] < 0) continue;  // wave-uniform (also past topk)
                 f16x8 af[4][4];
 #pragma unroll
@@ -827,7 +829,7 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
             }
         }
     } else {
-        for (int k = wave; k < topk; k += 4) {
+        for (int k = wave; k < topk; k += NW) {
             const int e = s_e[k];
             if (e < 0) continue;  // wave-uniform
             const size_t wr = (size_t)e * K + nt * 16 + n;
@@ -859,7 +861,8 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_kernel(PlanView pv, int
 // w2_token_shared_kernel: w2_token_kernel with slot topk the shared expert (SharedW2): row t of its
 // h, its own weights, weight sigma, added after the routed slots. The routed-only kernel is kept
 // separate so that it carries none of this.
-__global__ __launch_bounds__(256, W2T_OCC) void w2_token_shared_kernel(PlanView pv, int M, int topk, const f16 *__restrict__ hin,
+template <int NW>  // waves per block, as in w2_token_kernel
+__global__ __launch_bounds__(64 * NW, NW == 4 ? W2T_OCC : 1) void w2_token_shared_kernel(PlanView pv, int M, int topk, const f16 *__restrict__ hin,
                                                           const uint8_t *__restrict__ codes,
                                                           const uint8_t *__restrict__ scales,
                                                           const float *__restrict__ gscale, int K, int I,
@@ -905,15 +908,16 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_shared_kernel(PlanView 
         const int groups = I >> 7;
         const bool qv = q < groups;
         const int q_ld = qv ? q : groups - 1;
+        constexpr int SPW = 12 / NW;
         const int ngroups = (nslot + 11) / 12;  // block-uniform trip count (the loop holds a barrier)
         for (int gi = 0; gi < ngroups; ++gi) {
             const int k0 = wave + 12 * gi;
-            RawChunk w[3];
-            int eg[3], kg[3];
-            float gsk[3];
+            RawChunk w[SPW];
+            int eg[SPW], kg[SPW];
+            float gsk[SPW];
 #pragma unroll
-            for (int g = 0; g < 3; ++g) {
-                const int k = k0 + 4 * g;
+            for (int g = 0; g < SPW; ++g) {
+                const int k = k0 + NW * g;
                 const bool live = k < nslot && s_e[k] >= 0;
                 eg[g] = __builtin_amdgcn_readfirstlane(live ? s_e[k] : 0);
                 kg[g] = k < nslot ? k : 0;
@@ -921,14 +925,14 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_shared_kernel(PlanView 
                 w[g] = load_chunk(slot_codes(kg[g]) + wr * crow, slot_scales(kg[g]) + wr * srow, 0, live ? q_ld : 0);
             }
             if (gi == 0)
-                stage_slot_rows(s_h, nslot, pieces, [&](int k) { return slot_h(k) + (size_t)s_row[k] * I; },
+                stage_slot_rows<64 * NW>(s_h, nslot, pieces, [&](int k) { return slot_h(k) + (size_t)s_row[k] * I; },
                                 [&](int k) { return s_e[k] >= 0; });
 #pragma unroll
-            for (int g = 0; g < 3; ++g) gsk[g] = kg[g] < topk ? gscale[eg[g]] : shw.gscale[0];  // after the LDS reads
+            for (int g = 0; g < SPW; ++g) gsk[g] = kg[g] < topk ? gscale[eg[g]] : shw.gscale[0];  // after the LDS reads
             if (gi == 0) __syncthreads();  // s_h staged; it is not written again
 #pragma unroll
-            for (int g = 0; g < 3; ++g) {
-                const int k = k0 + 4 * g;
+            for (int g = 0; g < SPW; ++g) {
+                const int k = k0 + NW * g;
                 if (k >= nslot || s_e[k] < 0) continue;  // wave-uniform
                 f16x8 af[4][4];
 #pragma unroll
@@ -944,7 +948,7 @@ __global__ __launch_bounds__(256, W2T_OCC) void w2_token_shared_kernel(PlanView 
             }
         }
     } else {
-        for (int k = wave; k < nslot; k += 4) {
+        for (int k = wave; k < nslot; k += NW) {
             const int e = s_e[k];
             if (e < 0) continue;  // wave-uniform
             const size_t wr = slot_row0(k, e) + n;
@@ -1040,13 +1044,26 @@ int run_w2(const PlanView &pv, int64_t t_max, int32_t M, int32_t topk, const uin
     if (pair_ids && (!use_token_w2((int64_t)M * topk, w.groups) || shw.M > 0)) return NVFP4_ERR_UNSUPPORTED;
     if (use_token_w2((int64_t)M * topk, w.groups)) {
         const int64_t G = (int64_t)M * (K / 16);
-        if (shw.M > 0)
-            return launch(w2_token_shared_kernel, dim3((unsigned)((G + 7) / 8 * 8)), dim3(256), 0, s, pv, M, topk,
-                          reinterpret_cast<const f16 *>(h), w.codes, w.scales, w.global_scale, K, I, topk_weights,
-                          shw, reinterpret_cast<f16 *>(out));
-        return launch(w2_token_kernel, dim3((unsigned)((G + 7) / 8 * 8)), dim3(256), 0, s, pv, M, topk,
-                      reinterpret_cast<const f16 *>(h), w.codes, w.scales, w.global_scale, K, I, topk_weights, sh,
-                      reinterpret_cast<f16 *>(out), pair_ids, w.groups);
+        // Waves per block: with at most one block per CU, a block's slots are spread over 12 waves
+        // (one slot chain per wave instead of three in a row). Measured on MI355X (512 experts,
+        // top-10, K = 2048, I = 512; layer call): 15.3 -> 14.1 us at one token, 18.3 -> 17.3 at
+        // two; six waves at two blocks per CU were slower (25.0 -> 26.9 us at four tokens).
+        const int64_t nb = (G + 7) / 8 * 8, cus = device_cus();
+        const dim3 grid((unsigned)nb);
+        if (shw.M > 0) {
+            auto go_sh = [&](auto kern, int threads) {
+                return launch(kern, grid, dim3((unsigned)threads), 0, s, pv, M, topk, reinterpret_cast<const f16 *>(h),
+                              w.codes, w.scales, w.global_scale, K, I, topk_weights, shw, reinterpret_cast<f16 *>(out));
+            };
+            return nb <= cus ? go_sh(w2_token_shared_kernel<12>, 768) : go_sh(w2_token_shared_kernel<4>, 256);
+        }
+        auto go = [&](auto kern, int threads) {
+            return launch(kern, grid, dim3((unsigned)threads), 0, s, pv, M, topk, reinterpret_cast<const f16 *>(h), w.codes,
+                          w.scales, w.global_scale, K, I, topk_weights, sh, reinterpret_cast<f16 *>(out), pair_ids,
+                          w.groups);
+        };
+        if (nb <= cus) return go(w2_token_kernel<12>, 768);
+        return go(w2_token_kernel<4>, 256);
     }
     if (shw.M > 0) {  // the shared tiles write y; the reduction adds sigma * y after the routed slots
         sh.y = shw.y;
