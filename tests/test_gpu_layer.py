@@ -65,6 +65,28 @@ def test_layer_call_equals_separate_calls(m, routing):
         assert torch.equal(h[:nv].view(torch.int16), sep["h"][:nv].view(torch.int16)), f"h, m={m}"
 
 
+def _layer(d, m):
+    ws = torch.empty((G.nvfp4_moe_layer_workspace_bytes(m, 10, 512, 2048, 512),), dtype=torch.uint8, device="cuda")
+    out = torch.full((m, 2048), float("nan"), dtype=torch.float16, device="cuda")
+    G.nvfp4_moe_layer(d["ids"], 512, d["x"], d["w13"], d["w2"], d["tw"], out=out, ws=ws)
+    return out
+
+
+@pytest.mark.parametrize("m,routing", [(2, "zipf"), (3, "uniform"), (8, "repeat_invalid")])
+def test_layer_small_batch_equals_tokens_alone(m, routing):
+    """Each token of a small batch equals, bitwise, the layer on that token alone. One token runs
+    the token-major W2 with one slot chain per wave (12-wave blocks), three tokens and more with
+    three chains per wave (4-wave blocks), so this also pins the two block shapes to each other."""
+    case, d = _case(m, routing, pattern=7)
+    out = _layer(d, m)
+    for t in range(m):
+        dt = dict(d)
+        dt.update(x=d["x"][t:t + 1].contiguous(), ids=d["ids"][t:t + 1].contiguous(), tw=d["tw"][t:t + 1].contiguous())
+        one = _layer(dt, 1)
+        torch.cuda.synchronize()
+        assert torch.equal(one[0].view(torch.int16), out[t].view(torch.int16)), f"m={m} token {t}"
+
+
 @pytest.mark.parametrize("m,routing", [(4, "repeat_invalid"), (16, "uniform")])
 def test_layer_call_against_oracle(orc, m, routing):
     case, d = _case(m, routing)
