@@ -347,7 +347,7 @@ __device__ __forceinline__ void mma_chunk(const RawChunk (&w)[NW], const f16x8 a
 // PM (pair-major, small batches of the layer call): row tile p is pair p alone, taken straight
 // from fp.ids, and h is written in pair order; block 0 builds and writes the plan (for the caller)
 // and computes nothing, blocks 1.. share the units. No unit waits for the plan.
-template <int SPLIT, int TP, bool SH, bool FP = false, bool PM = false>
+template <int SPLIT, int TP, bool SH, bool FP = false, bool PM = false, bool PK = false>
 __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanView pv, int topk, const f16 *__restrict__ x,
                                                                              const uint8_t *__restrict__ codes,
                                                                              const uint8_t *__restrict__ scales,
@@ -356,11 +356,16 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
                                                                              SharedW13 shx, FusedPlan fp)
 {
     static_assert(!PM || (!SH && !FP), "the pair-major launch has neither shared tiles nor staged plan rows");
+    static_assert(!PK || (PM && TP == 1), "packed gate/up tiles are a pair-major, one-pair-per-wave form");
     using G = Geo<SPLIT>;
     constexpr int SL = G::GROUPS * TP;  // i slices per unit
     __shared__ float part[4][2 * TP][16][LDS_ROW];
     __shared__ TileStage st;
-    const int itiles = I >> 4;
+    // PK: a 16-row weight tile holds 8 gate rows and the same 8 up rows (lanes n < 8: gate i,
+    // n >= 8: up i), so a unit covers 8 columns of h and a launch has twice the units. Every
+    // output's MFMA chain is the same as with separate tiles, so h is bitwise the same.
+    constexpr int IS = PK ? 8 : 16;  // h columns per i slice
+    const int itiles = I / IS;
     const int upt = (itiles + SL - 1) / SL;  // units per row tile
     const int Ts = SH ? (shx.M + 15) >> 4 : 0;  // shared expert tiles, before the plan's
     int64_t u0, u1;
@@ -424,8 +429,9 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
     // 31 rows of at most 1 KiB of codes).
     const int rstep = layout ? 2 : 1;  // row distance between consecutive i
     const size_t up_rows = layout ? 1 : (size_t)I;  // an up row relative to its gate row
-    const uint32_t lane_c = (uint32_t)(rstep * g.n) * (uint32_t)crow + (uint32_t)(g.kb_ld >> 1) + 64u * (uint32_t)g.q_ld;
-    const uint32_t lane_s = (uint32_t)(rstep * g.n) * (uint32_t)srow + (uint32_t)(g.kb_ld >> 4) + 8u * (uint32_t)g.q_ld;
+    const uint32_t lrow = PK ? (uint32_t)(rstep * (g.n & 7)) + (g.n >= 8 ? (uint32_t)up_rows : 0u) : (uint32_t)(rstep * g.n);
+    const uint32_t lane_c = lrow * (uint32_t)crow + (uint32_t)(g.kb_ld >> 1) + 64u * (uint32_t)g.q_ld;
+    const uint32_t lane_s = lrow * (uint32_t)srow + (uint32_t)(g.kb_ld >> 4) + 8u * (uint32_t)g.q_ld;
     auto load_unit = [&](UnitPos pu, RawChunk (&w)[2 * TP], bool dummy) {
         const int it0 = pu.j * SL + g.sub * TP;
         const int e = __builtin_amdgcn_readfirstlane(st.e[pu.ti]);
@@ -436,10 +442,14 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
         const uint32_t lc = dummy ? 0u : lane_c, ls = dummy ? 0u : lane_s;
 #pragma unroll
         for (int p = 0; p < TP; ++p) {
-            const size_t rg = dummy ? 0 : eb + (size_t)rstep * (size_t)(min(it0 + p, itiles - 1) * 16);
-            const size_t ru = dummy ? 0 : rg + up_rows;
-            w[2 * p] = load_chunk_at(cb + rg * crow, lc, sb + rg * srow, ls);
-            w[2 * p + 1] = load_chunk_at(cb + ru * crow, lc, sb + ru * srow, ls);
+            const size_t rg = dummy ? 0 : eb + (size_t)rstep * (size_t)(min(it0 + p, itiles - 1) * IS);
+            if constexpr (PK) {
+                w[p] = load_chunk_at(cb + rg * crow, lc, sb + rg * srow, ls);
+            } else {
+                const size_t ru = dummy ? 0 : rg + up_rows;
+                w[2 * p] = load_chunk_at(cb + rg * crow, lc, sb + rg * srow, ls);
+                w[2 * p + 1] = load_chunk_at(cb + ru * crow, lc, sb + ru * srow, ls);
+            }
         }
     };
     // One unit: math on `w` (already loading) and the next unit's weights into `wn`, or the dummy
@@ -462,13 +472,14 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
         f32x4 acc[2 * TP];
 #pragma unroll
         for (int t = 0; t < 2 * TP; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        mma_chunk<2 * TP>(w, af, g.qv, acc);
+        constexpr int NA = PK ? TP : 2 * TP;  // accumulator tiles
+        mma_chunk<NA>(reinterpret_cast<const RawChunk(&)[NA]>(w), af, g.qv, reinterpret_cast<f32x4(&)[NA]>(acc));
         if (!(g.chunk && it0 < itiles)) {
 #pragma unroll
-            for (int t = 0; t < 2 * TP; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < NA; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int t = 0; t < 2 * TP; ++t)
+        for (int t = 0; t < NA; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j) part[g.wave][t][4 * g.q + j][g.n] = acc[t][j];
         lds_barrier();
@@ -479,14 +490,15 @@ __global__ __launch_bounds__(256, W13_OCC) void w13_swiglu_stream_kernel(PlanVie
 #pragma unroll
             for (int p = 0; p < TP; ++p) {
                 const int itx = pu.j * SL + gp * TP + p;
-                if (itx < itiles && row < cnt) {
-                    float Gs = part[gp * SPLIT][2 * p][row][col];
-                    float Us = part[gp * SPLIT][2 * p + 1][row][col];
+                const int tg = PK ? p : 2 * p, tu = PK ? p : 2 * p + 1, cu = PK ? col + 8 : col;
+                if (itx < itiles && row < cnt && (!PK || col < 8)) {
+                    float Gs = part[gp * SPLIT][tg][row][col];
+                    float Us = part[gp * SPLIT][tu][row][cu];
                     for (int cc = 1; cc < g.S; ++cc) {
-                        Gs += part[gp * SPLIT + cc][2 * p][row][col];
-                        Us += part[gp * SPLIT + cc][2 * p + 1][row][col];
+                        Gs += part[gp * SPLIT + cc][tg][row][col];
+                        Us += part[gp * SPLIT + cc][tu][row][cu];
                     }
-                    hb[(size_t)(base + row) * I + itx * 16 + col] = f16_of_f32(swiglu(Gs * gs, Us * gs));
+                    hb[(size_t)(base + row) * I + itx * IS + col] = f16_of_f32(swiglu(Gs * gs, Us * gs));
                 }
             }
         lds_barrier();
@@ -1007,19 +1019,28 @@ int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, 
     const f16 *xp = reinterpret_cast<const f16 *>(x);
     f16 *hp = reinterpret_cast<f16 *>(h);
     if (fp.ids && fp.pair_major) {  // block 0: the plan; blocks 1..: one pair per row tile
+        // Packed gate/up tiles (8 h columns per unit) while there are at most ten 16-column units
+        // per CU: twice the units, so the last ones spread more evenly over the CUs. Measured on
+        // MI355X (512 experts, top-10, K = 2048, I = 512; layer call): 14.1 -> 13.5 us at one
+        // token, 17.1 -> 16.6 at two, 24.8 -> 23.9 at four, 38.5 -> 38.3 at eight; at twelve
+        // tokens (15 units per CU) 50.6 -> 51.5, so larger batches keep 16-column units.
+        const bool pk = fp.L.P * upt <= 10 * (int64_t)cus;
+        const int64_t U = fp.L.P * (pk ? (I / 8 + sl - 1) / sl : upt);
         // Unit blocks as for any streaming launch (at least P / 10, so a range stays within the
         // staging), less one when that keeps block 0 and every unit block resident at once.
-        const int64_t U = fp.L.P * upt;
         int ub = sched::grid_blocks(W13_OCC, cus, U, fp.L.P);
         if (ub == W13_OCC * cus && ub > 1 && ub - 1 >= (fp.L.P + 9) / 10) --ub;
         const dim3 gp((unsigned)(ub + 1));
         // Block 0 takes a first slot but finishes early, so the unit block that shares its CU counts
         // as a first block: the weighted split stays on (cus first against cus - 1 second blocks).
         const int fpm = sched::first_blocks(W13_OCC, cus, ub + 1);
+        auto go = [&](auto kern) {
+            return launch(kern, gp, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, fpm, shx, fp);
+        };
         switch (split) {
-        case 1: return launch(w13_swiglu_stream_kernel<1, W13_TP, false, false, true>, gp, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, fpm, shx, fp);
-        case 2: return launch(w13_swiglu_stream_kernel<2, W13_TP, false, false, true>, gp, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, fpm, shx, fp);
-        default: return launch(w13_swiglu_stream_kernel<4, W13_TP, false, false, true>, gp, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, fpm, shx, fp);
+        case 1: return pk ? go(w13_swiglu_stream_kernel<1, W13_TP, false, false, true, true>) : go(w13_swiglu_stream_kernel<1, W13_TP, false, false, true>);
+        case 2: return pk ? go(w13_swiglu_stream_kernel<2, W13_TP, false, false, true, true>) : go(w13_swiglu_stream_kernel<2, W13_TP, false, false, true>);
+        default: return pk ? go(w13_swiglu_stream_kernel<4, W13_TP, false, false, true, true>) : go(w13_swiglu_stream_kernel<4, W13_TP, false, false, true>);
         }
     }
     if (fp.ids) {  // the plan built in the launch
