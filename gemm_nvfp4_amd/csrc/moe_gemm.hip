@@ -1024,7 +1024,8 @@ int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, 
         // MI355X (512 experts, top-10, K = 2048, I = 512; layer call): 14.1 -> 13.5 us at one
         // token, 17.1 -> 16.6 at two, 24.8 -> 23.9 at four, 38.5 -> 38.3 at eight; at twelve
         // tokens (15 units per CU) 50.6 -> 51.5, so larger batches keep 16-column units.
-        const bool pk = fp.L.P * upt <= 10 * (int64_t)cus;
+        constexpr bool PKF = W13_TP == 1;  // the packed form exists for one tile pair per wave
+        const bool pk = PKF && fp.L.P * upt <= 10 * (int64_t)cus;
         const int64_t U = fp.L.P * (pk ? (I / 8 + sl - 1) / sl : upt);
         // Unit blocks as for any streaming launch (at least P / 10, so a range stays within the
         // staging), less one when that keeps block 0 and every unit block resident at once.
@@ -1038,9 +1039,9 @@ int run_w13(const PlanView &pv, int64_t t_max, int32_t topk, const uint16_t *x, 
             return launch(kern, gp, block, 0, s, pv, topk, xp, w.codes, w.scales, w.global_scale, K, I, layout, hp, fpm, shx, fp);
         };
         switch (split) {
-        case 1: return pk ? go(w13_swiglu_stream_kernel<1, W13_TP, false, false, true, true>) : go(w13_swiglu_stream_kernel<1, W13_TP, false, false, true>);
-        case 2: return pk ? go(w13_swiglu_stream_kernel<2, W13_TP, false, false, true, true>) : go(w13_swiglu_stream_kernel<2, W13_TP, false, false, true>);
-        default: return pk ? go(w13_swiglu_stream_kernel<4, W13_TP, false, false, true, true>) : go(w13_swiglu_stream_kernel<4, W13_TP, false, false, true>);
+        case 1: return pk ? go(w13_swiglu_stream_kernel<1, W13_TP, false, false, true, PKF>) : go(w13_swiglu_stream_kernel<1, W13_TP, false, false, true>);
+        case 2: return pk ? go(w13_swiglu_stream_kernel<2, W13_TP, false, false, true, PKF>) : go(w13_swiglu_stream_kernel<2, W13_TP, false, false, true>);
+        default: return pk ? go(w13_swiglu_stream_kernel<4, W13_TP, false, false, true, PKF>) : go(w13_swiglu_stream_kernel<4, W13_TP, false, false, true>);
         }
     }
     if (fp.ids) {  // the plan built in the launch
